@@ -1,0 +1,258 @@
+"""CPU oracle for one sparse-MoE FFN layer (Step 3.5 Flash style).
+
+TEST INFRASTRUCTURE ONLY. This module is the slow, plain reference that the
+HIP library is checked against. Only the test suite, the package smoke check
+and the benchmark's CPU-baseline leg may import it; the library never calls
+it and it calls nothing in the library.
+
+Source: page "Step3.5 Flash 大模型技术深度解析：稀疏 MoE、混合注意力与 MTP 的
+高效推理革命", section 3.2.1 (expert configuration: 288 routed experts per
+layer, each an independent FFN, plus 1 always-active shared expert; d_model
+4096) and section 3.2.2 (Top-8 routing: a linear layer plus softmax gives
+each expert a probability; the 8 most probable routed experts and the shared
+expert, 9 in all, run; their outputs are summed with weights).
+
+Everything is float64 (inputs are converted exactly: bf16 and fp32 values and
+their pairwise products are exact in float64). Library primitives used as
+single steps: numpy matmul, exp, argsort (stable), bincount, cumsum.
+
+Readings where the pages leave a step open (each also listed with the design
+notes):
+  R1 softmax runs over all E routed experts before selection (3.2.2 computes
+     the probabilities, then selects the 8 most probable);
+  R2 the selected probabilities weight the routed outputs as they are, with
+     no renormalisation over the 8;
+  R3 the shared expert has weight 1 (it is always active and has no router
+     score);
+  R4 each expert is a bias-free SwiGLU FFN: y = W_d (silu(W_g x) * (W_u x));
+  R5 selection compares probabilities rounded to float32; equal float32
+     probabilities go to the lower expert index; the returned probabilities
+     are those float32 values;
+  R6 no capacity limit: every (token, choice) pair is processed (dropless);
+  R7 an optional per-expert router bias is added to the logits before the
+     softmax.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+try:  # accept torch tensors (bf16 included) as inputs without requiring torch
+    import torch as _torch
+except ImportError:  # pragma: no cover
+    _torch = None
+
+
+def as_f64(a) -> np.ndarray:
+    """Exact conversion of a host array or CPU torch tensor to float64."""
+    if _torch is not None and isinstance(a, _torch.Tensor):
+        return a.detach().to("cpu", _torch.float64).numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------- routing ---
+
+def router_logits(x, w_router, bias=None) -> np.ndarray:
+    """Linear router (3.2.2, step 1): l[t,e] = sum_d x[t,d] W_r[e,d] (+ b[e], R7)."""
+    l = as_f64(x) @ as_f64(w_router).T
+    if bias is not None:
+        l = l + as_f64(bias)[None, :]
+    return l
+
+
+def softmax(logits: np.ndarray) -> np.ndarray:
+    """Softmax over all routed experts (3.2.2, step 1; R1), max-subtracted."""
+    z = logits - logits.max(axis=1, keepdims=True)
+    w = np.exp(z)
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def select_topk(p32: np.ndarray, k: int):
+    """The k most probable experts per token (3.2.2, step 2; R5).
+
+    Order: float32 probability descending, then expert index ascending.
+    Returns (idx int32 [T,k], prob float32 [T,k], gap float64 [T]) where gap
+    is p of the k-th choice minus p of the (k+1)-th (inf when k == E).
+    """
+    order = np.argsort(-p32, axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int32)
+    prob = np.take_along_axis(p32, order[:, :k], axis=1).astype(np.float32)
+    if k < p32.shape[1]:
+        nxt = np.take_along_axis(p32, order[:, k:k + 1], axis=1)[:, 0]
+        gap = prob[:, -1].astype(np.float64) - nxt.astype(np.float64)
+    else:
+        gap = np.full(p32.shape[0], np.inf)
+    return idx, prob, gap
+
+
+def route(x, w_router, k: int, bias=None) -> dict:
+    """Router: logits -> softmax (fp64) -> float32 probabilities -> top-k."""
+    logits = router_logits(x, w_router, bias)
+    p64 = softmax(logits)
+    p32 = p64.astype(np.float32)
+    idx, prob, gap = select_topk(p32, k)
+    return dict(logits=logits, p64=p64, p32=p32, idx=idx, prob=prob, gap=gap)
+
+
+# ---------------------------------------------------------------- permute ---
+
+def permute(idx: np.ndarray, n_experts: int) -> dict:
+    """Group the (token, choice) pairs by expert (R6: all pairs kept).
+
+    Pairs are taken in token-major order (t, then choice k); a stable sort on
+    the expert id lays each expert's pairs out contiguously, in token order.
+      counts[e]        number of pairs routed to e
+      offsets[e]       first row of e's segment (exclusive scan), offsets[E] = T*k
+      sorted_token[r]  token of permuted row r
+      dest[t*k + j]    permuted row of pair (t, j)
+    """
+    T, k = idx.shape
+    flat = idx.reshape(-1).astype(np.int64)
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=n_experts).astype(np.int64)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    sorted_token = (order // k).astype(np.int64)
+    dest = np.empty(T * k, dtype=np.int64)
+    dest[order] = np.arange(T * k)
+    return dict(counts=counts, offsets=offsets, sorted_token=sorted_token, dest=dest)
+
+
+# -------------------------------------------------------------- experts ---
+
+def silu(g: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu_ffn(x_rows, w_gate, w_up, w_down) -> np.ndarray:
+    """One expert FFN on a block of rows (R4): W_d (silu(W_g x) * (W_u x))."""
+    xr = as_f64(x_rows)
+    g = xr @ as_f64(w_gate).T
+    u = xr @ as_f64(w_up).T
+    return (silu(g) * u) @ as_f64(w_down).T
+
+
+def grouped_ffn(x_rows, offsets, expert_weights) -> np.ndarray:
+    """Run expert e's FFN on rows offsets[e]:offsets[e+1] of x_rows.
+
+    expert_weights(e) -> (w_gate [F,D], w_up [F,D], w_down [D,F]).
+    """
+    xr = as_f64(x_rows)
+    y = np.zeros_like(xr)          # experts map d_model back to d_model
+    for e in range(len(offsets) - 1):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            y[a:b] = swiglu_ffn(xr[a:b], *expert_weights(e))
+    return y
+
+
+# -------------------------------------------------------------- combine ---
+
+def combine(ys, y_perm, dest, prob) -> np.ndarray:
+    """Weighted sum of the 9 expert outputs (3.2.2, step 3; R2, R3).
+
+    out[t] = ys[t] + sum over j ascending of prob[t,j] * y_perm[dest[t*k+j]].
+    ys is the shared expert's output (None: no shared expert).
+    """
+    prob = as_f64(prob)
+    T, k = prob.shape
+    y_perm = as_f64(y_perm)
+    out = np.zeros((T, y_perm.shape[1])) if ys is None else as_f64(ys).copy()
+    d = np.asarray(dest).reshape(T, k)
+    for j in range(k):
+        out += prob[:, j:j + 1] * y_perm[d[:, j]]
+    return out
+
+
+# ---------------------------------------------------------------- layer ---
+
+class LayerWeights:
+    """Weights of one layer as callables, so large layers can be paged in per expert.
+
+    router: [E, D]; bias: [E] or None; expert(e) -> (gate [F,D], up [F,D],
+    down [D,F]); shared() -> the same triple or None.
+    """
+
+    def __init__(self, router, expert, shared=None, bias=None):
+        self.router = router
+        self.expert = expert
+        self.shared = shared if shared is not None else (lambda: None)
+        self.bias = bias
+
+    @classmethod
+    def from_dict(cls, L: dict) -> "LayerWeights":
+        def expert(e):
+            return L["w_gate"][e], L["w_up"][e], L["w_down"][e]
+
+        def shared():
+            if L.get("s_gate") is None:
+                return None
+            return L["s_gate"], L["s_up"], L["s_down"]
+
+        return cls(L["w_router"], expert, shared, L.get("bias"))
+
+
+def layer_forward(x, W: LayerWeights, k: int) -> dict:
+    """The whole layer on all tokens: route, permute, experts, combine."""
+    xr = as_f64(x)
+    r = route(xr, W.router, k, W.bias)
+    E = r["p32"].shape[1]
+    p = permute(r["idx"], E)
+    x_perm = xr[p["sorted_token"]]
+    y_perm = grouped_ffn(x_perm, p["offsets"], W.expert)
+    sh = W.shared()
+    ys = None if sh is None else swiglu_ffn(xr, *sh)
+    out = combine(ys, y_perm, p["dest"], r["prob"])
+    return dict(**r, **p, y_perm=y_perm, ys=ys, out=out)
+
+
+def layer_rows(x, W: LayerWeights, k: int, rows) -> dict:
+    """The layer's output for selected tokens only, with routing for all tokens.
+
+    Routing and the permutation are computed for every token (they are
+    cheap); the expert FFNs run only for the (token, choice) pairs of the
+    selected tokens, grouped by expert so each expert's weights are read once.
+    out_rows[i] is the output of token rows[i].
+    """
+    xr = as_f64(x)
+    r = route(xr, W.router, k, W.bias)
+    E = r["p32"].shape[1]
+    p = permute(r["idx"], E)
+    rows = np.asarray(rows, dtype=np.int64)
+    idx = r["idx"][rows]                                  # [R, k]
+    y_sel = np.zeros((len(rows), k, xr.shape[1]))
+    for e in np.unique(idx):
+        ri, kj = np.nonzero(idx == e)
+        y_sel[ri, kj] = swiglu_ffn(xr[rows[ri]], *W.expert(int(e)))
+    sh = W.shared()
+    out = np.zeros((len(rows), xr.shape[1])) if sh is None else swiglu_ffn(xr[rows], *sh)
+    prob = as_f64(r["prob"][rows])
+    for j in range(k):
+        out += prob[:, j:j + 1] * y_sel[:, j]
+    return dict(**r, **p, rows=rows, out_rows=out)
+
+
+# -------------------------------------------------------------- helpers ---
+
+def round_out(out64: np.ndarray, dtype: str) -> np.ndarray:
+    """Round the float64 output once to the layer's output type (float32 values)."""
+    if dtype == "f32":
+        return out64.astype(np.float32)
+    if _torch is None:  # pragma: no cover
+        raise RuntimeError("bf16 rounding needs torch")
+    t = _torch.from_numpy(out64.astype(np.float32, copy=False))
+    return t.to(_torch.bfloat16).to(_torch.float32).numpy()
+
+
+def expert_load(counts: np.ndarray) -> dict:
+    """Expert Activation Skew = max / mean activation count over experts."""
+    c = np.asarray(counts, dtype=np.float64)
+    mean = c.mean() if c.size else 0.0
+    return dict(max=float(c.max()) if c.size else 0.0, mean=float(mean),
+                skew=float(c.max() / mean) if mean > 0 else 0.0,
+                touched=int((c > 0).sum()))
+
+
+def group_counts(counts: np.ndarray, groups: int) -> np.ndarray:
+    """Activation counts of `groups` contiguous equal expert groups (e // (E/groups))."""
+    c = np.asarray(counts)
+    return c.reshape(groups, -1).sum(axis=1)

@@ -1,0 +1,434 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each pin is a plain function so the planted-mistake test at the bottom can
+run the whole set against mutated copies of the oracle: every mutant must
+fail at least one pin. The pins use brute force on tiny inputs (pure-Python
+loops with math.fsum), closed forms, invariants of the layer, and the
+constants the page prints (tests/golden/step35_layer_constants.json).
+"""
+import json
+import math
+import os
+import struct
+from unittest import mock
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32(v: float) -> float:
+    return struct.unpack("f", struct.pack("f", v))[0]
+
+
+def rand_layer(rng, T, D, E, K, F, Fs, scale_r=1.0):
+    return dict(
+        x=rng.standard_normal((T, D)),
+        w_router=rng.standard_normal((E, D)) * scale_r,
+        w_gate=rng.standard_normal((E, F, D)) / math.sqrt(D),
+        w_up=rng.standard_normal((E, F, D)) / math.sqrt(D),
+        w_down=rng.standard_normal((E, D, F)) / math.sqrt(F),
+        s_gate=rng.standard_normal((Fs, D)) / math.sqrt(D) if Fs else None,
+        s_up=rng.standard_normal((Fs, D)) / math.sqrt(D) if Fs else None,
+        s_down=rng.standard_normal((D, Fs)) / math.sqrt(Fs) if Fs else None,
+        bias=None,
+    )
+
+
+# ------------------------------------------------------------ brute force ---
+
+def brute_route(x, wr, K, bias=None):
+    """Pure-Python router: fsum logits, exp/fsum softmax, K linear max scans."""
+    T, D = len(x), len(x[0])
+    E = len(wr)
+    idx, prob = [], []
+    for t in range(T):
+        l = [math.fsum(x[t][d] * wr[e][d] for d in range(D)) + (0.0 if bias is None else bias[e])
+             for e in range(E)]
+        m = max(l)
+        w = [math.exp(v - m) for v in l]
+        s = math.fsum(w)
+        p = [f32(v / s) for v in w]
+        taken, row_i, row_p = set(), [], []
+        for _ in range(K):
+            best = None
+            for e in range(E):           # first maximum wins: lower index on ties
+                if e not in taken and (best is None or p[e] > p[best]):
+                    best = e
+            taken.add(best)
+            row_i.append(best)
+            row_p.append(p[best])
+        idx.append(row_i)
+        prob.append(row_p)
+    return np.array(idx), np.array(prob, dtype=np.float32)
+
+
+def brute_ffn_row(xr, wg, wu, wd):
+    F, D = len(wg), len(xr)
+    h = []
+    for f in range(F):
+        g = math.fsum(wg[f][d] * xr[d] for d in range(D))
+        u = math.fsum(wu[f][d] * xr[d] for d in range(D))
+        h.append(g / (1.0 + math.exp(-g)) * u)
+    return [math.fsum(wd[d][f] * h[f] for f in range(F)) for d in range(D)]
+
+
+def brute_permute(idx, E):
+    """Per expert, walk the pairs in token-major order."""
+    T, K = idx.shape
+    sorted_token, dest = [], [None] * (T * K)
+    offsets = [0]
+    for e in range(E):
+        for t in range(T):
+            for j in range(K):
+                if idx[t, j] == e:
+                    dest[t * K + j] = len(sorted_token)
+                    sorted_token.append(t)
+        offsets.append(len(sorted_token))
+    return np.array(offsets), np.array(sorted_token), np.array(dest)
+
+
+# ------------------------------------------------------------------- pins ---
+
+def pin_route_bruteforce():
+    for seed, (T, D, E, K) in enumerate([(5, 4, 7, 3), (4, 6, 9, 9), (6, 3, 5, 1), (3, 8, 16, 8)]):
+        rng = np.random.default_rng(100 + seed)
+        x, wr = rng.standard_normal((T, D)), rng.standard_normal((E, D))
+        bias = rng.standard_normal(E) if seed % 2 else None
+        r = O.route(x, wr, K, bias)
+        bi, bp = brute_route(x.tolist(), wr.tolist(), K, None if bias is None else bias.tolist())
+        assert np.array_equal(r["idx"], bi), (seed, r["idx"], bi)
+        assert np.array_equal(r["prob"], bp), seed
+
+
+def pin_route_ties():
+    # experts 1 and 4 have identical router rows: equal probabilities, lower index first
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((6, 5))
+    wr = rng.standard_normal((6, 5)) * 0.1
+    wr[4] = wr[1]
+    wr[1] += 3.0 * np.sign(x.mean(axis=0))  # make the pair likely to be chosen
+    wr[4] = wr[1]
+    r = O.route(x, wr, 3)
+    for t in range(6):
+        row = list(r["idx"][t])
+        if 1 in row and 4 in row:
+            assert row.index(1) < row.index(4)
+        if 4 in row:
+            assert 1 in row, "index 4 chosen without its lower-index twin 1"
+    # all logits equal: the first K experts, each with probability fp32(1/E)
+    E, K = 10, 4
+    r = O.route(np.ones((2, 3)), np.zeros((E, 3)), K)
+    assert np.array_equal(r["idx"], np.tile(np.arange(K), (2, 1)))
+    assert np.all(r["prob"] == np.float32(f32(1.0 / E)))
+    assert np.all(r["gap"] == 0.0)
+
+
+def pin_route_properties():
+    rng = np.random.default_rng(3)
+    x, wr = rng.standard_normal((20, 16)), rng.standard_normal((12, 16))
+    r = O.route(x, wr, 5)
+    assert np.allclose(r["p64"].sum(axis=1), 1.0, atol=1e-12)
+    assert np.all(np.diff(r["prob"].astype(np.float64), axis=1) <= 0)
+    assert np.array_equal(r["prob"], np.take_along_axis(r["p32"], r["idx"], axis=1))
+    assert np.all(r["gap"] >= 0)
+    # K = E selects every expert once; gap is infinite
+    r = O.route(x, wr, 12)
+    assert np.array_equal(np.sort(r["idx"], axis=1), np.tile(np.arange(12), (20, 1)))
+    assert np.all(np.isinf(r["gap"]))
+    # huge logits stay finite (softmax is shift invariant)
+    r = O.route(x * 1e3, wr, 5)
+    assert np.all(np.isfinite(r["p64"])) and np.allclose(r["p64"].sum(axis=1), 1.0)
+
+
+def pin_route_bias():
+    rng = np.random.default_rng(5)
+    x, wr = rng.standard_normal((30, 8)), rng.standard_normal((10, 8)) * 0.3
+    b = rng.standard_normal(10)
+    r0, r1 = O.route(x, wr, 4, b), O.route(x, wr, 4, b + 2.5)   # shift: same routing
+    assert np.array_equal(r0["idx"], r1["idx"])
+    big = np.zeros(10)
+    big[6] = 60.0                                               # expert 6 always first
+    r = O.route(x, wr, 4, big)
+    assert np.all(r["idx"][:, 0] == 6) and np.all(r["prob"][:, 0] > 0.999)
+
+
+def pin_permute():
+    rng = np.random.default_rng(11)
+    for T, E, K in [(9, 5, 2), (13, 7, 3), (4, 6, 6), (1, 3, 1), (17, 12, 4)]:
+        idx = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+        p = O.permute(idx, E)
+        off, st, de = brute_permute(idx, E)
+        assert np.array_equal(p["offsets"], off)
+        assert np.array_equal(p["sorted_token"], st)
+        assert np.array_equal(p["dest"], de)
+        assert p["counts"].sum() == T * K and p["offsets"][-1] == T * K
+        assert np.array_equal(np.sort(p["dest"]), np.arange(T * K))      # bijection
+        for e in range(E):
+            seg = p["sorted_token"][p["offsets"][e]:p["offsets"][e + 1]]
+            assert np.all(np.diff(seg) > 0)                               # token order
+        # unpermute(permute(rows)) is the identity
+        rows = rng.standard_normal((T, 3))
+        perm = rows[p["sorted_token"]]
+        back = perm[p["dest"]].reshape(T, K, 3)
+        assert np.array_equal(back, np.repeat(rows[:, None], K, axis=1))
+
+
+def pin_ffn_closed_form():
+    # one input, one hidden unit: y = w_d * silu(w_g x) * (w_u x)
+    y = O.swiglu_ffn(np.array([[2.0]]), np.array([[0.5]]), np.array([[3.0]]), np.array([[-1.0]]))
+    silu1 = 1.0 / (1.0 + math.exp(-1.0))
+    assert math.isclose(y[0, 0], -6.0 * silu1, rel_tol=1e-15)
+    # gate weights zero: silu(0) = 0 -> output zero
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((3, 4))
+    z = O.swiglu_ffn(x, np.zeros((5, 4)), rng.standard_normal((5, 4)), rng.standard_normal((4, 5)))
+    assert np.all(z == 0)
+    # strongly positive gate: silu(g) = g to double precision, the FFN is W_d((W_g x)*(W_u x))
+    wg = np.abs(rng.standard_normal((5, 4))) + 50.0
+    xp = np.abs(x) + 1.0
+    wu, wd = rng.standard_normal((5, 4)), rng.standard_normal((4, 5))
+    lin = ((xp @ wg.T) * (xp @ wu.T)) @ wd.T
+    assert np.allclose(O.swiglu_ffn(xp, wg, wu, wd), lin, rtol=1e-13, atol=0)
+
+
+def pin_ffn_bruteforce():
+    rng = np.random.default_rng(9)
+    D, F = 5, 3
+    x = rng.standard_normal((4, D))
+    wg, wu, wd = rng.standard_normal((F, D)), rng.standard_normal((F, D)), rng.standard_normal((D, F))
+    y = O.swiglu_ffn(x, wg, wu, wd)
+    for t in range(4):
+        ref = brute_ffn_row(x[t].tolist(), wg.tolist(), wu.tolist(), wd.tolist())
+        assert np.allclose(y[t], ref, rtol=1e-12, atol=1e-14)
+    # grouped: segment e uses expert e's weights
+    E = 3
+    W = [(rng.standard_normal((F, D)), rng.standard_normal((F, D)), rng.standard_normal((D, F)))
+         for _ in range(E)]
+    offsets = [0, 2, 2, 5]
+    xr = rng.standard_normal((5, D))
+    y = O.grouped_ffn(xr, offsets, lambda e: W[e])
+    for r, e in [(0, 0), (1, 0), (2, 2), (3, 2), (4, 2)]:
+        ref = brute_ffn_row(xr[r].tolist(), *(w.tolist() for w in W[e]))
+        assert np.allclose(y[r], ref, rtol=1e-12, atol=1e-14)
+
+
+def pin_layer_worked_example():
+    """D=2, E=3, K=2, F=Fs=1, one token x=(1,0); every number by hand.
+
+    logits (0, ln 2, ln 3) -> p = (1/6, 1/3, 1/2) -> top-2 = (2, 1).
+    expert 1: g=1, u=2 -> h = 2 silu(1); y1 = (h, -h)
+    expert 2: g=-1, u=1 -> h = silu(-1); y2 = (2h, h/2)
+    shared: g=2, u=1 -> h = silu(2); ys = (h, h)
+    out = ys + f32(1/2) y2 + f32(1/3) y1
+    """
+    x = np.array([[1.0, 0.0]])
+    wr = np.array([[0.0, 0.0], [math.log(2.0), 0.0], [math.log(3.0), 0.0]])
+    wg = np.array([[[0.0, 0.0]], [[1.0, 0.0]], [[-1.0, 0.0]]])
+    wu = np.array([[[0.0, 0.0]], [[2.0, 0.0]], [[1.0, 0.0]]])
+    wd = np.array([[[0.0], [0.0]], [[1.0], [-1.0]], [[2.0], [0.5]]])
+    L = dict(x=x, w_router=wr, w_gate=wg, w_up=wu, w_down=wd,
+             s_gate=np.array([[2.0, 0.0]]), s_up=np.array([[1.0, 0.0]]),
+             s_down=np.array([[1.0], [1.0]]), bias=None)
+    r = O.layer_forward(x, O.LayerWeights.from_dict(L), 2)
+    assert list(r["idx"][0]) == [2, 1]
+    assert r["prob"][0, 0] == np.float32(0.5) and r["prob"][0, 1] == np.float32(f32(1 / 3))
+    s = lambda g: g / (1.0 + math.exp(-g))
+    p1, p2 = f32(1 / 3), 0.5
+    want = [s(2.0) + p2 * 2 * s(-1.0) + p1 * 2 * s(1.0),
+            s(2.0) + p2 * 0.5 * s(-1.0) - p1 * 2 * s(1.0)]
+    assert np.allclose(r["out"][0], want, rtol=1e-12, atol=1e-15)
+
+
+def pin_layer_special_cases():
+    rng = np.random.default_rng(21)
+    T, D, E, K, F = 12, 6, 5, 2, 4
+    L = rand_layer(rng, T, D, E, K, F, F)
+    W = O.LayerWeights.from_dict(L)
+    base = O.layer_forward(L["x"], W, K)
+    ys = O.swiglu_ffn(L["x"], L["s_gate"], L["s_up"], L["s_down"])
+    # routed experts silenced: output is the shared expert alone
+    Lz = dict(L, w_down=np.zeros_like(L["w_down"]))
+    assert np.array_equal(O.layer_forward(L["x"], O.LayerWeights.from_dict(Lz), K)["out"], ys)
+    # all experts identical: out = ys + (sum_k prob) FFN(x)
+    Li = dict(L, w_gate=np.repeat(L["w_gate"][:1], E, 0), w_up=np.repeat(L["w_up"][:1], E, 0),
+              w_down=np.repeat(L["w_down"][:1], E, 0))
+    ri = O.layer_forward(L["x"], O.LayerWeights.from_dict(Li), K)
+    f0 = O.swiglu_ffn(L["x"], L["w_gate"][0], L["w_up"][0], L["w_down"][0])
+    want = ys + ri["prob"].astype(np.float64).sum(axis=1, keepdims=True) * f0
+    assert np.allclose(ri["out"], want, rtol=1e-12, atol=1e-13)
+    # K = E: the dense mixture sum_e p32_e FFN_e(x) + ys, no permutation involved
+    rd = O.layer_forward(L["x"], W, E)
+    dense = ys.copy()
+    for e in range(E):
+        dense += rd["p32"][:, e:e + 1].astype(np.float64) * O.swiglu_ffn(
+            L["x"], L["w_gate"][e], L["w_up"][e], L["w_down"][e])
+    assert np.allclose(rd["out"], dense, rtol=1e-12, atol=1e-13)
+    # permuting tokens permutes output rows
+    perm = rng.permutation(T)
+    rp = O.layer_forward(L["x"][perm], W, K)
+    assert np.allclose(rp["out"], base["out"][perm], rtol=1e-12, atol=1e-13)
+    # relabelling experts (router rows move with their weights) leaves the output unchanged
+    q = rng.permutation(E)
+    Lq = dict(L, w_router=L["w_router"][q], w_gate=L["w_gate"][q], w_up=L["w_up"][q],
+              w_down=L["w_down"][q])
+    rq = O.layer_forward(L["x"], O.LayerWeights.from_dict(Lq), K)
+    assert np.allclose(rq["out"], base["out"], rtol=1e-12, atol=1e-13)
+    # sampled rows agree with the full layer
+    rr = O.layer_rows(L["x"], W, K, [0, 5, 11])
+    assert np.allclose(rr["out_rows"], base["out"][[0, 5, 11]], rtol=1e-12, atol=1e-13)
+
+
+def pin_page_constants():
+    """The page's structural numbers, and the width reading they force."""
+    g = json.load(open(os.path.join(GOLDEN, "step35_layer_constants.json")))["values"]
+    v = {k: d["value"] for k, d in g.items()}
+    import synth
+    for name in ("decode", "prefill", "skew", "full"):
+        s = synth.spec(name)
+        assert (s.E, s.K, s.D) == (v["routed_experts_per_layer"], v["top_k"], v["d_model"])
+        assert s.Fs > 0 and v["shared_experts_per_layer"] == 1
+    assert v["top_k"] + v["shared_experts_per_layer"] == v["experts_run_per_token"]
+    assert round(100 * v["top_k"] / v["routed_experts_per_layer"], 2) == v["routed_fraction_percent"]
+    assert v["ep_groups"] * v["experts_per_group"] == v["routed_experts_per_layer"]
+    # expert width: 1280 fits the 196.81B / 11B totals; the literal 4096 cannot
+    D, E, L = v["d_model"], v["routed_experts_per_layer"], v["moe_layers"]
+    moe = lambda F: L * ((E + 1) * 3 * D * F + E * D) / 1e9
+    act = lambda F: L * 9 * 3 * D * F / 1e9
+    assert moe(1280) < v["total_params_billion"] < moe(1280) + 10
+    assert act(1280) < v["active_params_billion"]
+    assert moe(4096) > 3 * v["total_params_billion"]
+    assert synth.spec("prefill").F == 1280
+
+
+PINS = [pin_route_bruteforce, pin_route_ties, pin_route_properties, pin_route_bias, pin_permute,
+        pin_ffn_closed_form, pin_ffn_bruteforce, pin_layer_worked_example,
+        pin_layer_special_cases, pin_page_constants]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin()
+
+
+# --------------------------------------------------------- planted mistakes ---
+
+def _renormalised(p32, k):
+    idx, prob, gap = _orig["select_topk"](p32, k)
+    return idx, (prob / prob.sum(axis=1, keepdims=True)).astype(np.float32), gap
+
+
+def _ties_high(p32, k):
+    E = p32.shape[1]
+    order = E - 1 - np.argsort(-p32[:, ::-1], axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int32)
+    prob = np.take_along_axis(p32, order[:, :k], axis=1).astype(np.float32)
+    return idx, prob, np.zeros(p32.shape[0])
+
+
+def _softmax_after_topk(x, w_router, k, bias=None):
+    l = O.router_logits(x, w_router, bias)
+    order = np.argsort(-l, axis=1, kind="stable")[:, :k]
+    top = np.take_along_axis(l, order, axis=1)
+    p = O.softmax(top).astype(np.float32)
+    p32 = O.softmax(l).astype(np.float32)
+    return dict(logits=l, p64=O.softmax(l), p32=p32, idx=order.astype(np.int32), prob=p,
+                gap=np.ones(len(l)))
+
+
+def _no_max_sub(logits):
+    w = np.exp(logits)
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def _swapped_gate_up(x_rows, w_gate, w_up, w_down):
+    return _orig["swiglu_ffn"](x_rows, w_up, w_gate, w_down)
+
+
+def _sigmoid_not_silu(g):
+    return 1.0 / (1.0 + np.exp(-g))
+
+
+def _unstable_permute(idx, n_experts):
+    p = _orig["permute"](idx, n_experts)
+    st, de = p["sorted_token"].copy(), p["dest"].copy()
+    off = p["offsets"]
+    for e in range(n_experts):                  # reverse token order inside each segment
+        a, b = off[e], off[e + 1]
+        st[a:b] = st[a:b][::-1]
+    inv = np.empty_like(de)
+    for r in range(len(de)):
+        inv[de[r]] = r
+    T, k = idx.shape
+    pos = {}
+    for r, t in enumerate(st):
+        pos.setdefault(int(t), []).append(r)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            rows = [r for r in pos[t] if off[e] <= r < off[e + 1]]
+            de[t * k + j] = rows[0]
+    return dict(p, sorted_token=st, dest=de)
+
+
+def _inclusive_offsets(idx, n_experts):
+    p = _orig["permute"](idx, n_experts)
+    return dict(p, offsets=np.concatenate([np.cumsum(p["counts"]), [idx.size]]))
+
+
+def _kmajor_dest(ys, y_perm, dest, prob):
+    T, k = np.asarray(prob).shape
+    return _orig["combine"](ys, y_perm, np.asarray(dest).reshape(k, T).T.reshape(-1), prob)
+
+
+def _drop_shared(ys, y_perm, dest, prob):
+    return _orig["combine"](None, y_perm, dest, prob)
+
+
+def _drop_bias(x, w_router, bias=None):
+    return _orig["router_logits"](x, w_router, None)
+
+
+def _transposed_down(x_rows, w_gate, w_up, w_down):
+    g = O.as_f64(x_rows) @ O.as_f64(w_gate).T
+    u = O.as_f64(x_rows) @ O.as_f64(w_up).T
+    h = O.silu(g) * u
+    wd = O.as_f64(w_down)
+    if wd.shape[0] == wd.shape[1]:
+        return h @ wd
+    return h @ wd.reshape(wd.shape[1], wd.shape[0])   # plausible reshape-for-transpose slip
+
+
+_orig = {n: getattr(O, n) for n in ("select_topk", "swiglu_ffn", "permute", "combine",
+                                    "router_logits", "softmax", "silu", "route")}
+
+MUTANTS = {
+    "renormalised_topk": ("select_topk", _renormalised),
+    "ties_to_higher_index": ("select_topk", _ties_high),
+    "softmax_after_selection": ("route", _softmax_after_topk),
+    "softmax_without_max_subtraction": ("softmax", _no_max_sub),
+    "gate_up_swapped": ("swiglu_ffn", _swapped_gate_up),
+    "sigmoid_instead_of_silu": ("silu", _sigmoid_not_silu),
+    "unstable_permute": ("permute", _unstable_permute),
+    "inclusive_offsets": ("permute", _inclusive_offsets),
+    "choice_major_dest": ("combine", _kmajor_dest),
+    "shared_expert_dropped": ("combine", _drop_shared),
+    "router_bias_dropped": ("router_logits", _drop_bias),
+    "down_projection_transposed": ("swiglu_ffn", _transposed_down),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    attr, fn = MUTANTS[name]
+    failed = []
+    with mock.patch.object(O, attr, fn), np.errstate(all="ignore"):
+        for pin in PINS:
+            try:
+                pin()
+            except AssertionError:     # a crash does not count: the pin must notice
+                failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
