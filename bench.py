@@ -1,0 +1,237 @@
+"""Benchmark of one sparse-MoE FFN layer (Step 3.5 Flash shape) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skew|full|tiny]
+
+A step is one moe_layer_forward over one batch of synthetic tokens already
+resident in HBM: router linear + softmax + top-8, permutation, routed and
+shared expert SwiGLU FFNs, weighted combine. The timed region holds exactly
+K steps; each step is bracketed by HIP events on the stream the library
+launches on, with a 512 MiB write between steps (outside the events) so the
+256 MiB Infinity Cache does not keep the previous step's experts.
+
+One JSON line is printed. Besides the layer throughput it carries:
+  roofline      the dominant kernel (expert gate/up projection with the
+                SwiGLU epilogue, timed alone through moe_expert_gate_up with
+                the layer's exact arguments): algorithmic bytes or flops per
+                launch / average launch time, against the MI355X peak;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload;
+  secondary     the prefill workload (T=8192) measured the same way, for the
+                MFMA-side figure, unless --no-secondary.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s on 1 MI355X; % bf16 MFMA peak (prefill) / % HBM BW (decode)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector, TFLOP/s
+FLUSH_BYTES = 512 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "skew", "full"])
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8)
+    ap.add_argument("--no-flush", action="store_true")
+    return ap.parse_args()
+
+
+class Flusher:
+    def __init__(self, enabled: bool):
+        import torch
+        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") if enabled else None
+        self.i = 0
+
+    def __call__(self):
+        if self.buf is not None:
+            self.i += 1
+            self.buf.fill_(float(self.i))
+
+
+def timed(fn, steps: int, warmup: int, flush: Flusher):
+    """Run fn warmup times, then time `steps` calls with HIP events; returns per-call ms list and wall s."""
+    import torch
+    for _ in range(warmup):
+        flush()
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush()
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)], wall
+
+
+def layer_flops_bytes(spec, counts):
+    """Algorithmic flops and HBM bytes of one layer call (touched experts only)."""
+    import numpy as np
+    T, D, E, K, F, Fs = spec.T, spec.D, spec.E, spec.K, spec.F, spec.Fs
+    es = 2 if spec.dtype == "bf16" else 4
+    touched = int((np.asarray(counts) > 0).sum())
+    flops = 2 * T * D * E + 2 * T * K * 3 * D * F + 2 * T * 3 * D * Fs
+    wbytes = (touched * 3 * D * F + 3 * D * Fs + E * D) * es
+    abytes = T * D * es * 2  # x in, out
+    return flops, wbytes + abytes, touched
+
+
+def measure(spec, steps, warmup, flush_on):
+    import numpy as np
+    import torch
+
+    import synth
+    import top_routed_expert_amd as moe
+
+    L = synth.make_layer(spec, "cuda")
+    cfg = moe.config_for(spec)
+    flush = Flusher(flush_on)
+    dev = L["x"].device
+    T, D, E, K, F = spec.T, spec.D, spec.E, spec.K, spec.F
+    # --- whole layer -------------------------------------------------------
+    ws = moe.Workspace(cfg, T, dev)
+    wt = moe.weights_struct(cfg, L)
+    out = torch.empty((T, D), dtype=cfg.odtype, device=dev)
+    layer = lambda: moe.layer_forward(cfg, L["x"], L, out=out, workspace=ws, weights=wt)
+    ms, wall = timed(layer, steps, warmup, flush)
+    ms_step = float(np.mean(ms))
+    # routing of this batch (outside the timed region) for the work accounting
+    idx, prob = moe.route(cfg, L["x"], L["w_router"], L["bias"])
+    offs, st, dest = moe.permute(cfg, idx)
+    counts = np.diff(offs.cpu().numpy())
+    flops, nbytes, touched = layer_flops_bytes(spec, counts)
+    res = dict(ms=ms_step, ms_min=float(np.min(ms)), wall=wall, tokens_per_s=T / (ms_step * 1e-3),
+               touched=touched, layer_tflops=flops / (ms_step * 1e-3) / 1e12,
+               layer_gbs=nbytes / (ms_step * 1e-3) / 1e9, skew=float(counts.max() / counts.mean()))
+    # --- dominant kernel: expert gate/up + SwiGLU, the layer's own arguments -
+    P = T * K
+    fused = spec.Fs == spec.F and spec.Fs > 0
+    offs_ext = torch.cat([offs, torch.tensor([P + T], dtype=torch.int32, device=dev)]) if fused else offs
+    n_rows = P + (T if fused else 0)
+    h = torch.empty((n_rows, F), dtype=cfg.dtype, device=dev)
+    gws = torch.empty(moe.lib().moe_expert_workspace_bytes(
+        __import__("ctypes").byref(cfg.c()), E + (1 if fused else 0), n_rows, F), dtype=torch.uint8, device=dev)
+    gate_up = lambda: moe.expert_gate_up(cfg, offs_ext, L["x"], L["w_gate"], L["w_up"], gather=st, n_rows=n_rows,
+                                         s_gate=L["s_gate"] if fused else None, s_up=L["s_up"] if fused else None,
+                                         h=h, ws=gws)
+    kms, _ = timed(gate_up, steps, warmup, flush)
+    k_ms = float(np.mean(kms))
+    es = 2 if spec.dtype == "bf16" else 4
+    k_experts = touched + (1 if fused else 0)
+    k_bytes = k_experts * 2 * F * D * es + T * D * es + n_rows * F * es
+    k_flops = 2 * n_rows * 2 * F * D
+    t_hbm = k_bytes / (HBM_PEAK_GBS * 1e9)
+    peak_tf = MFMA_BF16_PEAK_TFLOPS if spec.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    t_mfma = k_flops / (peak_tf * 1e12)
+    gbs = k_bytes / (k_ms * 1e-3) / 1e9
+    tfs = k_flops / (k_ms * 1e-3) / 1e12
+    if t_hbm >= t_mfma:
+        roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        roof = dict(bound="mfma", achieved=round(tfs, 1), peak=peak_tf, unit="TFLOP/s", frac=round(tfs / peak_tf, 4))
+    roof.update(traffic=None, kernel="gemm_bf16_mfma<EPI_SWIGLU> (expert gate/up + SwiGLU)",
+                launch_ms=round(k_ms, 4), algorithmic_bytes=int(k_bytes), algorithmic_flops=int(k_flops),
+                experts_read=k_experts, mfma_frac=round(tfs / peak_tf, 4), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+    res["roofline"] = roof
+    res["L"] = L
+    return res
+
+
+def cpu_baseline(spec, L, n_tokens: int):
+    """The oracle, as it stands, on the first n_tokens tokens of the workload (single thread)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import moe_oracle as O
+
+    n = min(n_tokens, spec.T)
+    x = L["x"][:n].cpu()
+    host = lambda t: None if t is None else t.cpu()
+    W = O.LayerWeights(host(L["w_router"]), lambda e: (host(L["w_gate"][e]), host(L["w_up"][e]), host(L["w_down"][e])),
+                       (lambda: (host(L["s_gate"]), host(L["s_up"]), host(L["s_down"]))) if spec.Fs else None,
+                       host(L.get("bias")))
+    prev = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            r = O.layer_forward(x, W, spec.K)
+            dt = time.perf_counter() - t0
+    finally:
+        torch.set_num_threads(prev)
+    assert np.all(np.isfinite(r["out"]))
+    return dict(value=round(n / dt, 3), unit="tokens/s", cores=1, kind="oracle",
+                sample=f"first {n} of the {spec.T} tokens of the {spec.name} batch, whole layer "
+                       f"(numpy fp64, expert weights copied to host as used), {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+
+    spec = synth.spec(args.workload)
+    print(f"[bench] workload={spec.name} T={spec.T} steps={args.steps} warmup={args.warmup}", file=sys.stderr,
+          flush=True)
+    res = measure(spec, args.steps, args.warmup, not args.no_flush)
+    print(f"[bench] layer {res['ms']:.4f} ms/step; gate/up kernel {res['roofline']['launch_ms']:.4f} ms",
+          file=sys.stderr, flush=True)
+    line = {
+        "metric": METRIC, "value": round(res["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if spec.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": spec.name, "tokens": spec.T, "d_model": spec.D, "routed_experts": spec.E,
+                   "top_k": spec.K, "d_expert": spec.F, "shared_experts": 1 if spec.Fs else 0,
+                   "d_shared": spec.Fs, "router_bias": "zipf" if spec.skew else "none",
+                   "parallelism": "single-gpu"},
+        "roofline": res["roofline"],
+        "layer": {"ms_min": round(res["ms_min"], 5), "experts_touched": res["touched"],
+                  "expert_load_skew": round(res["skew"], 3), "tflops": round(res["layer_tflops"], 2),
+                  "gbs": round(res["layer_gbs"], 1),
+                  "mfma_frac": round(res["layer_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                  "hbm_frac": round(res["layer_gbs"] / HBM_PEAK_GBS, 4), "timed_wall_s": round(res["wall"], 3),
+                  "cache_flush_between_steps": not args.no_flush},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(spec, res["L"], args.cpu_sample_tokens)
+    del res["L"]
+    if not args.no_secondary and spec.name != "prefill":
+        torch.cuda.empty_cache()
+        sec = synth.spec("prefill")
+        print(f"[bench] secondary workload={sec.name} T={sec.T}", file=sys.stderr, flush=True)
+        r2 = measure(sec, args.steps, args.warmup, not args.no_flush)
+        line["secondary"] = {"workload": sec.name, "tokens": sec.T, "value": round(r2["tokens_per_s"], 1),
+                             "unit": "tokens/s", "ms_per_step": round(r2["ms"], 5),
+                             "layer_mfma_frac": round(r2["layer_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "layer_tflops": round(r2["layer_tflops"], 2), "roofline": r2["roofline"]}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

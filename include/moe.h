@@ -1,0 +1,205 @@
+/*
+ * moe.h - C ABI of a sparse Mixture-of-Experts FFN layer on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer is the one the page "Step3.5 Flash 大模型技术深度解析：稀疏 MoE、
+ * 混合注意力与 MTP 的高效推理革命" states in section 3.2.1 (per MoE layer: 288
+ * routed experts, each an independent FFN, and 1 always-active shared
+ * expert; model width d_model = 4096) and section 3.2.2 (Top-8 routing: a
+ * linear layer plus softmax gives every routed expert a probability, the 8
+ * most probable routed experts and the shared expert run, and their outputs
+ * are summed with weights). For token x:
+ *
+ *   p      = softmax(W_r x + b)                 over all E routed experts
+ *   S      = the K most probable experts        (ties: lower index first)
+ *   out(x) = FFN_s(x) + sum_{e in S} p_e FFN_e(x)
+ *   FFN(x) = W_d (silu(W_g x) * (W_u x))        (SwiGLU, no biases)
+ *
+ * The selected probabilities are used as they are (no renormalisation over
+ * S); the shared expert has weight 1; no token is dropped (no capacity).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is DEVICE memory owned by the caller, dense
+ *    row-major, 16-byte aligned. The library never allocates, frees or keeps
+ *    a pointer past the call; it holds no mutable global state.
+ *  - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *    null stream) and returns; results are valid once the stream is
+ *    synchronised. No call copies device data to the host or synchronises.
+ *  - Arguments are checked on the host before anything is enqueued; a
+ *    failed check returns a non-zero moe_status and enqueues nothing.
+ *    moe_last_error() then describes the failure (per thread).
+ *  - T == 0 (no tokens / rows) is a valid no-op returning MOE_OK.
+ *  - Device-side index inputs (expert ids, offsets, row maps) supplied by
+ *    the caller are clamped to their valid ranges inside the kernels, so a
+ *    malformed index never causes an out-of-bounds access; the results for
+ *    such entries are unspecified.
+ *  - Routing and permutation results are bit-deterministic. Floating-point
+ *    outputs are deterministic for a fixed configuration (no atomics).
+ *
+ * dtype: MOE_BF16 -> x and all weights bfloat16, products accumulated in
+ * fp32 on the matrix cores; MOE_F32 -> everything fp32.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL                    */
+  MOE_ERR_SHAPE = 2,       /* a size is negative, zero where it may not be, or inconsistent */
+  MOE_ERR_UNSUPPORTED = 3, /* dtype or size outside what the kernels implement */
+  MOE_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than *_workspace_bytes */
+  MOE_ERR_MISALIGNED = 5,  /* a pointer is not 16-byte aligned             */
+  MOE_ERR_HIP = 6          /* the HIP runtime reported an error (launch)   */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Shape of one layer (section 3.2.1 / 3.2.2 of the page above). */
+typedef struct {
+  int32_t d_model;   /* D: token width (4096 on the page)                    */
+  int32_t n_experts; /* E: routed experts (288); 1 <= E <= 1024              */
+  int32_t top_k;     /* K: routed experts per token (8); 1 <= K <= min(E,64) */
+  int32_t d_expert;  /* F: SwiGLU width of a routed expert                   */
+  int32_t d_shared;  /* Fs: SwiGLU width of the shared expert; 0 = none      */
+  int32_t dtype;     /* moe_dtype of x and of every weight                   */
+  int32_t out_dtype; /* moe_dtype of the layer output                        */
+} moe_config;
+
+/* The layer's weights (device pointers, row-major).
+ *   w_router    [E, D]      router linear layer
+ *   router_bias [E] fp32 or NULL, added to the logits before the softmax
+ *   w_gate      [E, F, D]   routed experts, gate projection
+ *   w_up        [E, F, D]   routed experts, up projection
+ *   w_down      [E, D, F]   routed experts, down projection
+ *   s_gate      [Fs, D], s_up [Fs, D], s_down [D, Fs]: the shared expert
+ *               (ignored when d_shared == 0).                              */
+typedef struct {
+  const void* w_router;
+  const float* router_bias;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* s_gate;
+  const void* s_up;
+  const void* s_down;
+} moe_weights;
+
+/* Workspace queries. They return the bytes the matching entry point needs
+ * in its `ws` argument, or SIZE_MAX when the configuration is invalid. */
+size_t moe_route_workspace_bytes(const moe_config* cfg, int64_t T);
+size_t moe_permute_workspace_bytes(const moe_config* cfg, int64_t T);
+size_t moe_grouped_ffn_workspace_bytes(const moe_config* cfg, int32_t n_groups, int64_t n_rows,
+                                       int32_t d_ff);
+size_t moe_layer_workspace_bytes(const moe_config* cfg, int64_t T);
+
+/* Router (section 3.2.2, steps 1-2): logits = x W_r^T + b, softmax over all
+ * E experts in fp32, then the K most probable experts per token.
+ *   x          [T, D] dtype
+ *   w_router   [E, D] dtype;  bias [E] fp32 or NULL
+ *   topk_idx   [T, K] int32 out: expert ids, probability descending,
+ *              equal probabilities ordered by lower expert id
+ *   topk_prob  [T, K] fp32 out: their softmax probabilities (not renormalised)
+ *   gap        [T] fp32 out or NULL: p of the K-th choice minus p of the
+ *              (K+1)-th (+inf when K == E); small gaps flag near-ties
+ *   ws         >= moe_route_workspace_bytes(cfg, T) bytes                   */
+moe_status moe_route(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                     const float* bias, int32_t* topk_idx, float* topk_prob, float* gap,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Permutation of the T*K (token, choice) pairs into per-expert segments
+ * (the grouping that lets every expert run its FFN as one dense block;
+ * section 3.2.2 step 2). Pairs are taken in token-major order and kept in
+ * that order inside a segment (stable), so the result is unique.
+ *   topk_idx     [T, K] int32 in (ids outside [0,E) are not placed: their
+ *                dest is -1 and they are not counted)
+ *   offsets      [E+1] int32 out: segment e is rows offsets[e]..offsets[e+1]-1
+ *   sorted_token [T*K] int32 out: token of each permuted row
+ *   dest         [T*K] int32 out: permuted row of pair (t, j) at t*K+j
+ *   x, x_perm    optional pair (both NULL or both set): x [T, D] dtype is
+ *                gathered into x_perm [T*K, D] in permuted row order
+ *   ws           >= moe_permute_workspace_bytes(cfg, T) bytes               */
+moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx,
+                       int32_t* offsets, int32_t* sorted_token, int32_t* dest,
+                       const void* x, void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Grouped SwiGLU expert FFN over row segments (section 3.2.1: every expert
+ * is an independent FFN). Group g (0 <= g < n_groups) owns rows
+ * offsets[g]..offsets[g+1]-1 and uses weights
+ *   w_gate + g*d_ff*D, w_up + g*d_ff*D  ([d_ff, D] each, dtype)
+ *   w_down + g*D*d_ff                   ([D, d_ff], dtype)
+ * Row r reads input row gather[r] of x (gather NULL: row r of x) and writes
+ *   y[r] = W_d (silu(W_g x) * (W_u x))       y: [n_rows, D] fp32
+ * The SwiGLU activation is rounded once to dtype before the down projection.
+ * Rows outside every segment are left unwritten.
+ *   offsets   [n_groups+1] int32, non-decreasing, offsets[n_groups] <= n_rows
+ *   x         [n_x_rows, D] dtype;  gather [n_rows] int32 or NULL
+ *   ws        >= moe_grouped_ffn_workspace_bytes(cfg, n_groups, n_rows, d_ff) bytes
+ * The shared expert is the case n_groups = 1, offsets = {0, T}, gather NULL. */
+moe_status moe_grouped_ffn(const moe_config* cfg, int32_t n_groups, int64_t n_rows,
+                           const int32_t* offsets, const void* x, int64_t n_x_rows,
+                           const int32_t* gather, const void* w_gate, const void* w_up,
+                           const void* w_down, int32_t d_ff, float* y, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* The two halves of moe_grouped_ffn, for callers that keep the SwiGLU
+ * activation or run the halves apart. Groups 0..n_groups-1 use the stacked
+ * weights as in moe_grouped_ffn; when s_gate/s_up (s_down) is non-NULL one
+ * more group, n_groups, owns rows offsets[n_groups]..offsets[n_groups+1]-1
+ * and uses that single expert's weights ([d_ff, D] / [D, d_ff]), so
+ * `offsets` then has n_groups+2 entries (the layer runs its shared expert
+ * this way, in the same launch as the routed experts).
+ *
+ * moe_expert_gate_up: h[r] = dtype(silu(W_g x_r) * (W_u x_r)), h [n_rows, d_ff]
+ *   where x_r = x[gather[r]] for r < n_gather and x[r - n_gather] otherwise
+ *   (gather may be NULL only with n_gather == 0).
+ * moe_expert_down: y[r] = W_d h[r] (fp32), y [n_rows, D].
+ *   ws >= moe_expert_workspace_bytes(cfg, n_groups (+1 with the extra group), n_rows, d_ff) */
+size_t moe_expert_workspace_bytes(const moe_config* cfg, int32_t n_groups, int64_t n_rows, int32_t d_ff);
+
+moe_status moe_expert_gate_up(const moe_config* cfg, int32_t n_groups, int64_t n_rows,
+                              const int32_t* offsets, const void* x, int64_t n_x_rows,
+                              const int32_t* gather, int64_t n_gather, const void* w_gate,
+                              const void* w_up, const void* s_gate, const void* s_up, int32_t d_ff,
+                              void* h, void* ws, size_t ws_bytes, void* stream);
+
+moe_status moe_expert_down(const moe_config* cfg, int32_t n_groups, int64_t n_rows,
+                           const int32_t* offsets, const void* h, const void* w_down,
+                           const void* s_down, int32_t d_ff, float* y, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Weighted combine (section 3.2.2, step 3):
+ *   out[t] = y_shared[t] + sum_{j=0..K-1} topk_prob[t,j] * y_perm[dest[t*K+j]]
+ * summed in fp32 in that order, rounded once to out_dtype.
+ *   y_perm [T*K, D] fp32; dest [T*K] int32 (-1: pair skipped);
+ *   topk_prob [T, K] fp32; y_shared [T, D] fp32 or NULL; out [T, D] out_dtype */
+moe_status moe_combine(const moe_config* cfg, int64_t T, const float* y_perm, const int32_t* dest,
+                       const float* topk_prob, const float* y_shared, void* out, void* stream);
+
+/* The whole layer: route, permute, routed + shared expert FFNs, combine.
+ *   x     [T, D] dtype;   out [T, D] out_dtype
+ *   topk_idx_out [T, K], topk_prob_out [T, K], offsets_out [E+1]: optional
+ *   copies of the routing decision (NULL to skip)
+ *   ws    >= moe_layer_workspace_bytes(cfg, T) bytes                        */
+moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x,
+                             const moe_weights* w, void* out, int32_t* topk_idx_out,
+                             float* topk_prob_out, int32_t* offsets_out, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status s);
+
+/* Text of the last failed check or HIP error in the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

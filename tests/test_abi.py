@@ -1,0 +1,194 @@
+"""Host-side tests of the C ABI (no GPU): the library loads and exports every
+function include/moe.h declares, status strings, workspace queries, and every
+argument check that must fail before anything is enqueued."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import top_routed_expert_amd as moe
+from top_routed_expert_amd import moe as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, NULL, SHAPE, UNSUP, WS, MISALIGNED, HIP = range(7)
+
+
+def header_functions() -> list[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def cfg(**kw) -> M.MoeConfig:
+    c = dict(d_model=256, n_experts=16, top_k=4, d_expert=128, d_shared=128, dtype=moe.BF16, out_dtype=moe.BF16)
+    c.update(kw)
+    return M.MoeConfig(**c)
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails its checks first
+
+
+def test_exports_every_declared_function():
+    L = moe.lib()
+    names = header_functions()
+    assert len(names) == 14, names
+    for n in names:
+        assert hasattr(L, n), f"libmoe.so does not export {n}"
+    assert set(names) == set(M._SIGS), "binding signatures out of sync with the header"
+
+
+def test_status_strings():
+    L = moe.lib()
+    seen = set()
+    for s in range(7):
+        txt = L.moe_status_string(s).decode()
+        assert txt and txt != "unknown status"
+        seen.add(txt)
+    assert len(seen) == 7
+    assert L.moe_status_string(99).decode() == "unknown status"
+
+
+def test_workspace_queries():
+    L = moe.lib()
+    c = cfg()
+    r = L.moe_route_workspace_bytes(ctypes.byref(c), 100)
+    assert r >= 100 * 16 * 4
+    p = L.moe_permute_workspace_bytes(ctypes.byref(c), 100)
+    assert p >= 100 * 4 * 4 + 16 * 4
+    f = L.moe_grouped_ffn_workspace_bytes(ctypes.byref(c), 16, 400, 128)
+    assert f >= 400 * 128 * 2
+    lay = L.moe_layer_workspace_bytes(ctypes.byref(c), 100)
+    assert lay >= (100 * 4 + 100) * 256 * 4  # fp32 expert outputs of routed + shared rows
+    assert L.moe_layer_workspace_bytes(ctypes.byref(c), 0) >= 0
+    # monotone in T
+    assert L.moe_layer_workspace_bytes(ctypes.byref(c), 1000) > lay
+    bad = [cfg(top_k=17), cfg(n_experts=0), cfg(n_experts=2000), cfg(dtype=7), cfg(d_model=-1), cfg(top_k=65, n_experts=100)]
+    for b in bad:
+        assert L.moe_layer_workspace_bytes(ctypes.byref(b), 10) == M.SIZE_MAX
+        assert L.moe_route_workspace_bytes(ctypes.byref(b), 10) == M.SIZE_MAX
+    assert L.moe_layer_workspace_bytes(None, 10) == M.SIZE_MAX
+    assert L.moe_layer_workspace_bytes(ctypes.byref(c), -1) == M.SIZE_MAX
+    assert L.moe_layer_workspace_bytes(ctypes.byref(c), 1 << 30) == M.SIZE_MAX
+    assert L.moe_grouped_ffn_workspace_bytes(ctypes.byref(c), 0, 10, 128) == M.SIZE_MAX
+    assert L.moe_grouped_ffn_workspace_bytes(ctypes.byref(c), 4, 10, 0) == M.SIZE_MAX
+
+
+def _last():
+    return moe.lib().moe_last_error().decode()
+
+
+def test_route_checks():
+    L = moe.lib()
+    c = cfg()
+    ws = L.moe_route_workspace_bytes(ctypes.byref(c), 8)
+    call = lambda c_, T, x=FAKE, w=FAKE, b=None, i=FAKE, p=FAKE, g=None, wsp=FAKE, wsb=ws: \
+        L.moe_route(c_, T, x, w, b, i, p, g, wsp, wsb, None)
+    assert call(None, 8) == NULL and "cfg" in _last()
+    assert call(ctypes.byref(cfg(top_k=20)), 8) == SHAPE
+    assert call(ctypes.byref(cfg(dtype=3)), 8) == UNSUP
+    assert call(ctypes.byref(cfg(n_experts=1025)), 8) == UNSUP
+    assert call(ctypes.byref(c), -1) == SHAPE
+    assert call(ctypes.byref(c), 0) == OK          # nothing to do, nothing enqueued
+    assert call(ctypes.byref(c), 8, x=None) == NULL
+    assert call(ctypes.byref(c), 8, i=None) == NULL
+    assert call(ctypes.byref(c), 8, wsp=None) == NULL
+    assert call(ctypes.byref(c), 8, x=FAKE + 8) == MISALIGNED
+    assert call(ctypes.byref(c), 8, g=FAKE + 4) == MISALIGNED
+    assert call(ctypes.byref(c), 8, wsb=ws - 1) == WS and str(ws) in _last()
+    assert call(ctypes.byref(cfg(d_model=252)), 8) == UNSUP   # bf16 rows of 504 bytes
+
+
+def test_permute_checks():
+    L = moe.lib()
+    c = cfg()
+    ws = L.moe_permute_workspace_bytes(ctypes.byref(c), 8)
+    call = lambda T, idx=FAKE, off=FAKE, st=FAKE, de=FAKE, x=None, xp=None, wsp=FAKE, wsb=ws: \
+        L.moe_permute(ctypes.byref(c), T, idx, off, st, de, x, xp, wsp, wsb, None)
+    assert call(0) == OK
+    assert call(8, idx=None) == NULL
+    assert call(8, x=FAKE) == NULL               # x without x_perm
+    assert call(8, de=FAKE + 2) == MISALIGNED
+    assert call(8, wsb=0) == WS
+    assert call(-3) == SHAPE
+
+
+def test_grouped_ffn_checks():
+    L = moe.lib()
+    c = cfg()
+    ws = L.moe_grouped_ffn_workspace_bytes(ctypes.byref(c), 4, 64, 128)
+    call = lambda G=4, rows=64, off=FAKE, x=FAKE, gat=None, d_ff=128, y=FAKE, wsb=ws: \
+        L.moe_grouped_ffn(ctypes.byref(c), G, rows, off, x, 64, gat, FAKE, FAKE, FAKE, d_ff, y, FAKE, wsb, None)
+    assert call(rows=0) == OK
+    assert call(G=0) == SHAPE
+    assert call(G=2000) == SHAPE
+    assert call(d_ff=0) == SHAPE
+    assert call(off=None) == NULL
+    assert call(y=None) == NULL
+    assert call(gat=FAKE + 4) == MISALIGNED
+    assert call(d_ff=100) == UNSUP or call(d_ff=100) == WS   # bf16 rows need d_ff % 8 == 0
+    assert call(d_ff=132) == UNSUP
+    assert call(wsb=ws - 16) == WS
+
+
+def test_expert_half_checks():
+    L = moe.lib()
+    c = cfg()
+    ws = L.moe_expert_workspace_bytes(ctypes.byref(c), 5, 64, 128)
+    assert ws != M.SIZE_MAX and L.moe_expert_workspace_bytes(ctypes.byref(c), 0, 64, 128) == M.SIZE_MAX
+    gu = lambda n_gather=0, gat=None, sg=None, su=None, wsb=ws, rows=64: L.moe_expert_gate_up(
+        ctypes.byref(c), 4, rows, FAKE, FAKE, 64, gat, n_gather, FAKE, FAKE, sg, su, 128, FAKE, FAKE, wsb, None)
+    assert gu(rows=0) == OK
+    assert gu(n_gather=8) == NULL                 # gather required when n_gather > 0
+    assert gu(n_gather=65, gat=FAKE) == SHAPE     # n_gather > n_rows
+    assert gu(sg=FAKE) == NULL                    # s_gate without s_up
+    assert gu(sg=FAKE, su=FAKE + 4) == MISALIGNED
+    assert gu(sg=FAKE, su=FAKE, wsb=L.moe_expert_workspace_bytes(ctypes.byref(c), 5, 64, 128) - 1) == WS
+    dn = lambda sd=None, y=FAKE, wsb=ws: L.moe_expert_down(ctypes.byref(c), 4, 64, FAKE, FAKE, FAKE, sd, 128, y,
+                                                           FAKE, wsb, None)
+    assert dn(y=None) == NULL
+    assert dn(sd=FAKE + 2) == MISALIGNED
+    assert dn(wsb=16) == WS
+
+
+def test_combine_and_layer_checks():
+    L = moe.lib()
+    c = cfg()
+    assert L.moe_combine(ctypes.byref(c), 0, FAKE, FAKE, FAKE, None, FAKE, None) == OK
+    assert L.moe_combine(ctypes.byref(c), 4, None, FAKE, FAKE, None, FAKE, None) == NULL
+    assert L.moe_combine(ctypes.byref(c), 4, FAKE, FAKE, FAKE, FAKE + 12, FAKE, None) == MISALIGNED
+    ws = L.moe_layer_workspace_bytes(ctypes.byref(c), 8)
+    w = M.MoeWeights(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    call = lambda T=8, cc=c, ww=w, wsb=ws: L.moe_layer_forward(ctypes.byref(cc), T, FAKE, ctypes.byref(ww), FAKE,
+                                                               None, None, None, FAKE, wsb, None)
+    assert call(T=0) == OK
+    assert call(wsb=ws - 1) == WS
+    assert L.moe_layer_forward(ctypes.byref(c), 8, FAKE, None, FAKE, None, None, None, FAKE, ws, None) == NULL
+    no_shared = M.MoeWeights(FAKE, None, FAKE, FAKE, FAKE, None, None, None)
+    assert call(ww=no_shared) == NULL and "d_shared" in _last()
+    no_router = M.MoeWeights(None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert call(ww=no_router) == NULL
+    bad_bias = M.MoeWeights(FAKE, FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert call(ww=bad_bias) == MISALIGNED
+    c0 = cfg(d_shared=0)
+    ws0 = L.moe_layer_workspace_bytes(ctypes.byref(c0), 8)
+    assert call(cc=c0, ww=no_shared, wsb=ws0 - 1) == WS   # no shared expert: its weights may be NULL
+
+
+def test_binding_rejects_host_tensors():
+    c = moe.Config(256, 16, 4, 128, 128, torch.bfloat16)
+    x = torch.zeros(8, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device"):
+        moe.route(c, x, torch.zeros(16, 256, dtype=torch.bfloat16))
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(M, "_lib", None)
+    monkeypatch.setattr(M, "LIB_PATH", os.path.join(ROOT, "does_not_exist", "libmoe.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        M.lib()

@@ -1,0 +1,83 @@
+// Weighted combine (page "Step3.5 Flash 大模型技术深度解析", section 3.2.2,
+// step 3): the outputs of a token's K routed experts, weighted by their
+// router probabilities, are added to the shared expert's output:
+//   out[t] = y_shared[t] + sum_{k=0..K-1} prob[t,k] * y_perm[dest[t*K+k]]
+// in fp32, in that order, with one final rounding to the output type.
+// One block per token; the K source rows are read with 16-byte loads.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+template <typename TO>
+__device__ __forceinline__ void store4(TO* p, float4 v) {
+  store_out(p, v.x);
+  store_out(p + 1, v.y);
+  store_out(p + 2, v.z);
+  store_out(p + 3, v.w);
+}
+
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float4 v) {
+  *(float4*)p = v;
+}
+
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 v) {
+  const uint32_t lo = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+  *(uint2*)p = make_uint2(lo, hi);
+}
+
+template <typename TO>
+__global__ void __launch_bounds__(256) combine_kernel(int D, int K, const float* __restrict__ y_perm, int64_t n_perm,
+                                                      const int32_t* __restrict__ dest, const float* __restrict__ prob,
+                                                      const float* __restrict__ y_shared, TO* __restrict__ out) {
+  __shared__ int64_t s_row[64];
+  __shared__ float s_p[64];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < K) {
+    const int64_t d = dest[t * K + tid];
+    s_row[tid] = (d >= 0 && d < n_perm) ? d : -1;
+    s_p[tid] = prob[t * K + tid];
+  }
+  __syncthreads();
+  if ((D & 3) == 0) {
+    for (int c = tid * 4; c < D; c += 1024) {
+      float4 acc = y_shared ? *(const float4*)(y_shared + t * D + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < K; ++k) {
+        if (s_row[k] < 0) continue;
+        const float4 v = *(const float4*)(y_perm + s_row[k] * D + c);
+        const float w = s_p[k];
+        acc.x = fmaf(w, v.x, acc.x);
+        acc.y = fmaf(w, v.y, acc.y);
+        acc.z = fmaf(w, v.z, acc.z);
+        acc.w = fmaf(w, v.w, acc.w);
+      }
+      store4(out + t * D + c, acc);
+    }
+  } else {
+    for (int c = tid; c < D; c += 256) {
+      float acc = y_shared ? y_shared[t * D + c] : 0.f;
+      for (int k = 0; k < K; ++k)
+        if (s_row[k] >= 0) acc = fmaf(s_p[k], y_perm[s_row[k] * D + c], acc);
+      store_out(out + t * D + c, acc);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(int out_dtype, int64_t T, int D, int K, const float* y_perm, int64_t n_perm_rows,
+                          const int32_t* dest, const float* prob, const float* y_shared, void* out, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (out_dtype == MOE_BF16)
+    combine_kernel<bf16_t><<<(unsigned)T, 256, 0, s>>>(D, K, y_perm, n_perm_rows, dest, prob, y_shared, (bf16_t*)out);
+  else
+    combine_kernel<float><<<(unsigned)T, 256, 0, s>>>(D, K, y_perm, n_perm_rows, dest, prob, y_shared, (float*)out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

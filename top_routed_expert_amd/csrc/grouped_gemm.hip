@@ -1,0 +1,359 @@
+// Grouped GEMMs of the MoE layer: the experts' gate/up projections with the
+// SwiGLU epilogue, their down projections, and the router's linear layer
+// (one group). Every expert is an independent FFN (page "Step3.5 Flash
+// 大模型技术深度解析", section 3.2.1), so the permuted rows routed to expert e
+// form one dense block multiplied by that expert's weights alone.
+//
+// Fast path (bf16, contraction length a multiple of 64): bf16 MFMA
+// 16x16x32 with fp32 accumulation. A block owns up to BM = 16*MT rows of one
+// expert and 4*NW*16 output columns (for gate/up: that many gate columns
+// and the same up columns, so the SwiGLU is applied in registers). The A
+// rows are gathered through the permutation on the fly (the permuted
+// activations are never written to HBM) and staged in LDS, 64 contraction
+// elements per stage, double buffered, XOR-swizzled so MFMA operand reads
+// are bank-conflict free. The weights are streamed straight from HBM into
+// VGPRs in MFMA operand layout, one stage ahead, and read once per row tile.
+//
+// Generic path (fp32, or shapes the fast path does not cover): 64x64 output
+// tiles staged through LDS, plain fp32 FMA.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+
+__device__ __forceinline__ bool fetch_tile(const GemmArgs& p, int ti, int BM, Tile& t) {
+  if (p.tiles == nullptr) {
+    const int64_t r0 = (int64_t)ti * BM;
+    if (r0 >= p.dense_rows) return false;
+    t.group = 0;
+    t.row0 = (int32_t)r0;
+    t.row1 = (int32_t)(r0 + BM < p.dense_rows ? r0 + BM : p.dense_rows);
+    return true;
+  }
+  if (ti >= *p.n_tiles) return false;
+  t = p.tiles[ti];
+  return true;
+}
+
+// Source row of problem row r (gathered through the permutation, or direct);
+// -1 when it falls outside the A operand.
+__device__ __forceinline__ int64_t source_row(const GemmArgs& p, int64_t r) {
+  const int64_t src = r < p.n_gather ? (int64_t)p.gather[r] : r - p.n_gather;
+  return (src >= 0 && src < p.n_a_rows) ? src : -1;
+}
+
+template <typename T>
+__device__ __forceinline__ const T* group_b(const GemmArgs& p, const void* main, const void* extra,
+                                            int g) {
+  return g < p.n_main ? (const T*)main + (int64_t)g * p.b_stride : (const T*)extra;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// LDS offset (in bf16 elements) of 16-byte chunk `c` of staged row `r` (row
+// length KS): chunks are XOR-swizzled by (r & 7) so the 16-byte operand reads
+// of 8 consecutive rows hit distinct banks.
+template <int KS>
+__device__ __forceinline__ int lds_off(int r, int c) { return r * KS + ((c ^ (r & 7)) << 3); }
+
+// EPI: epilogue; MT: 16-row MFMA tiles per block; NW: 16-column weight tiles
+// per wave and operand; KSTEPS: 32-element MFMA steps per pipeline stage.
+template <int EPI, int MT, int NW, int KSTEPS>
+__global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
+  constexpr int KS = 32 * KSTEPS;                       // contraction elements per stage
+  constexpr int CPR = KS / 8;                           // 16-byte chunks per staged row
+  constexpr int RPP = 256 / CPR;                        // rows staged per pass of the block
+  constexpr int BM = 16 * MT;
+  constexpr int NA = BM / RPP;                          // chunks staged per thread
+  constexpr int NBT = EPI == EPI_SWIGLU ? 2 * NW : NW;  // weight tiles (16 columns) per wave
+  constexpr int BN = 4 * NW * 16;                       // output columns per block
+  static_assert(BM % RPP == 0, "row tile must be a whole number of staging passes");
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * KS];
+
+  // Hardware places block b on XCD b % 8. Give each XCD a contiguous run of
+  // logical blocks, column blocks fastest: the column blocks of a row tile
+  // (same A rows) and the row tiles of one expert (same weights) then run
+  // together on one XCD and share its L2.
+  const int n_nb = (p.N + BN - 1) / BN;
+  const int per_xcd = gridDim.x >> 3;
+  const int L = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int ti = L / n_nb, nb = L - ti * n_nb;
+  Tile t;
+  if (!fetch_tile(p, ti, BM, t)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Kdim = p.Kdim, nk = Kdim / KS;
+  const bf16_t* A = (const bf16_t*)p.a;
+
+  // A staging: this thread copies 16-byte chunk (tid % CPR) of local rows
+  // tid / CPR + RPP*i. Rows outside the tile are zero.
+  const bf16_t* arow[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int64_t r = (int64_t)t.row0 + tid / CPR + RPP * i;
+    const int64_t src = r < t.row1 ? source_row(p, r) : -1;
+    arow[i] = src >= 0 ? A + src * Kdim + (tid % CPR) * 8 : nullptr;
+  }
+
+  // Weight rows of this wave: tile j covers output columns wcol0 + (j % NW)*16 + 0..15.
+  // Lane (c = lane & 15, q = lane >> 4) reads column c, contraction offset q*8 of each
+  // 32-element MFMA step. Columns past N are clamped to a valid row; their
+  // results are never stored.
+  const int wcol0 = nb * BN + wave * NW * 16;
+  const bf16_t* bg = group_b<bf16_t>(p, p.b0, p.b0_extra, t.group);
+  const bf16_t* bu = EPI == EPI_SWIGLU ? group_b<bf16_t>(p, p.b1, p.b1_extra, t.group) : bg;
+  const bf16_t* bptr[NBT];
+#pragma unroll
+  for (int j = 0; j < NBT; ++j) {
+    int col = wcol0 + (j % NW) * 16 + (lane & 15);
+    col = col < p.N ? col : p.N - 1;
+    bptr[j] = (j < NW ? bg : bu) + (int64_t)col * Kdim + (lane >> 4) * 8;
+  }
+
+  uint4 ra[NA];
+  uint4 rb0[NBT][KSTEPS], rb1[NBT][KSTEPS];
+  f32x4 acc[MT][NBT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < NBT; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_a = [&](int ks) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      ra[i] = arow[i] ? *(const uint4*)(arow[i] + ks * KS) : make_uint4(0u, 0u, 0u, 0u);
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) *(uint4*)&sA[buf][lds_off<KS>(tid / CPR + RPP * i, tid % CPR)] = ra[i];
+  };
+  auto load_b = [&](uint4(&rb)[NBT][KSTEPS], int ks) {
+#pragma unroll
+    for (int j = 0; j < NBT; ++j)
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) rb[j][s] = *(const uint4*)(bptr[j] + ks * KS + s * 32);
+  };
+  auto compute = [&](int buf, uint4(&rb)[NBT][KSTEPS]) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const bf16x8 a =
+            as_bf16x8(*(const uint4*)&sA[buf][lds_off<KS>(m * 16 + (lane & 15), s * 4 + (lane >> 4))]);
+#pragma unroll
+        for (int j = 0; j < NBT; ++j)
+          acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(rb[j][s]), acc[m][j], 0, 0, 0);
+      }
+    }
+  };
+
+  load_a(0);
+  load_b(rb0, 0);
+  store_a(0);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ks += 2) {
+    if (ks + 1 < nk) {
+      load_a(ks + 1);
+      load_b(rb1, ks + 1);
+    }
+    compute(0, rb0);
+    if (ks + 1 < nk) store_a(1);
+    __syncthreads();
+    if (ks + 1 >= nk) break;
+    if (ks + 2 < nk) {
+      load_a(ks + 2);
+      load_b(rb0, ks + 2);
+    }
+    compute(1, rb1);
+    if (ks + 2 < nk) store_a(0);
+    __syncthreads();
+  }
+
+  // Accumulator layout of a 16x16 MFMA tile: lane holds column (lane & 15),
+  // rows 4*(lane >> 4) + v for v = 0..3.
+  const int64_t rbase = (int64_t)t.row0 + (lane >> 4) * 4;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const int col = wcol0 + j * 16 + (lane & 15);
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t r = rbase + m * 16 + v;
+        if (r >= t.row1) continue;
+        if constexpr (EPI == EPI_SWIGLU) {
+          ((bf16_t*)p.out)[r * p.ldo + col] = f32_to_bf16(silu(acc[m][j][v]) * acc[m][j + NW][v]);
+        } else {
+          ((float*)p.out)[r * p.ldo + col] = acc[m][j][v] + (p.bias ? p.bias[col] : 0.f);
+        }
+      }
+    }
+  }
+}
+
+// Generic grouped GEMM: 64x64 output tile, 16x16 threads with 4x4 outputs
+// each, contraction in chunks of 16 through LDS. TI is float or bf16_t.
+template <typename TI, int EPI>
+__global__ void __launch_bounds__(256) gemm_generic(GemmArgs p) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
+  __shared__ float sA[BK][BM + 1];
+  __shared__ float sB[NB][BK][BN + 1];
+
+  const int n_nb = (p.N + BN - 1) / BN;
+  const int ti = blockIdx.x / n_nb, nb = blockIdx.x - ti * n_nb;
+  Tile t;
+  if (!fetch_tile(p, ti, BM, t)) return;
+
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const TI* A = (const TI*)p.a;
+  const TI* B[NB];
+  B[0] = group_b<TI>(p, p.b0, p.b0_extra, t.group);
+  if constexpr (NB == 2) B[1] = group_b<TI>(p, p.b1, p.b1_extra, t.group);
+
+  // Staging: element e = tid + 256*i is (row or column e / 16, contraction e % 16).
+  int64_t asrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = (int64_t)t.row0 + ((tid + 256 * i) >> 4);
+    asrc[i] = r < t.row1 ? source_row(p, r) : -1;
+  }
+  float acc[NB][4][4] = {};
+  for (int k0 = 0; k0 < p.Kdim; k0 += BK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i, rc = e >> 4, kk = e & 15, k = k0 + kk;
+      sA[kk][rc] = (asrc[i] >= 0 && k < p.Kdim) ? load_f32(A + asrc[i] * p.Kdim + k) : 0.f;
+      const int col = nb * BN + rc;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        sB[b][kk][rc] = (col < p.N && k < p.Kdim) ? load_f32(B[b] + (int64_t)col * p.Kdim + k) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float a[4], bv[NB][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sA[kk][ty * 4 + i];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[b][j] = sB[b][kk][tx * 4 + j];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[b][i][j] = fmaf(a[i], bv[b][j], acc[b][i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = (int64_t)t.row0 + ty * 4 + i;
+    if (r >= t.row1) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = nb * BN + tx * 4 + j;
+      if (col >= p.N) continue;
+      if constexpr (EPI == EPI_SWIGLU) {
+        store_out((TI*)p.out + r * p.ldo + col, silu(acc[0][i][j]) * acc[NB - 1][i][j]);
+      } else {
+        ((float*)p.out)[r * p.ldo + col] = acc[0][i][j] + (p.bias ? p.bias[col] : 0.f);
+      }
+    }
+  }
+}
+
+// Device-side schedule: cut every group's row segment into tiles of BM rows,
+// in group order. Segment bounds are clamped to [0, n_rows] and made
+// non-decreasing, so malformed offsets cannot address rows out of range.
+__global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __restrict__ offsets, int n_groups,
+                                                           int64_t n_rows, int BM, Tile* __restrict__ tiles,
+                                                           int32_t* __restrict__ n_tiles, int32_t max_tiles) {
+  __shared__ int32_t s_scan[1024];
+  const int tid = threadIdx.x;
+  const int per = (n_groups + 1023) / 1024;
+  const int g0 = tid * per, g1 = min(g0 + per, n_groups);
+  auto seg = [&](int g, int64_t& a, int64_t& b) {
+    a = offsets[g];
+    b = offsets[g + 1];
+    a = a < 0 ? 0 : (a > n_rows ? n_rows : a);
+    b = b < a ? a : (b > n_rows ? n_rows : b);
+  };
+  int mine = 0;
+  for (int g = g0; g < g1; ++g) {
+    int64_t a, b;
+    seg(g, a, b);
+    mine += (int)((b - a + BM - 1) / BM);
+  }
+  s_scan[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += v;
+    __syncthreads();
+  }
+  int slot = s_scan[tid] - mine;
+  for (int g = g0; g < g1; ++g) {
+    int64_t a, b;
+    seg(g, a, b);
+    for (int64_t r = a; r < b; r += BM, ++slot)
+      if (slot < max_tiles) tiles[slot] = Tile{g, (int32_t)r, (int32_t)(r + BM < b ? r + BM : b), 0};
+  }
+  if (tid == 1023) *n_tiles = min(s_scan[1023], max_tiles);
+}
+
+}  // namespace
+
+int gemm_block_rows(bool fast, int64_t rows, int n_groups) {
+  if (!fast) return 64;
+  return rows <= 32 * (int64_t)n_groups ? 32 : 128;
+}
+
+int64_t gemm_max_tiles(int64_t n_rows, int n_groups, int block_rows) {
+  return n_rows / block_rows + n_groups;  // sum over groups of ceil(len / BM)
+}
+
+hipError_t launch_build_tiles(const int32_t* offsets, int n_groups, int64_t n_rows, int block_rows, Tile* tiles,
+                              int32_t* n_tiles, int32_t max_tiles, hipStream_t s) {
+  build_tiles_kernel<<<1, 1024, 0, s>>>(offsets, n_groups, n_rows, block_rows, tiles, n_tiles, max_tiles);
+  return hipGetLastError();
+}
+
+template <int EPI, int MT, int NW, int KSTEPS = 2>
+static hipError_t launch_fast(const GemmArgs& g, hipStream_t s) {
+  const int n_nb = (g.N + 4 * NW * 16 - 1) / (4 * NW * 16);
+  const int64_t blocks = ((int64_t)g.max_tiles * n_nb + 7) / 8 * 8;
+  gemm_bf16_mfma<EPI, MT, NW, KSTEPS><<<(unsigned)blocks, 256, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm(int dtype, int epi, int block_rows, const GemmArgs& g, hipStream_t s) {
+  if (g.max_tiles <= 0 || g.N <= 0) return hipSuccess;
+  if (block_rows == 64) {
+    const int n_nb = (g.N + 63) / 64;
+    const unsigned blocks = (unsigned)((int64_t)g.max_tiles * n_nb);
+    if (dtype == MOE_BF16) {
+      if (epi == EPI_SWIGLU) gemm_generic<bf16_t, EPI_SWIGLU><<<blocks, 256, 0, s>>>(g);
+      else gemm_generic<bf16_t, EPI_F32><<<blocks, 256, 0, s>>>(g);
+    } else {
+      if (epi == EPI_SWIGLU) gemm_generic<float, EPI_SWIGLU><<<blocks, 256, 0, s>>>(g);
+      else gemm_generic<float, EPI_F32><<<blocks, 256, 0, s>>>(g);
+    }
+    return hipGetLastError();
+  }
+  const bool narrow = g.N <= 512;  // router-sized outputs: 64 columns per block
+  if (block_rows == 32) {
+    if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 2, 2>(g, s);
+    return narrow ? launch_fast<EPI_F32, 2, 1>(g, s) : launch_fast<EPI_F32, 2, 4>(g, s);
+  }
+  if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 8, 2>(g, s);
+  return narrow ? launch_fast<EPI_F32, 8, 1>(g, s) : launch_fast<EPI_F32, 8, 4>(g, s);
+}
+
+}  // namespace moe

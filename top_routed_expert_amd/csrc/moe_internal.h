@@ -1,0 +1,93 @@
+// Internal declarations shared by the HIP translation units of libmoe.
+// Nothing here is part of the C ABI (include/moe.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // storage type of bfloat16 values
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// float -> bfloat16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float load_f32(const float* p) { return *p; }
+__device__ __forceinline__ float load_f32(const bf16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_out(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// One row segment of a grouped GEMM: rows [row0, row1) of group `group`.
+struct Tile {
+  int32_t group, row0, row1, pad;
+};
+
+// Epilogues of the grouped GEMM.
+enum GemmEpilogue {
+  EPI_SWIGLU = 0,  // two B operands (gate, up): out = dtype(silu(A Bg^T) * (A Bu^T))
+  EPI_F32 = 1      // one B operand: out = fp32(A B^T + bias)
+};
+
+// Arguments of one grouped GEMM launch: out[r, n] for rows r of each tile and
+// columns n < N, contracting over Kdim.
+struct GemmArgs {
+  const void* a;          // A rows: [n_a_rows, Kdim] (row r of the problem reads row map(r))
+  int64_t n_a_rows;
+  const int32_t* gather;  // map(r) = gather[r] for r < n_gather, else r - n_gather
+  int64_t n_gather;
+  const void* b0;         // B of group g < n_main: b0 + g*b_stride; group n_main: b0_extra
+  const void* b1;         // second B operand (EPI_SWIGLU only), same indexing
+  const void* b0_extra;
+  const void* b1_extra;
+  int64_t b_stride;       // elements between consecutive groups' B matrices ([N, Kdim])
+  int32_t n_main;
+  int32_t N;
+  int32_t Kdim;
+  const Tile* tiles;      // schedule built on the device, or NULL: one group (group 0)
+  const int32_t* n_tiles; //   of dense_rows rows cut into consecutive row tiles
+  int64_t dense_rows;
+  int32_t max_tiles;      // host-side upper bound of the tile count (grid size)
+  void* out;              // [rows, ldo]
+  int64_t ldo;
+  const float* bias;      // EPI_F32: per-column bias or NULL
+};
+
+// Launchers (grouped_gemm.hip). `dtype` is MOE_BF16 or MOE_F32 for A/B; the
+// SwiGLU output has the same dtype; EPI_F32 output is fp32.
+// Row-tile height: 32 or 128 on the bf16 MFMA path (`fast`), 64 otherwise.
+int gemm_block_rows(bool fast, int64_t rows, int n_groups);
+int64_t gemm_max_tiles(int64_t n_rows, int n_groups, int block_rows);
+hipError_t launch_build_tiles(const int32_t* offsets, int n_groups, int64_t n_rows, int block_rows,
+                              Tile* tiles, int32_t* n_tiles, int32_t max_tiles, hipStream_t s);
+hipError_t launch_grouped_gemm(int dtype, int epi, int block_rows, const GemmArgs& g, hipStream_t s);
+
+// route.hip
+hipError_t launch_topk(const float* logits, int64_t T, int E, int K, int32_t* idx, float* prob,
+                       float* gap, hipStream_t s);
+
+// permute.hip
+hipError_t launch_permute(const int32_t* idx, int64_t T, int K, int E, int32_t* rank, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_token, int32_t* dest,
+                          int32_t* offsets_ext, int32_t extra_rows, hipStream_t s);
+hipError_t launch_gather_rows(const void* x, int64_t T, int D, int elem_bytes, const int32_t* sorted_token,
+                              int64_t rows, void* x_perm, hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(int out_dtype, int64_t T, int D, int K, const float* y_perm, int64_t n_perm_rows,
+                          const int32_t* dest, const float* prob, const float* y_shared, void* out,
+                          hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,173 @@
+// Permutation of the (token, choice) pairs into per-expert row segments, so
+// each expert's FFN (page "Step3.5 Flash 大模型技术深度解析", section 3.2.1:
+// independent FFN per expert) runs on one contiguous block of rows.
+//
+// Pairs are numbered token-major (j = t*K + k). Row of pair j:
+//   dest[j] = offsets[e] + #{ j' < j : idx[j'] == e },   e = idx[j]
+// which is stable and unique, so the result is independent of scheduling.
+//
+//  1. rank: one block per expert walks all pairs in order, a block-wide
+//     prefix sum of match flags per 4096-pair chunk giving each matching
+//     pair its rank; the total is the expert's count. No atomics.
+//  2. place: every block rebuilds the exclusive scan of the E counts in LDS,
+//     then maps each pair to dest and writes sorted_token[dest] = t.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int PR_PER = 16;            // pairs per thread per chunk
+constexpr int PR_CHUNK = 256 * PR_PER;
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int w = __shfl_up(v, o, 64);
+    if (lane >= o) v += w;
+  }
+  return v;
+}
+
+__global__ void __launch_bounds__(256) permute_rank_kernel(const int32_t* __restrict__ idx, int64_t P, int E,
+                                                           int32_t* __restrict__ rank, int32_t* __restrict__ counts) {
+  __shared__ int s_wave[4];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int running = 0;
+  for (int64_t base = 0; base < P; base += PR_CHUNK) {
+    const int64_t j0 = base + (int64_t)tid * PR_PER;
+    int v[PR_PER];
+    if (j0 + PR_PER <= P) {
+#pragma unroll
+      for (int i = 0; i < PR_PER; i += 4) {
+        const int4 q = *(const int4*)(idx + j0 + i);
+        v[i] = q.x;
+        v[i + 1] = q.y;
+        v[i + 2] = q.z;
+        v[i + 3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PR_PER; ++i) v[i] = j0 + i < P ? idx[j0 + i] : -1;
+    }
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < PR_PER; ++i) c += v[i] == e;
+    const int incl = wave_incl_scan(c, lane);
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      before += w < wave ? s_wave[w] : 0;
+      total += s_wave[w];
+    }
+    int r = running + before + incl - c;
+#pragma unroll
+    for (int i = 0; i < PR_PER; ++i)
+      if (v[i] == e) rank[j0 + i] = r++;
+    running += total;
+    __syncthreads();
+  }
+  if (tid == 0) counts[e] = running;
+}
+
+__global__ void __launch_bounds__(256) permute_place_kernel(const int32_t* __restrict__ idx, int64_t P, int K, int E,
+                                                            const int32_t* __restrict__ rank,
+                                                            const int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ sorted_token,
+                                                            int32_t* __restrict__ dest,
+                                                            int32_t* __restrict__ offsets_ext, int32_t extra_rows) {
+  __shared__ int s_off[1025];
+  __shared__ int s_wave[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // exclusive scan of counts: thread owns experts 4*tid .. 4*tid+3
+  int c[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * tid + i;
+    c[i] = e < E ? counts[e] : 0;
+    sum += c[i];
+  }
+  const int incl = wave_incl_scan(sum, lane);
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  int run = incl - sum;
+  for (int w = 0; w < wave; ++w) run += s_wave[w];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * tid + i;
+    if (e < E) s_off[e] = run;
+    run += c[i];
+  }
+  if (tid == 255) s_off[E] = run;  // the last thread ends on the total
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int e = tid; e <= E; e += 256) {
+      if (offsets) offsets[e] = s_off[e];
+      if (offsets_ext) offsets_ext[e] = s_off[e];
+    }
+    if (offsets_ext && tid == 0) offsets_ext[E + 1] = s_off[E] + extra_rows;
+  }
+  for (int64_t j = (int64_t)blockIdx.x * 256 + tid; j < P; j += (int64_t)gridDim.x * 256) {
+    const int e = idx[j];
+    if (e >= 0 && e < E) {
+      const int d = s_off[e] + rank[j];
+      dest[j] = d;
+      sorted_token[d] = (int32_t)(j / K);
+    } else {
+      dest[j] = -1;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) gather_rows_kernel(const uint4* __restrict__ x, int row_vecs,
+                                                          const int32_t* __restrict__ sorted_token, int64_t T,
+                                                          uint4* __restrict__ x_perm) {
+  const int64_t r = blockIdx.x;
+  int64_t t = sorted_token[r];
+  t = t < 0 ? 0 : (t >= T ? T - 1 : t);
+  for (int i = threadIdx.x; i < row_vecs; i += 256) x_perm[r * row_vecs + i] = x[t * row_vecs + i];
+}
+
+__global__ void __launch_bounds__(256) gather_rows_bytes_kernel(const uint8_t* __restrict__ x, int row_bytes,
+                                                                const int32_t* __restrict__ sorted_token, int64_t T,
+                                                                uint8_t* __restrict__ x_perm) {
+  const int64_t r = blockIdx.x;
+  int64_t t = sorted_token[r];
+  t = t < 0 ? 0 : (t >= T ? T - 1 : t);
+  for (int i = threadIdx.x; i < row_bytes; i += 256) x_perm[r * row_bytes + i] = x[t * row_bytes + i];
+}
+
+}  // namespace
+
+hipError_t launch_permute(const int32_t* idx, int64_t T, int K, int E, int32_t* rank, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_token, int32_t* dest, int32_t* offsets_ext,
+                          int32_t extra_rows, hipStream_t s) {
+  const int64_t P = T * K;
+  permute_rank_kernel<<<E, 256, 0, s>>>(idx, P, E, rank, counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  int64_t blocks = (P + 255) / 256;
+  blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
+  permute_place_kernel<<<(unsigned)blocks, 256, 0, s>>>(idx, P, K, E, rank, counts, offsets, sorted_token, dest,
+                                                        offsets_ext, extra_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, int64_t T, int D, int elem_bytes, const int32_t* sorted_token,
+                              int64_t rows, void* x_perm, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int row_bytes = D * elem_bytes;
+  if (row_bytes % 16 == 0)
+    gather_rows_kernel<<<(unsigned)rows, 256, 0, s>>>((const uint4*)x, row_bytes / 16, sorted_token, T,
+                                                      (uint4*)x_perm);
+  else
+    gather_rows_bytes_kernel<<<(unsigned)rows, 256, 0, s>>>((const uint8_t*)x, row_bytes, sorted_token, T,
+                                                            (uint8_t*)x_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe
