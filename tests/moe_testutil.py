@@ -4,10 +4,20 @@ view of the same weights, and the comparison rules.
 Comparison rules (the layer's tolerances):
   - routing: expert ids equal as ordered lists, except tokens whose oracle
     gap between the K-th and (K+1)-th float32 probability is below 1e-6
-    (near-ties, counted and reported); selected probabilities within 1e-6;
+    (near-ties, counted and reported). Selected probabilities: a logit error
+    d shifts p by at most a factor exp(+-2d); the logits are length-D dot
+    products of exact bf16 products summed in fp32, whose error is bounded
+    (probabilistically, Higham and Mary 2019) by sqrt(D) * u * sum_d |x_d w_d|
+    with u = 2^-24. So |p_gpu - p| <= 2 p sqrt(D) u S_te + 8 u p, with S_te
+    the sum of absolute products of token t and expert e;
   - permutation (offsets, sorted_token, dest): bit-exact given the same ids;
-  - output: max |gpu - oracle| <= 2e-2 * RMS(oracle) over compared rows
-    (bf16 inputs and output, fp32 accumulation); fp32 layers 1e-4 * RMS.
+  - output of a bf16 layer (bf16 inputs, fp32 accumulation): the layer run
+    with an fp32 output, i.e. the arithmetic before the final cast, satisfies
+    max |gpu - oracle| <= 2e-2 * RMS(oracle); the bf16 output is within
+    2e-2 * RMS + half a bf16 ulp of the oracle value, element by element.
+    The half ulp is the final cast's own error: rounding the exact result to
+    bf16 can by itself exceed 2e-2 * RMS once |out| >= 4 with RMS < 0.78;
+  - output of an fp32 layer: max |gpu - oracle| <= 1e-4 * RMS(oracle).
 """
 from __future__ import annotations
 
@@ -20,7 +30,6 @@ import synth
 from oracle import moe_oracle as O
 
 NEAR_TIE = 1e-6
-PROB_TOL = 1e-6
 
 
 def out_tol(spec) -> float:
@@ -69,17 +78,36 @@ def oracle_weights(L: dict) -> O.LayerWeights:
     return O.LayerWeights(host(L["w_router"]), expert, shared, host(L.get("bias")))
 
 
-def compare_routing(idx_gpu, prob_gpu, ref) -> dict:
-    """Ordered-id equality and probability closeness outside near-ties."""
+U32 = 2.0 ** -24
+
+
+def prob_bound(x, w_router, idx, prob) -> np.ndarray:
+    """Per selected (t, k): 2 p sqrt(D) u S + 8 u p, S = sum_d |x_td W_r[e,d]| (see the module notes)."""
+    xa = np.abs(O.as_f64(x))
+    wa = np.abs(O.as_f64(w_router))
+    S = np.take_along_axis(xa @ wa.T, np.asarray(idx, dtype=np.int64), axis=1)
+    p = np.asarray(prob, dtype=np.float64)
+    return 2.0 * p * math.sqrt(xa.shape[1]) * U32 * S + 8.0 * U32 * p
+
+
+def compare_routing(idx_gpu, prob_gpu, ref, x, w_router) -> dict:
+    """Ordered-id equality outside near-ties; probabilities within the fp32 accumulation bound."""
     idx_gpu = np.asarray(idx_gpu)
     prob_gpu = np.asarray(prob_gpu, dtype=np.float64)
     keep = ref["gap"] >= NEAR_TIE
     bad = np.nonzero(keep & np.any(idx_gpu != ref["idx"], axis=1))[0]
     assert bad.size == 0, f"{bad.size} tokens routed differently, first {bad[:5]}: " \
                           f"gpu {idx_gpu[bad[0]]} oracle {ref['idx'][bad[0]]}"
-    dp = np.abs(prob_gpu - ref["prob"].astype(np.float64))[keep]
-    assert dp.size == 0 or dp.max() <= PROB_TOL, f"probability error {dp.max():.3e}"
-    return dict(near_ties=int((~keep).sum()), prob_err=float(dp.max()) if dp.size else 0.0)
+    pref = ref["prob"].astype(np.float64)
+    dp = np.abs(prob_gpu - pref)[keep]
+    bound = prob_bound(x, w_router, ref["idx"], pref)[keep]
+    worst = int(np.argmax(dp - bound)) if dp.size else 0
+    assert dp.size == 0 or np.all(dp <= bound), \
+        f"probability error {dp.flat[worst]:.3e} > bound {bound.flat[worst]:.3e}"
+    rel = dp / np.maximum(pref[keep], 1e-30)
+    return dict(near_ties=int((~keep).sum()), prob_err=float(dp.max()) if dp.size else 0.0,
+                prob_rel=float(rel.max()) if rel.size else 0.0,
+                bound_use=float((dp / bound).max()) if dp.size else 0.0)
 
 
 def compare_permutation(offs, st, dest, ref) -> None:
@@ -95,6 +123,27 @@ def compare_out(out_gpu, out_ref, tol_rel: float, what="out") -> dict:
     err = float(np.max(np.abs(g - out_ref))) if out_ref.size else 0.0
     assert err <= tol_rel * rms + 1e-30, f"{what}: max abs error {err:.4e} > {tol_rel} * RMS {rms:.4e}"
     return dict(max_abs=err, rms=rms, rel=err / rms if rms else 0.0)
+
+
+def bf16_half_ulp(v: np.ndarray) -> np.ndarray:
+    """Half a bfloat16 ulp at |v| (8 significant bits): 2**(floor(log2|v|) - 8)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.exp2(e - 8)
+
+
+def compare_bf16_out(out16, out_ref, tol_rel: float = 2e-2, what="out bf16") -> dict:
+    """bf16 output: |gpu - oracle| <= tol_rel * RMS + half ulp(oracle), element by element."""
+    g = np.asarray(out16, dtype=np.float64)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    rms = math.sqrt(float(np.mean(out_ref ** 2))) if out_ref.size else 0.0
+    err = np.abs(g - out_ref)
+    bound = tol_rel * rms + bf16_half_ulp(out_ref)
+    worst = int(np.argmax(err - bound)) if err.size else 0
+    assert err.size == 0 or np.all(err <= bound), \
+        f"{what}: error {err.flat[worst]:.4e} > bound {bound.flat[worst]:.4e} at |ref| {abs(out_ref.flat[worst]):.3f}"
+    return dict(max_abs=float(err.max()) if err.size else 0.0, rms=rms,
+                rel=float(err.max()) / rms if rms else 0.0)
 
 
 def to_host(t: torch.Tensor) -> np.ndarray:
