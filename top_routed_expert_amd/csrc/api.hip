@@ -391,6 +391,7 @@ moe_status moe_expert_gate_up(const moe_config* cfg, int32_t n_groups, int64_t n
   if (n_x_rows < 0 || n_gather < 0 || n_gather > n_rows)
     return fail(MOE_ERR_SHAPE, "need n_x_rows >= 0 and 0 <= n_gather <= n_rows");
   if (n_rows == 0) return ok();
+  if (n_x_rows == 0) return fail(MOE_ERR_SHAPE, "n_rows > 0 needs n_x_rows > 0");
   if (!offsets || !x || !w_gate || !w_up || !h || !ws || (n_gather > 0 && !gather))
     return fail(MOE_ERR_NULL, "offsets, x, w_gate, w_up, h, ws (and gather when n_gather > 0) are required");
   if ((s_gate == nullptr) != (s_up == nullptr)) return fail(MOE_ERR_NULL, "s_gate and s_up go together");
@@ -434,6 +435,7 @@ moe_status moe_grouped_ffn(const moe_config* cfg, int32_t n_groups, int64_t n_ro
   MOE_TRY(check_grouped(cfg, n_groups, n_rows, d_ff));
   if (n_x_rows < 0) return fail(MOE_ERR_SHAPE, "n_x_rows < 0");
   if (n_rows == 0) return ok();
+  if (n_x_rows == 0) return fail(MOE_ERR_SHAPE, "n_rows > 0 needs n_x_rows > 0");
   if (!offsets || !x || !w_gate || !w_up || !w_down || !y || !ws)
     return fail(MOE_ERR_NULL, "offsets, x, w_gate, w_up, w_down, y and ws are required");
   if (misaligned(offsets) || misaligned(x) || misaligned(gather) || misaligned(w_gate) || misaligned(w_up) ||

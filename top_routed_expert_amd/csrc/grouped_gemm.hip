@@ -16,7 +16,16 @@
 //
 // Generic path (fp32, or shapes the fast path does not cover): 64x64 output
 // tiles staged through LDS, plain fp32 FMA.
+#include <type_traits>
+
 #include "moe_internal.h"
+
+#ifndef MOE_NS_SMALL
+#define MOE_NS_SMALL 4  // pipeline depth of the 32-row tiles (few rows per expert: weight streaming)
+#endif
+#ifndef MOE_NS_LARGE
+#define MOE_NS_LARGE 4  // pipeline depth of the 128-row tiles
+#endif
 
 namespace moe {
 
@@ -37,6 +46,11 @@ __device__ __forceinline__ bool fetch_tile(const GemmArgs& p, int ti, int BM, Ti
   return true;
 }
 
+// Number of row tiles of a launch (device schedule, or dense rows).
+__device__ __forceinline__ int tile_count(const GemmArgs& p, int BM) {
+  return p.tiles ? *p.n_tiles : (int)((p.dense_rows + BM - 1) / BM);
+}
+
 // Source row of problem row r (gathered through the permutation, or direct);
 // -1 when it falls outside the A operand.
 __device__ __forceinline__ int64_t source_row(const GemmArgs& p, int64_t r) {
@@ -52,6 +66,16 @@ __device__ __forceinline__ const T* group_b(const GemmArgs& p, const void* main,
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// f(std::integral_constant<int, I>{}) for I = B .. E-1: indices into register
+// arrays are constant expressions, so the arrays never need memory.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // LDS offset (in bf16 elements) of 16-byte chunk `c` of staged row `r` (row
 // length KS): chunks are XOR-swizzled by (r & 7) so the 16-byte operand reads
 // of 8 consecutive rows hit distinct banks.
@@ -59,8 +83,12 @@ template <int KS>
 __device__ __forceinline__ int lds_off(int r, int c) { return r * KS + ((c ^ (r & 7)) << 3); }
 
 // EPI: epilogue; MT: 16-row MFMA tiles per block; NW: 16-column weight tiles
-// per wave and operand; KSTEPS: 32-element MFMA steps per pipeline stage.
-template <int EPI, int MT, int NW, int KSTEPS>
+// per wave and operand; KSTEPS: 32-element MFMA steps per pipeline stage;
+// NS: pipeline depth. Loads of stage k+NS-1 are issued before stage k is
+// multiplied, so NS-1 stages of weights (and A rows) are in flight per wave
+// while the matrix cores work; the ring lives in VGPRs and the loop is
+// unrolled by NS so every ring slot is a fixed register range.
+template <int EPI, int MT, int NW, int KSTEPS, int NS>
 __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
   constexpr int KS = 32 * KSTEPS;                       // contraction elements per stage
   constexpr int CPR = KS / 8;                           // 16-byte chunks per staged row
@@ -70,15 +98,21 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
   constexpr int NBT = EPI == EPI_SWIGLU ? 2 * NW : NW;  // weight tiles (16 columns) per wave
   constexpr int BN = 4 * NW * 16;                       // output columns per block
   static_assert(BM % RPP == 0, "row tile must be a whole number of staging passes");
+  static_assert(NS >= 2, "pipeline needs at least two stages");
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * KS];
 
-  // Hardware places block b on XCD b % 8. Give each XCD a contiguous run of
-  // logical blocks, column blocks fastest: the column blocks of a row tile
-  // (same A rows) and the row tiles of one expert (same weights) then run
-  // together on one XCD and share its L2.
+  // Hardware places block b on XCD b % 8. The grid is sized for the most
+  // tiles the schedule can produce; the active (tile, column block) pairs,
+  // counted on the device, are split evenly over the 8 XCDs, each XCD taking
+  // a contiguous run with column blocks fastest: the column blocks of a row
+  // tile (same A rows) and the row tiles of one expert (same weights) then
+  // run together on one XCD and share its L2.
   const int n_nb = (p.N + BN - 1) / BN;
-  const int per_xcd = gridDim.x >> 3;
-  const int L = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int active = tile_count(p, BM) * n_nb;
+  const int per_xcd = (active + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  const int L = (blockIdx.x & 7) * per_xcd + slot;
+  if (slot >= per_xcd || L >= active) return;
   const int ti = L / n_nb, nb = L - ti * n_nb;
   Tile t;
   if (!fetch_tile(p, ti, BM, t)) return;
@@ -88,13 +122,15 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
   const bf16_t* A = (const bf16_t*)p.a;
 
   // A staging: this thread copies 16-byte chunk (tid % CPR) of local rows
-  // tid / CPR + RPP*i. Rows outside the tile are zero.
+  // tid / CPR + RPP*i. Rows outside the tile (or with an invalid source) read
+  // row 0 of A instead: their outputs are never stored, and keeping every
+  // load unconditional keeps the pipeline's wait counts exact.
   const bf16_t* arow[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int64_t r = (int64_t)t.row0 + tid / CPR + RPP * i;
     const int64_t src = r < t.row1 ? source_row(p, r) : -1;
-    arow[i] = src >= 0 ? A + src * Kdim + (tid % CPR) * 8 : nullptr;
+    arow[i] = A + (src >= 0 ? src : 0) * Kdim + (tid % CPR) * 8;
   }
 
   // Weight rows of this wave: tile j covers output columns wcol0 + (j % NW)*16 + 0..15.
@@ -112,30 +148,27 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
     bptr[j] = (j < NW ? bg : bu) + (int64_t)col * Kdim + (lane >> 4) * 8;
   }
 
-  uint4 ra[NA];
-  uint4 rb0[NBT][KSTEPS], rb1[NBT][KSTEPS];
+  uint4 ra[NS][NA];
+  uint4 rb[NS][NBT][KSTEPS];
   f32x4 acc[MT][NBT];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int j = 0; j < NBT; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto load_a = [&](int ks) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i)
-      ra[i] = arow[i] ? *(const uint4*)(arow[i] + ks * KS) : make_uint4(0u, 0u, 0u, 0u);
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i) *(uint4*)&sA[buf][lds_off<KS>(tid / CPR + RPP * i, tid % CPR)] = ra[i];
-  };
-  auto load_b = [&](uint4(&rb)[NBT][KSTEPS], int ks) {
+  auto load_stage = [&](uint4(&a)[NA], uint4(&b)[NBT][KSTEPS], int ks) {
 #pragma unroll
     for (int j = 0; j < NBT; ++j)
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) rb[j][s] = *(const uint4*)(bptr[j] + ks * KS + s * 32);
+      for (int s = 0; s < KSTEPS; ++s) b[j][s] = *(const uint4*)(bptr[j] + ks * KS + s * 32);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) a[i] = *(const uint4*)(arow[i] + ks * KS);
   };
-  auto compute = [&](int buf, uint4(&rb)[NBT][KSTEPS]) {
+  auto store_a = [&](const uint4(&a)[NA], int buf) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) *(uint4*)&sA[buf][lds_off<KS>(tid / CPR + RPP * i, tid % CPR)] = a[i];
+  };
+  auto compute = [&](int buf, const uint4(&b)[NBT][KSTEPS]) {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
@@ -144,31 +177,44 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
             as_bf16x8(*(const uint4*)&sA[buf][lds_off<KS>(m * 16 + (lane & 15), s * 4 + (lane >> 4))]);
 #pragma unroll
         for (int j = 0; j < NBT; ++j)
-          acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(rb[j][s]), acc[m][j], 0, 0, 0);
+          acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(b[j][s]), acc[m][j], 0, 0, 0);
       }
     }
   };
 
-  load_a(0);
-  load_b(rb0, 0);
-  store_a(0);
+  // Software pipeline over nkp = nk rounded up to a multiple of NS stages.
+  // Every trip of the loop runs NS stages with no exit and no conditional
+  // memory operation, so the compiler's wait counts follow the fixed
+  // instruction order: a stage's loads are waited for only when its A tile
+  // is stored to LDS, NS-2 stages after they were issued. Stages past the
+  // end load the last real stage again (never used) and stage zeros as
+  // their A tile, so they add exactly zero to the accumulators.
+  const int last = nk - 1;
+  const int nkp = (nk + NS - 1) / NS * NS;
+  auto store_next = [&](const uint4(&a)[NA], int k_next) {
+    // component-wise mask (a select of whole vector structs would keep the
+    // ring in memory instead of registers)
+    const uint32_t keep = k_next < nk ? 0xffffffffu : 0u;
+    uint4 v[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) v[i] = make_uint4(a[i].x & keep, a[i].y & keep, a[i].z & keep, a[i].w & keep);
+    store_a(v, k_next & 1);
+  };
+  static_for<0, NS - 1>([&](auto S) {
+    constexpr int s = decltype(S)::value;
+    load_stage(ra[s], rb[s], s < nk ? s : last);
+  });
+  store_a(ra[0], 0);
   __syncthreads();
-  for (int ks = 0; ks < nk; ks += 2) {
-    if (ks + 1 < nk) {
-      load_a(ks + 1);
-      load_b(rb1, ks + 1);
-    }
-    compute(0, rb0);
-    if (ks + 1 < nk) store_a(1);
-    __syncthreads();
-    if (ks + 1 >= nk) break;
-    if (ks + 2 < nk) {
-      load_a(ks + 2);
-      load_b(rb0, ks + 2);
-    }
-    compute(1, rb1);
-    if (ks + 2 < nk) store_a(0);
-    __syncthreads();
+  for (int k0 = 0; k0 < nkp; k0 += NS) {
+    static_for<0, NS>([&](auto U) {
+      constexpr int u = decltype(U)::value;
+      const int k = k0 + u;
+      load_stage(ra[(u + NS - 1) % NS], rb[(u + NS - 1) % NS], k + NS - 1 < nk ? k + NS - 1 : last);
+      compute(k & 1, rb[u]);
+      store_next(ra[(u + 1) % NS], k + 1);
+      __syncthreads();
+    });
   }
 
   // Accumulator layout of a 16x16 MFMA tile: lane holds column (lane & 15),
@@ -325,11 +371,11 @@ hipError_t launch_build_tiles(const int32_t* offsets, int n_groups, int64_t n_ro
   return hipGetLastError();
 }
 
-template <int EPI, int MT, int NW, int KSTEPS = 2>
+template <int EPI, int MT, int NW, int NS, int KSTEPS = 2>
 static hipError_t launch_fast(const GemmArgs& g, hipStream_t s) {
   const int n_nb = (g.N + 4 * NW * 16 - 1) / (4 * NW * 16);
   const int64_t blocks = ((int64_t)g.max_tiles * n_nb + 7) / 8 * 8;
-  gemm_bf16_mfma<EPI, MT, NW, KSTEPS><<<(unsigned)blocks, 256, 0, s>>>(g);
+  gemm_bf16_mfma<EPI, MT, NW, KSTEPS, NS><<<(unsigned)blocks, 256, 0, s>>>(g);
   return hipGetLastError();
 }
 
@@ -349,11 +395,11 @@ hipError_t launch_grouped_gemm(int dtype, int epi, int block_rows, const GemmArg
   }
   const bool narrow = g.N <= 512;  // router-sized outputs: 64 columns per block
   if (block_rows == 32) {
-    if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 2, 2>(g, s);
-    return narrow ? launch_fast<EPI_F32, 2, 1>(g, s) : launch_fast<EPI_F32, 2, 4>(g, s);
+    if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 2, 2, MOE_NS_SMALL>(g, s);
+    return narrow ? launch_fast<EPI_F32, 2, 1, MOE_NS_SMALL>(g, s) : launch_fast<EPI_F32, 2, 4, MOE_NS_SMALL>(g, s);
   }
-  if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 8, 2>(g, s);
-  return narrow ? launch_fast<EPI_F32, 8, 1>(g, s) : launch_fast<EPI_F32, 8, 4>(g, s);
+  if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 8, 2, MOE_NS_LARGE>(g, s);
+  return narrow ? launch_fast<EPI_F32, 8, 1, MOE_NS_LARGE>(g, s) : launch_fast<EPI_F32, 8, 4, MOE_NS_LARGE>(g, s);
 }
 
 }  // namespace moe
