@@ -37,6 +37,37 @@ MFMA_F32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector, TFLOP/s
 FLUSH_BYTES = 512 << 20
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "top_routed_expert_amd", "csrc", f) for f in ("grouped_gemm.hip", "moe_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the gate/up kernel from the committed PMC summary.
+
+    The summary holds lines `source_sha256: <hash>` and
+    `traffic_bytes[<workload>]: <bytes>`; the figure is used only while the
+    kernel sources still hash the same (else null: the kernel changed since
+    the counters were taken).
+    """
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    import re
+    m = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    t = re.search(r"traffic_bytes\[%s\]:\s*([0-9.eE+]+)" % re.escape(workload), text)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return int(float(t.group(1)))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -45,8 +76,10 @@ def parse():
     ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "skew", "full"])
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=8)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one 1 GiB device-to-device copy: the known-size reference for HBM byte counters")
     return ap.parse_args()
 
 
@@ -147,7 +180,7 @@ def measure(spec, steps, warmup, flush_on):
         roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4))
     else:
         roof = dict(bound="mfma", achieved=round(tfs, 1), peak=peak_tf, unit="TFLOP/s", frac=round(tfs / peak_tf, 4))
-    roof.update(traffic=None, kernel="gemm_bf16_mfma<EPI_SWIGLU> (expert gate/up + SwiGLU)",
+    roof.update(traffic=measured_traffic(spec.name), kernel="gemm_bf16_mfma<EPI_SWIGLU> (expert gate/up + SwiGLU)",
                 launch_ms=round(k_ms, 4), algorithmic_bytes=int(k_bytes), algorithmic_flops=int(k_flops),
                 experts_read=k_experts, mfma_frac=round(tfs / peak_tf, 4), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
     res["roofline"] = roof
@@ -197,6 +230,13 @@ def main():
     spec = synth.spec(args.workload)
     print(f"[bench] workload={spec.name} T={spec.T} steps={args.steps} warmup={args.warmup}", file=sys.stderr,
           flush=True)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     res = measure(spec, args.steps, args.warmup, not args.no_flush)
     print(f"[bench] layer {res['ms']:.4f} ms/step; gate/up kernel {res['roofline']['launch_ms']:.4f} ms",
           file=sys.stderr, flush=True)

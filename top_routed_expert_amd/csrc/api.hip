@@ -96,7 +96,12 @@ bool fast_path(int dtype, int D, int F) { return dtype == MOE_BF16 && D % 64 == 
 struct RouteWs {
   float* logits;
 };
-RouteWs carve_route(Arena& a, const moe_config* c, int64_t T) { return {a.take<float>(T * c->n_experts)}; }
+int route_ksplit(const moe_config* c, int64_t T) {
+  return router_ksplit(fast_path(c->dtype, c->d_model, 64), T, c->d_model);
+}
+RouteWs carve_route(Arena& a, const moe_config* c, int64_t T) {
+  return {a.take<float>(route_ksplit(c, T) * T * c->n_experts)};
+}
 
 struct PermuteWs {
   int32_t* rank;
@@ -189,8 +194,10 @@ moe_status run_route(const moe_config* c, int64_t T, const void* x, const void* 
   g.out = ws.logits;
   g.ldo = c->n_experts;
   g.bias = bias;
+  g.ksplit = route_ksplit(c, T);
+  g.slice_stride = T * c->n_experts;
   MOE_TRY_HIP(launch_grouped_gemm(c->dtype, EPI_F32, BM, g, s), "router linear layer");
-  MOE_TRY_HIP(launch_topk(ws.logits, T, c->n_experts, c->top_k, idx, prob, gap, s), "router top-k");
+  MOE_TRY_HIP(launch_topk(ws.logits, g.ksplit, T, c->n_experts, c->top_k, idx, prob, gap, s), "router top-k");
   return MOE_OK;
 }
 
@@ -198,6 +205,7 @@ moe_status run_route(const moe_config* c, int64_t T, const void* x, const void* 
 // `build` is set), or dense rows of a single group when offsets is NULL.
 moe_status fill_tiles(GemmArgs& g, const SchedWs& ws, const int32_t* offsets, int n_groups, int64_t n_rows,
                       bool build, hipStream_t s) {
+  g.ksplit = 1;
   if (offsets && build)
     MOE_TRY_HIP(launch_build_tiles(offsets, n_groups, n_rows, ws.block_rows, ws.tiles, ws.n_tiles, ws.max_tiles, s),
                 "tile schedule");

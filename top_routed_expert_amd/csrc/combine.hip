@@ -3,7 +3,8 @@
 // router probabilities, are added to the shared expert's output:
 //   out[t] = y_shared[t] + sum_{k=0..K-1} prob[t,k] * y_perm[dest[t*K+k]]
 // in fp32, in that order, with one final rounding to the output type.
-// One block per token; the K source rows are read with 16-byte loads.
+// One block per (token, 1024-column chunk); the K source rows are read with
+// 16-byte loads.
 #include "moe_internal.h"
 
 namespace moe {
@@ -38,6 +39,8 @@ __global__ void __launch_bounds__(256) combine_kernel(int D, int K, const float*
   __shared__ float s_p[64];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
+  const int c0 = (int)blockIdx.y * 1024;  // this block's column chunk
+  const int c1 = D < c0 + 1024 ? D : c0 + 1024;
   if (tid < K) {
     const int64_t d = dest[t * K + tid];
     s_row[tid] = (d >= 0 && d < n_perm) ? d : -1;
@@ -45,7 +48,7 @@ __global__ void __launch_bounds__(256) combine_kernel(int D, int K, const float*
   }
   __syncthreads();
   if ((D & 3) == 0) {
-    for (int c = tid * 4; c < D; c += 1024) {
+    for (int c = c0 + tid * 4; c < c1; c += 1024) {
       float4 acc = y_shared ? *(const float4*)(y_shared + t * D + c) : make_float4(0.f, 0.f, 0.f, 0.f);
       for (int k = 0; k < K; ++k) {
         if (s_row[k] < 0) continue;
@@ -59,7 +62,7 @@ __global__ void __launch_bounds__(256) combine_kernel(int D, int K, const float*
       store4(out + t * D + c, acc);
     }
   } else {
-    for (int c = tid; c < D; c += 256) {
+    for (int c = c0 + tid; c < c1; c += 256) {
       float acc = y_shared ? y_shared[t * D + c] : 0.f;
       for (int k = 0; k < K; ++k)
         if (s_row[k] >= 0) acc = fmaf(s_p[k], y_perm[s_row[k] * D + c], acc);
@@ -73,10 +76,11 @@ __global__ void __launch_bounds__(256) combine_kernel(int D, int K, const float*
 hipError_t launch_combine(int out_dtype, int64_t T, int D, int K, const float* y_perm, int64_t n_perm_rows,
                           const int32_t* dest, const float* prob, const float* y_shared, void* out, hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  const dim3 grid((unsigned)T, (unsigned)((D + 1023) / 1024));
   if (out_dtype == MOE_BF16)
-    combine_kernel<bf16_t><<<(unsigned)T, 256, 0, s>>>(D, K, y_perm, n_perm_rows, dest, prob, y_shared, (bf16_t*)out);
+    combine_kernel<bf16_t><<<grid, 256, 0, s>>>(D, K, y_perm, n_perm_rows, dest, prob, y_shared, (bf16_t*)out);
   else
-    combine_kernel<float><<<(unsigned)T, 256, 0, s>>>(D, K, y_perm, n_perm_rows, dest, prob, y_shared, (float*)out);
+    combine_kernel<float><<<grid, 256, 0, s>>>(D, K, y_perm, n_perm_rows, dest, prob, y_shared, (float*)out);
   return hipGetLastError();
 }
 

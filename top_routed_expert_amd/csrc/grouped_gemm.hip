@@ -23,9 +23,16 @@
 #ifndef MOE_NS_SMALL
 #define MOE_NS_SMALL 4  // pipeline depth of the 32-row tiles (few rows per expert: weight streaming)
 #endif
+#ifndef MOE_GU_NW_SMALL
+#define MOE_GU_NW_SMALL 1  // 16-column tiles per wave (gate and up each), 32-row tiles
+#endif
+#ifndef MOE_DN_NW_SMALL
+#define MOE_DN_NW_SMALL 2  // 16-column tiles per wave, down projection, 32-row tiles
+#endif
 #ifndef MOE_NS_LARGE
 #define MOE_NS_LARGE 4  // pipeline depth of the 128-row tiles
 #endif
+
 
 namespace moe {
 
@@ -118,8 +125,11 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
   if (!fetch_tile(p, ti, BM, t)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int Kdim = p.Kdim, nk = Kdim / KS;
-  const bf16_t* A = (const bf16_t*)p.a;
+  const int Kdim = p.Kdim;
+  // contraction slice of this block (router split-K): stages [kbase, kbase + nk)
+  const int nk = Kdim / KS / p.ksplit;
+  const int kbase = (int)blockIdx.y * nk;
+  const bf16_t* A = (const bf16_t*)p.a + (int64_t)kbase * KS;
 
   // A staging: this thread copies 16-byte chunk (tid % CPR) of local rows
   // tid / CPR + RPP*i. Rows outside the tile (or with an invalid source) read
@@ -145,7 +155,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
   for (int j = 0; j < NBT; ++j) {
     int col = wcol0 + (j % NW) * 16 + (lane & 15);
     col = col < p.N ? col : p.N - 1;
-    bptr[j] = (j < NW ? bg : bu) + (int64_t)col * Kdim + (lane >> 4) * 8;
+    bptr[j] = (j < NW ? bg : bu) + (int64_t)col * Kdim + (int64_t)kbase * KS + (lane >> 4) * 8;
   }
 
   uint4 ra[NS][NA];
@@ -233,7 +243,8 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
         if constexpr (EPI == EPI_SWIGLU) {
           ((bf16_t*)p.out)[r * p.ldo + col] = f32_to_bf16(silu(acc[m][j][v]) * acc[m][j + NW][v]);
         } else {
-          ((float*)p.out)[r * p.ldo + col] = acc[m][j][v] + (p.bias ? p.bias[col] : 0.f);
+          const float b = (p.bias && blockIdx.y == 0) ? p.bias[col] : 0.f;
+          ((float*)p.out + (int64_t)blockIdx.y * p.slice_stride)[r * p.ldo + col] = acc[m][j][v] + b;
         }
       }
     }
@@ -361,6 +372,14 @@ int gemm_block_rows(bool fast, int64_t rows, int n_groups) {
   return rows <= 32 * (int64_t)n_groups ? 32 : 128;
 }
 
+int router_ksplit(bool fast, int64_t T, int Kdim) {
+  if (!fast || T > 64) return 1;
+  const int nk = Kdim / 64;
+  int ks = 16;
+  while (ks > 1 && nk % ks) ks >>= 1;
+  return ks;
+}
+
 int64_t gemm_max_tiles(int64_t n_rows, int n_groups, int block_rows) {
   return n_rows / block_rows + n_groups;  // sum over groups of ceil(len / BM)
 }
@@ -375,7 +394,7 @@ template <int EPI, int MT, int NW, int NS, int KSTEPS = 2>
 static hipError_t launch_fast(const GemmArgs& g, hipStream_t s) {
   const int n_nb = (g.N + 4 * NW * 16 - 1) / (4 * NW * 16);
   const int64_t blocks = ((int64_t)g.max_tiles * n_nb + 7) / 8 * 8;
-  gemm_bf16_mfma<EPI, MT, NW, KSTEPS, NS><<<(unsigned)blocks, 256, 0, s>>>(g);
+  gemm_bf16_mfma<EPI, MT, NW, KSTEPS, NS><<<dim3((unsigned)blocks, (unsigned)g.ksplit), 256, 0, s>>>(g);
   return hipGetLastError();
 }
 
@@ -395,8 +414,9 @@ hipError_t launch_grouped_gemm(int dtype, int epi, int block_rows, const GemmArg
   }
   const bool narrow = g.N <= 512;  // router-sized outputs: 64 columns per block
   if (block_rows == 32) {
-    if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 2, 2, MOE_NS_SMALL>(g, s);
-    return narrow ? launch_fast<EPI_F32, 2, 1, MOE_NS_SMALL>(g, s) : launch_fast<EPI_F32, 2, 4, MOE_NS_SMALL>(g, s);
+    if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 2, MOE_GU_NW_SMALL, MOE_NS_SMALL>(g, s);
+    return narrow ? launch_fast<EPI_F32, 2, 1, MOE_NS_SMALL>(g, s)
+                  : launch_fast<EPI_F32, 2, MOE_DN_NW_SMALL, MOE_NS_SMALL>(g, s);
   }
   if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 8, 2, MOE_NS_LARGE>(g, s);
   return narrow ? launch_fast<EPI_F32, 8, 1, MOE_NS_LARGE>(g, s) : launch_fast<EPI_F32, 8, 4, MOE_NS_LARGE>(g, s);

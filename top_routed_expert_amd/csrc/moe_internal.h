@@ -63,19 +63,24 @@ struct GemmArgs {
   void* out;              // [rows, ldo]
   int64_t ldo;
   const float* bias;      // EPI_F32: per-column bias or NULL
+  int32_t ksplit;         // EPI_F32 only: the contraction is cut into ksplit slices;
+  int64_t slice_stride;   //   slice s writes its partial sums to out + s*slice_stride
 };
 
 // Launchers (grouped_gemm.hip). `dtype` is MOE_BF16 or MOE_F32 for A/B; the
 // SwiGLU output has the same dtype; EPI_F32 output is fp32.
 // Row-tile height: 32 or 128 on the bf16 MFMA path (`fast`), 64 otherwise.
 int gemm_block_rows(bool fast, int64_t rows, int n_groups);
+// Contraction slices of the router GEMM for T tokens (1 unless T is small).
+int router_ksplit(bool fast, int64_t T, int Kdim);
 int64_t gemm_max_tiles(int64_t n_rows, int n_groups, int block_rows);
 hipError_t launch_build_tiles(const int32_t* offsets, int n_groups, int64_t n_rows, int block_rows,
                               Tile* tiles, int32_t* n_tiles, int32_t max_tiles, hipStream_t s);
 hipError_t launch_grouped_gemm(int dtype, int epi, int block_rows, const GemmArgs& g, hipStream_t s);
 
 // route.hip
-hipError_t launch_topk(const float* logits, int64_t T, int E, int K, int32_t* idx, float* prob,
+// Logits are the sum of nsplit partial arrays [nsplit][T][E], added in slice order.
+hipError_t launch_topk(const float* logits, int nsplit, int64_t T, int E, int K, int32_t* idx, float* prob,
                        float* gap, hipStream_t s);
 
 // permute.hip
