@@ -124,7 +124,7 @@ struct SchedWs {
 };
 SchedWs carve_sched(Arena& a, const moe_config* c, int n_groups, int64_t n_rows, int d_ff) {
   SchedWs w;
-  w.block_rows = gemm_block_rows(fast_path(c->dtype, c->d_model, d_ff), n_rows, n_groups);
+  w.block_rows = gemm_block_rows(fast_path(c->dtype, c->d_model, d_ff), n_rows, n_groups, true);
   w.max_tiles = (int32_t)gemm_max_tiles(n_rows, n_groups, w.block_rows);
   w.tiles = a.take<Tile>(w.max_tiles);
   w.n_tiles = a.take<int32_t>(1);
@@ -189,7 +189,7 @@ moe_status run_route(const moe_config* c, int64_t T, const void* x, const void* 
   g.N = c->n_experts;
   g.Kdim = c->d_model;
   g.dense_rows = T;
-  const int BM = gemm_block_rows(fast, T, 1);
+  const int BM = gemm_block_rows(fast, T, 1, false);
   g.max_tiles = (int32_t)((T + BM - 1) / BM);
   g.out = ws.logits;
   g.ldo = c->n_experts;

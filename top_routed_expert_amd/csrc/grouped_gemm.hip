@@ -367,9 +367,10 @@ __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __rest
 
 }  // namespace
 
-int gemm_block_rows(bool fast, int64_t rows, int n_groups) {
+int gemm_block_rows(bool fast, int64_t rows, int n_groups, bool allow_big) {
   if (!fast) return 64;
-  return rows <= 32 * (int64_t)n_groups ? 32 : 128;
+  if (rows <= 32 * (int64_t)n_groups) return 32;
+  return allow_big && rows >= 96 * (int64_t)n_groups ? 256 : 128;
 }
 
 int router_ksplit(bool fast, int64_t T, int Kdim) {
@@ -412,6 +413,7 @@ hipError_t launch_grouped_gemm(int dtype, int epi, int block_rows, const GemmArg
     }
     return hipGetLastError();
   }
+  if (block_rows == 256) return launch_grouped_gemm_big(epi, g, s);
   const bool narrow = g.N <= 512;  // router-sized outputs: 64 columns per block
   if (block_rows == 32) {
     if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 2, MOE_GU_NW_SMALL, MOE_NS_SMALL>(g, s);

@@ -1,0 +1,249 @@
+// Expert GEMMs for many rows per expert (prefill): 256 x 256 block tiles.
+//
+// Every expert is an independent FFN (page "Step3.5 Flash 大模型技术深度解析",
+// section 3.2.1). With a few hundred rows per expert, the weights of one
+// column block should leave HBM once and be multiplied by all of the
+// expert's rows; a 256-row tile covers a whole expert in most cases, and a
+// 256-weight-row tile halves the operand bytes per flop pulled from L2
+// relative to 128 x 256 tiles.
+//
+// Block: 4 waves in a 2 x 2 layout, each wave 128 rows x 128 weight rows =
+// 8 x 8 MFMA 16x16x32 tiles (256 fp32 accumulators per lane). For gate/up
+// the 256 weight rows of a block are [gate c0..c0+63, up c0..c0+63,
+// gate c0+64..c0+127, up c0+64..c0+127], so each wave holds the gate and up
+// sums of the same 64 columns and applies the SwiGLU in registers.
+//
+// Both operands go HBM/L2 -> LDS through direct loads (global_load_lds,
+// 16 bytes per lane, no VGPR staging) into a ring of NS = 4 stages of one
+// 32-element MFMA step each (16 KB of A + 16 KB of B per stage, 128 KB in
+// all). Waits are explicit: a wave waits for its own loads of stage k with
+// s_waitcnt vmcnt (loads complete in issue order; two younger stages stay
+// in flight), then one s_barrier makes every wave's stage-k loads visible
+// and ends every wave's reads of the slot about to be refilled. The
+// barrier is issued as inline asm with a memory clobber: the compiler may
+// not move memory accesses across it and does not add a drain of its own.
+//
+// LDS rows are 64 bytes (four 16-byte chunks); chunk q of row r is stored
+// at position q ^ ((r >> 1) & 3), so the 16-byte MFMA operand reads of
+// consecutive rows spread over all banks.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+#ifndef MOE_BIG_NS
+#define MOE_BIG_NS 4
+#endif
+constexpr int BIG_NS = MOE_BIG_NS;  // ring stages
+constexpr int BIG_KS = 32;     // contraction elements per stage (one MFMA step)
+constexpr int BIG_ROWS = 256;  // A rows and B (weight) rows per block tile
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte operand chunk
+
+__device__ __forceinline__ bf16x8 as_bf16x8_big(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// s_waitcnt immediate (gfx9 encoding) waiting for at most `vm` outstanding
+// vector-memory operations and leaving the other counters unconstrained.
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+
+template <int EPI>
+__global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[BIG_NS][2][BIG_ROWS * BIG_KS];
+
+  const int BN = EPI == EPI_SWIGLU ? BIG_ROWS / 2 : BIG_ROWS;  // output columns per block
+  const int n_nb = (p.N + BN - 1) / BN;
+  const int n_tiles = p.tiles ? *p.n_tiles : (int)((p.dense_rows + BIG_ROWS - 1) / BIG_ROWS);
+  const int active = n_tiles * n_nb;
+  const int per_xcd = (active + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  const int L = (blockIdx.x & 7) * per_xcd + slot;
+  if (slot >= per_xcd || L >= active) return;
+  const int ti = L / n_nb, nb = L - ti * n_nb;
+  Tile t;
+  if (p.tiles) {
+    t = p.tiles[ti];
+  } else {
+    t.group = 0;
+    t.row0 = ti * BIG_ROWS;
+    t.row1 = (int32_t)((int64_t)t.row0 + BIG_ROWS < p.dense_rows ? t.row0 + BIG_ROWS : p.dense_rows);
+  }
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Kdim = p.Kdim, nk = Kdim / BIG_KS;
+  const bf16_t* A = (const bf16_t*)p.a;
+  const bf16_t* Bg = p.b0 == nullptr ? nullptr
+                   : (t.group < p.n_main ? (const bf16_t*)p.b0 + (int64_t)t.group * p.b_stride
+                                         : (const bf16_t*)p.b0_extra);
+  const bf16_t* Bu = EPI == EPI_SWIGLU ? (t.group < p.n_main ? (const bf16_t*)p.b1 + (int64_t)t.group * p.b_stride
+                                                             : (const bf16_t*)p.b1_extra)
+                                       : Bg;
+
+  // Direct-load sources. Load instruction i (0..3) of this wave fills rows
+  // R = wave*64 + i*16 .. R+15 of a stage; lane l writes the 16 bytes at LDS
+  // position (row R + l/4, physical chunk l%4), i.e. logical chunk
+  // (l%4) ^ swz(row). Rows outside the tile read row 0 (never stored).
+  const bf16_t* asrc[4];
+  const bf16_t* bsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = wave * 64 + i * 16 + (lane >> 2);
+    const int q = (lane & 3) ^ swz(row);
+    const int64_t r = (int64_t)t.row0 + row;
+    int64_t src = -1;
+    if (r < t.row1) {
+      src = r < p.n_gather ? (int64_t)p.gather[r] : r - p.n_gather;
+      if (src >= p.n_a_rows) src = -1;
+    }
+    asrc[i] = A + (src >= 0 ? src : 0) * Kdim + q * 8;
+    // weight row `row` of the block tile
+    int col;
+    const bf16_t* base;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int seg = row >> 6;                  // gate, up, gate, up
+      col = nb * BN + (seg >> 1) * 64 + (row & 63);
+      base = (seg & 1) ? Bu : Bg;
+    } else {
+      col = nb * BN + row;
+      base = Bg;
+    }
+    col = col < p.N ? col : p.N - 1;
+    bsrc[i] = base + (int64_t)col * Kdim + q * 8;
+  }
+
+  auto issue_stage = [&](int slot, int ks) {
+    const int koff = ks * BIG_KS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + koff),
+                                       (lds_void_t*)&lds[slot][0][(wave * 64 + i * 16) * BIG_KS], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + koff),
+                                       (lds_void_t*)&lds[slot][1][(wave * 64 + i * 16) * BIG_KS], 16, 0, 0);
+    }
+  };
+
+  // wave (wm, wn): rows wm*128 .., weight rows wn*128 ..
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // operand read of lane (r = lane & 15, q = lane >> 4) from a 16-row tile
+  const int rq = lane >> 4, rr = lane & 15;
+  // LDS byte offsets of this lane's operand chunks inside a slot (the row
+  // swizzle depends only on the row, which is fixed per lane and tile)
+  uint32_t aoff[8], boff[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int row = wm * 128 + m * 16 + rr;
+    aoff[m] = (uint32_t)(row * BIG_KS + ((rq ^ swz(row)) << 3)) * 2u;
+  }
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int row = wn * 128 + n * 16 + rr;
+    boff[n] = (uint32_t)(BIG_ROWS * BIG_KS + row * BIG_KS + ((rq ^ swz(row)) << 3)) * 2u;
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)&lds[0][0][0];
+  constexpr uint32_t SLOT_BYTES = 2u * BIG_ROWS * BIG_KS * 2u;
+  // Operand reads are issued as inline ds_read_b128 followed by an explicit
+  // lgkmcnt wait: the compiler cannot prove they do not alias the direct
+  // loads still in flight and would otherwise drain every load first.
+  // LDS reads complete in issue order: the eight B chunks first, then A row
+  // tile by row tile, and the multiplies of row tile m start as soon as its
+  // chunk is in (lgkmcnt(7 - m)). Each wait names the registers it guards,
+  // so no multiply can be scheduled above the wait that covers its operand.
+  auto compute = [&](int slot) {
+    u32x4 a[8], b[8];
+    const uint32_t sb = lds_base + (uint32_t)slot * SLOT_BYTES;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) asm volatile("ds_read_b128 %0, %1" : "=v"(b[n]) : "v"(sb + boff[n]));
+#pragma unroll
+    for (int m = 0; m < 8; ++m) asm volatile("ds_read_b128 %0, %1" : "=v"(a[m]) : "v"(sb + aoff[m]));
+    asm volatile("s_waitcnt lgkmcnt(7)"
+                 : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(b[4]), "+v"(b[5]), "+v"(b[6]), "+v"(b[7]),
+                   "+v"(a[0]));
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (m == 1) asm volatile("s_waitcnt lgkmcnt(6)" : "+v"(a[1]));
+      if (m == 2) asm volatile("s_waitcnt lgkmcnt(5)" : "+v"(a[2]));
+      if (m == 3) asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(a[3]));
+      if (m == 4) asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(a[4]));
+      if (m == 5) asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(a[5]));
+      if (m == 6) asm volatile("s_waitcnt lgkmcnt(1)" : "+v"(a[6]));
+      if (m == 7) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[7]));
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_big(a[m]), as_bf16x8_big(b[n]), acc[m][n], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // keep each row tile's wait ahead of its own multiplies only
+    }
+  };
+
+  // Prologue: stages 0..NS-2 in flight (clamped: stages past the end re-load
+  // the last stage; they are never read).
+  const int last = nk - 1;
+#pragma unroll
+  for (int s = 0; s < BIG_NS - 1; ++s) issue_stage(s, s < nk ? s : last);
+  // Every iteration issues the same 8 loads per wave, unconditionally, so
+  // one fixed wait count holds: when at most the 2 younger stages' loads are
+  // outstanding, this wave's stage k has landed. The barrier then publishes
+  // every wave's stage k and retires every wave's reads of slot (k-1)%NS,
+  // which the loads issued next refill.
+#pragma unroll 1
+  for (int k = 0; k < nk; ++k) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * (BIG_NS - 2)));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    issue_stage((k + BIG_NS - 1) % BIG_NS, k + BIG_NS - 1 < nk ? k + BIG_NS - 1 : last);
+    compute(k % BIG_NS);
+  }
+  // drain the loads of the clamped trailing stages before the block ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+  // Accumulator layout of a 16x16 MFMA tile: lane holds column (lane & 15),
+  // rows 4*(lane >> 4) + v.
+  const int64_t rbase = (int64_t)t.row0 + wm * 128 + (lane >> 4) * 4;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t r = rbase + m * 16 + v;
+      if (r >= t.row1) continue;
+      if constexpr (EPI == EPI_SWIGLU) {
+        // weight tiles 0..3: gate of columns wn*64 + n*16; 4..7: up of the same columns
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int col = nb * BN + wn * 64 + n * 16 + (lane & 15);
+          if (col < p.N)
+            ((bf16_t*)p.out)[r * p.ldo + col] = f32_to_bf16(silu(acc[m][n][v]) * acc[m][n + 4][v]);
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          const int col = nb * BN + wn * 128 + n * 16 + (lane & 15);
+          if (col < p.N) ((float*)p.out)[r * p.ldo + col] = acc[m][n][v] + (p.bias ? p.bias[col] : 0.f);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool big_tiles_fit(int Kdim) { return Kdim % BIG_KS == 0; }
+
+hipError_t launch_grouped_gemm_big(int epi, const GemmArgs& g, hipStream_t s) {
+  if (g.max_tiles <= 0 || g.N <= 0) return hipSuccess;
+  const int BN = epi == EPI_SWIGLU ? BIG_ROWS / 2 : BIG_ROWS;
+  const int n_nb = (g.N + BN - 1) / BN;
+  const int64_t blocks = ((int64_t)g.max_tiles * n_nb + 7) / 8 * 8;
+  if (epi == EPI_SWIGLU) gemm_bf16_big<EPI_SWIGLU><<<(unsigned)blocks, 256, 0, s>>>(g);
+  else gemm_bf16_big<EPI_F32><<<(unsigned)blocks, 256, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+}  // namespace moe
