@@ -38,7 +38,8 @@ FLUSH_BYTES = 512 << 20
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "top_routed_expert_amd", "csrc", f) for f in ("grouped_gemm.hip", "moe_internal.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "top_routed_expert_amd", "csrc", f)
+                  for f in ("grouped_gemm.hip", "grouped_gemm_big.hip", "moe_internal.h")]
 
 
 def kernel_source_hash() -> str:
@@ -78,6 +79,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--layout", default="packed", choices=["packed", "rows"],
+                    help="weight layout the timed steps read (bf16 layers; converted once before timing)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 1 GiB device-to-device copy: the known-size reference for HBM byte counters")
     return ap.parse_args()
@@ -127,7 +130,16 @@ def layer_flops_bytes(spec, counts):
     return flops, wbytes + abytes, touched
 
 
-def measure(spec, steps, warmup, flush_on):
+def gate_up_kernel(rows: int, groups: int) -> str:
+    """Name of the gate/up kernel the library picks for `rows` rows over `groups` groups (bf16)."""
+    if rows <= 32 * groups:
+        return "gemm_bf16_mfma<EPI_SWIGLU>, 32-row tiles"
+    if rows >= 96 * groups:
+        return "gemm_bf16_big<EPI_SWIGLU>, 256x256 tiles"
+    return "gemm_bf16_mfma<EPI_SWIGLU>, 128-row tiles"
+
+
+def measure(spec, steps, warmup, flush_on, packed=True):
     import numpy as np
     import torch
 
@@ -135,19 +147,23 @@ def measure(spec, steps, warmup, flush_on):
     import top_routed_expert_amd as moe
 
     L = synth.make_layer(spec, "cuda")
-    cfg = moe.config_for(spec)
+    packed = packed and spec.dtype == "bf16"
+    cfg = moe.config_for(spec, packed=packed)
+    # weights are converted once, as at load time; the timed steps read only the packed copy
+    W = moe.pack_layer(L) if packed else L
+    torch.cuda.synchronize()
     flush = Flusher(flush_on)
     dev = L["x"].device
     T, D, E, K, F = spec.T, spec.D, spec.E, spec.K, spec.F
     # --- whole layer -------------------------------------------------------
     ws = moe.Workspace(cfg, T, dev)
-    wt = moe.weights_struct(cfg, L)
+    wt = moe.weights_struct(cfg, W)
     out = torch.empty((T, D), dtype=cfg.odtype, device=dev)
-    layer = lambda: moe.layer_forward(cfg, L["x"], L, out=out, workspace=ws, weights=wt)
+    layer = lambda: moe.layer_forward(cfg, L["x"], W, out=out, workspace=ws, weights=wt)
     ms, wall = timed(layer, steps, warmup, flush)
     ms_step = float(np.mean(ms))
     # routing of this batch (outside the timed region) for the work accounting
-    idx, prob = moe.route(cfg, L["x"], L["w_router"], L["bias"])
+    idx, prob = moe.route(cfg, L["x"], W["w_router"], L["bias"])
     offs, st, dest = moe.permute(cfg, idx)
     counts = np.diff(offs.cpu().numpy())
     flops, nbytes, touched = layer_flops_bytes(spec, counts)
@@ -162,8 +178,8 @@ def measure(spec, steps, warmup, flush_on):
     h = torch.empty((n_rows, F), dtype=cfg.dtype, device=dev)
     gws = torch.empty(moe.lib().moe_expert_workspace_bytes(
         __import__("ctypes").byref(cfg.c()), E + (1 if fused else 0), n_rows, F), dtype=torch.uint8, device=dev)
-    gate_up = lambda: moe.expert_gate_up(cfg, offs_ext, L["x"], L["w_gate"], L["w_up"], gather=st, n_rows=n_rows,
-                                         s_gate=L["s_gate"] if fused else None, s_up=L["s_up"] if fused else None,
+    gate_up = lambda: moe.expert_gate_up(cfg, offs_ext, L["x"], W["w_gate"], W["w_up"], gather=st, n_rows=n_rows,
+                                         s_gate=W["s_gate"] if fused else None, s_up=W["s_up"] if fused else None,
                                          h=h, ws=gws)
     kms, _ = timed(gate_up, steps, warmup, flush)
     k_ms = float(np.mean(kms))
@@ -180,11 +196,14 @@ def measure(spec, steps, warmup, flush_on):
         roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4))
     else:
         roof = dict(bound="mfma", achieved=round(tfs, 1), peak=peak_tf, unit="TFLOP/s", frac=round(tfs / peak_tf, 4))
-    roof.update(traffic=measured_traffic(spec.name), kernel="gemm_bf16_mfma<EPI_SWIGLU> (expert gate/up + SwiGLU)",
+    kname = gate_up_kernel(n_rows, E + (1 if fused else 0)) if spec.dtype == "bf16" else "gemm_generic<EPI_SWIGLU>"
+    roof.update(traffic=measured_traffic(spec.name), kernel=kname + " (expert gate/up + SwiGLU)",
                 launch_ms=round(k_ms, 4), algorithmic_bytes=int(k_bytes), algorithmic_flops=int(k_flops),
                 experts_read=k_experts, mfma_frac=round(tfs / peak_tf, 4), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
     res["roofline"] = roof
     res["L"] = L
+    res["layout"] = "packed" if packed else "rows"
+    del W
     return res
 
 
@@ -237,7 +256,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    res = measure(spec, args.steps, args.warmup, not args.no_flush)
+    res = measure(spec, args.steps, args.warmup, not args.no_flush, args.layout == "packed")
     print(f"[bench] layer {res['ms']:.4f} ms/step; gate/up kernel {res['roofline']['launch_ms']:.4f} ms",
           file=sys.stderr, flush=True)
     line = {
@@ -248,7 +267,7 @@ def main():
         "config": {"workload": spec.name, "tokens": spec.T, "d_model": spec.D, "routed_experts": spec.E,
                    "top_k": spec.K, "d_expert": spec.F, "shared_experts": 1 if spec.Fs else 0,
                    "d_shared": spec.Fs, "router_bias": "zipf" if spec.skew else "none",
-                   "parallelism": "single-gpu"},
+                   "weight_layout": res["layout"], "parallelism": "single-gpu"},
         "roofline": res["roofline"],
         "layer": {"ms_min": round(res["ms_min"], 5), "experts_touched": res["touched"],
                   "expert_load_skew": round(res["skew"], 3), "tflops": round(res["layer_tflops"], 2),
@@ -265,7 +284,7 @@ def main():
         torch.cuda.empty_cache()
         sec = synth.spec("prefill")
         print(f"[bench] secondary workload={sec.name} T={sec.T}", file=sys.stderr, flush=True)
-        r2 = measure(sec, args.steps, args.warmup, not args.no_flush)
+        r2 = measure(sec, args.steps, args.warmup, not args.no_flush, args.layout == "packed")
         line["secondary"] = {"workload": sec.name, "tokens": sec.T, "value": round(r2["tokens_per_s"], 1),
                              "unit": "tokens/s", "ms_per_step": round(r2["ms"], 5),
                              "layer_mfma_frac": round(r2["layer_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -21,7 +21,7 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every tensor pointer is DEVICE memory owned by the caller, dense
- *    row-major, 16-byte aligned. The library never allocates, frees or keeps
+ *    row-major (weights: or packed, below), 16-byte aligned. The library never allocates, frees or keeps
  *    a pointer past the call; it holds no mutable global state.
  *  - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
  *    null stream) and returns; results are valid once the stream is
@@ -62,6 +62,9 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Storage layout of the weight matrices (see "Packed weights" below). */
+typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_PACKED = 1 } moe_weight_layout;
+
 /* Shape of one layer (section 3.2.1 / 3.2.2 of the page above). */
 typedef struct {
   int32_t d_model;   /* D: token width (4096 on the page)                    */
@@ -71,6 +74,7 @@ typedef struct {
   int32_t d_shared;  /* Fs: SwiGLU width of the shared expert; 0 = none      */
   int32_t dtype;     /* moe_dtype of x and of every weight                   */
   int32_t out_dtype; /* moe_dtype of the layer output                        */
+  int32_t weight_layout; /* moe_weight_layout of every weight matrix argument  */
 } moe_config;
 
 /* The layer's weights (device pointers, row-major).
@@ -91,6 +95,33 @@ typedef struct {
   const void* s_up;
   const void* s_down;
 } moe_weights;
+
+/* Packed weights
+ * --------------
+ * With cfg->weight_layout == MOE_LAYOUT_PACKED every weight matrix argument
+ * (w_router, w_gate, w_up, w_down, s_gate, s_up, s_down) points to the
+ * output of moe_pack_weights for that array instead of the row-major array.
+ * This is a storage layout only, made once when weights are loaded: the
+ * results are bit-identical to those with row-major weights. It exists so
+ * that every weight load of the matrix-core kernels reads 1 KB contiguous.
+ * It requires dtype MOE_BF16 and d_model, d_expert, d_shared (and d_ff of the
+ * grouped entry points) multiples of 64 (else MOE_ERR_UNSUPPORTED).
+ *
+ * Layout of one matrix W [rows, cols] (cols % 32 == 0): 16-row x 32-column
+ * fragments, fragment (ct, kb) = rows 16ct.., columns 32kb.., stored in the
+ * order ct-major, kb-minor; a fragment is 64 lanes x 8 values where lane
+ * l = c + 16q holds W[16ct + c][32kb + 8q + 0..7]. Rows past `rows` (when
+ * rows % 16 != 0) are zero. A stack of n_mats matrices is packed matrix
+ * after matrix.
+ *
+ * moe_packed_weights_bytes: bytes of the packed form of n_mats [rows, cols]
+ *   bf16 matrices: n_mats * ceil(rows/16)*16 * cols * 2; SIZE_MAX when a
+ *   size is negative or cols % 32 != 0.
+ * moe_pack_weights: src [n_mats, rows, cols] bf16 row-major -> dst (device,
+ *   >= dst_bytes = moe_packed_weights_bytes(...) bytes, not overlapping src). */
+size_t moe_packed_weights_bytes(int64_t n_mats, int64_t rows, int64_t cols);
+moe_status moe_pack_weights(int64_t n_mats, int64_t rows, int64_t cols, const void* src, void* dst,
+                            size_t dst_bytes, void* stream);
 
 /* Workspace queries. They return the bytes the matching entry point needs
  * in its `ws` argument, or SIZE_MAX when the configuration is invalid. */

@@ -26,7 +26,8 @@ def header_functions() -> list[str]:
 
 
 def cfg(**kw) -> M.MoeConfig:
-    c = dict(d_model=256, n_experts=16, top_k=4, d_expert=128, d_shared=128, dtype=moe.BF16, out_dtype=moe.BF16)
+    c = dict(d_model=256, n_experts=16, top_k=4, d_expert=128, d_shared=128, dtype=moe.BF16, out_dtype=moe.BF16,
+             weight_layout=moe.LAYOUT_ROWS)
     c.update(kw)
     return M.MoeConfig(**c)
 
@@ -37,7 +38,7 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails its checks
 def test_exports_every_declared_function():
     L = moe.lib()
     names = header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), f"libmoe.so does not export {n}"
     assert set(names) == set(M._SIGS), "binding signatures out of sync with the header"
@@ -77,6 +78,35 @@ def test_workspace_queries():
     assert L.moe_layer_workspace_bytes(ctypes.byref(c), 1 << 30) == M.SIZE_MAX
     assert L.moe_grouped_ffn_workspace_bytes(ctypes.byref(c), 0, 10, 128) == M.SIZE_MAX
     assert L.moe_grouped_ffn_workspace_bytes(ctypes.byref(c), 4, 10, 0) == M.SIZE_MAX
+
+
+def test_packed_weights_queries_and_checks():
+    L = moe.lib()
+    # n_mats * ceil(rows/16)*16 * cols * 2 bytes
+    assert L.moe_packed_weights_bytes(1, 288, 4096) == 288 * 4096 * 2
+    assert L.moe_packed_weights_bytes(3, 12, 64) == 3 * 16 * 64 * 2
+    assert L.moe_packed_weights_bytes(0, 12, 64) == 0
+    assert L.moe_packed_weights_bytes(1, 16, 48) == M.SIZE_MAX      # cols % 32 != 0
+    assert L.moe_packed_weights_bytes(-1, 16, 64) == M.SIZE_MAX
+    need = L.moe_packed_weights_bytes(2, 20, 64)
+    call = lambda n=2, r=20, c=64, src=FAKE, dst=FAKE, nb=need: L.moe_pack_weights(n, r, c, src, dst, nb, None)
+    assert call(c=40) == SHAPE
+    assert call(n=0) == OK                      # nothing to pack
+    assert call(src=None) == NULL
+    assert call(dst=FAKE + 8) == MISALIGNED
+    assert call(nb=need - 1) == WS and str(need) in _last()
+    # packed layout needs bf16 and widths multiple of 64
+    for bad in (cfg(weight_layout=2), cfg(weight_layout=moe.LAYOUT_PACKED, dtype=moe.F32),
+                cfg(weight_layout=moe.LAYOUT_PACKED, d_model=320 - 32), cfg(weight_layout=moe.LAYOUT_PACKED, d_expert=96)):
+        assert L.moe_layer_workspace_bytes(ctypes.byref(bad), 10) == M.SIZE_MAX
+    good = cfg(weight_layout=moe.LAYOUT_PACKED)
+    assert L.moe_layer_workspace_bytes(ctypes.byref(good), 10) != M.SIZE_MAX
+    ws = L.moe_grouped_ffn_workspace_bytes(ctypes.byref(good), 4, 64, 96)
+    assert L.moe_grouped_ffn(ctypes.byref(good), 4, 64, FAKE, FAKE, 64, None, FAKE, FAKE, FAKE, 96, FAKE, FAKE, ws,
+                             None) == UNSUP and "64" in _last()
+    assert moe.Config(256, 16, 4, 128, 128, packed=True).wshape(16, 256) == (16, 256)
+    assert moe.Config(256, 12, 4, 128, 128, packed=True).wshape(12, 256) == (16, 256)
+    assert moe.Config(256, 12, 4, 128, 128).wshape(12, 256) == (12, 256)
 
 
 def _last():

@@ -2,12 +2,13 @@
 
 The compute path is libmoe.so: hand-written HIP kernels for gfx950 behind
 the C ABI of include/moe.h (moe_route, moe_permute, moe_expert_gate_up,
-moe_expert_down, moe_grouped_ffn, moe_combine, moe_layer_forward). This package is its Python binding.
+moe_expert_down, moe_grouped_ffn, moe_combine, moe_layer_forward, moe_pack_weights). This package is its Python binding.
 """
-from .moe import (BF16, F32, Config, MoeError, Workspace, combine, expert_down, expert_gate_up,  # noqa: F401
-                  grouped_ffn, layer_forward, lib, permute, route, status_string, weights_struct)
+from .moe import (BF16, F32, LAYOUT_PACKED, LAYOUT_ROWS, Config, MoeError, Workspace, combine,  # noqa: F401
+                  expert_down, expert_gate_up, grouped_ffn, layer_forward, lib, pack_layer, pack_weights,
+                  packed_weights_bytes, permute, route, status_string, weights_struct)
 
 
-def config_for(spec) -> Config:
+def config_for(spec, packed: bool = False) -> Config:
     """Config of a layer workload description with fields D, E, K, F, Fs and torch_dtype."""
-    return Config(spec.D, spec.E, spec.K, spec.F, spec.Fs, spec.torch_dtype, spec.out_dtype)
+    return Config(spec.D, spec.E, spec.K, spec.F, spec.Fs, spec.torch_dtype, spec.out_dtype, packed)

@@ -78,8 +78,15 @@ moe_status check_cfg(const moe_config* c) {
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "dtype %d", c->dtype);
   if (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "out_dtype %d", c->out_dtype);
+  if (c->weight_layout != MOE_LAYOUT_ROWS && c->weight_layout != MOE_LAYOUT_PACKED)
+    return fail(MOE_ERR_UNSUPPORTED, "weight_layout %d", c->weight_layout);
+  if (c->weight_layout == MOE_LAYOUT_PACKED &&
+      (c->dtype != MOE_BF16 || c->d_model % 64 || c->d_expert % 64 || c->d_shared % 64))
+    return fail(MOE_ERR_UNSUPPORTED, "packed weights need bf16 and d_model, d_expert, d_shared multiples of 64");
   return MOE_OK;
 }
+
+bool packed(const moe_config* c) { return c->weight_layout == MOE_LAYOUT_PACKED; }
 
 moe_status check_tokens(const moe_config* c, int64_t T) {
   if (T < 0) return fail(MOE_ERR_SHAPE, "T = %lld < 0", (long long)T);
@@ -194,6 +201,7 @@ moe_status run_route(const moe_config* c, int64_t T, const void* x, const void* 
   g.out = ws.logits;
   g.ldo = c->n_experts;
   g.bias = bias;
+  g.b_packed = packed(c);
   g.ksplit = route_ksplit(c, T);
   g.slice_stride = T * c->n_experts;
   MOE_TRY_HIP(launch_grouped_gemm(c->dtype, EPI_F32, BM, g, s), "router linear layer");
@@ -238,6 +246,7 @@ moe_status run_gate_up(const moe_config* c, const SchedWs& ws, bool build, int n
   g.Kdim = c->d_model;
   g.out = h;
   g.ldo = d_ff;
+  g.b_packed = packed(c);
   MOE_TRY_HIP(launch_grouped_gemm(c->dtype, EPI_SWIGLU, ws.block_rows, g, s), "expert gate/up projection");
   return MOE_OK;
 }
@@ -257,6 +266,7 @@ moe_status run_down(const moe_config* c, const SchedWs& ws, bool build, int n_gr
   g.Kdim = d_ff;
   g.out = y;
   g.ldo = c->d_model;
+  g.b_packed = packed(c);
   MOE_TRY_HIP(launch_grouped_gemm(c->dtype, EPI_F32, ws.block_rows, g, s), "expert down projection");
   return MOE_OK;
 }
@@ -265,9 +275,9 @@ moe_status run_down(const moe_config* c, const SchedWs& ws, bool build, int n_gr
 moe_status run_ffn(const moe_config* c, int n_groups, int n_main, int64_t n_rows, const int32_t* offsets,
                    const void* x, int64_t n_x_rows, const int32_t* gather, int64_t n_gather, const void* w_gate,
                    const void* w_up, const void* w_down, const void* s_gate, const void* s_up, const void* s_down,
-                   int d_ff, float* y, const FfnWs& ws, hipStream_t s) {
-  MOE_TRY(run_gate_up(c, ws.sched, true, n_groups, n_main, n_rows, offsets, x, n_x_rows, gather, n_gather, w_gate,
-                      w_up, s_gate, s_up, d_ff, ws.h, s));
+                   int d_ff, float* y, const FfnWs& ws, hipStream_t s, bool tiles_ready = false) {
+  MOE_TRY(run_gate_up(c, ws.sched, !tiles_ready, n_groups, n_main, n_rows, offsets, x, n_x_rows, gather, n_gather,
+                      w_gate, w_up, s_gate, s_up, d_ff, ws.h, s));
   MOE_TRY(run_down(c, ws.sched, false, n_groups, n_main, n_rows, offsets, ws.h, w_down, s_down, d_ff, y, s));
   return MOE_OK;
 }
@@ -280,6 +290,7 @@ moe_status check_grouped(const moe_config* cfg, int32_t n_groups, int64_t n_rows
     return fail(MOE_ERR_SHAPE, "n_rows must be in [0, 2^31) and d_ff > 0");
   if (cfg->dtype == MOE_BF16 && (cfg->d_model % 8 || d_ff % 8))
     return fail(MOE_ERR_UNSUPPORTED, "bf16 rows need d_model and d_ff multiples of 8");
+  if (packed(cfg) && d_ff % 64) return fail(MOE_ERR_UNSUPPORTED, "packed weights need d_ff %% 64 == 0");
   return MOE_OK;
 }
 
@@ -301,6 +312,23 @@ const char* moe_status_string(moe_status s) {
 }
 
 const char* moe_last_error(void) { return g_last_error; }
+
+size_t moe_packed_weights_bytes(int64_t n_mats, int64_t rows, int64_t cols) {
+  if (n_mats < 0 || rows < 0 || cols < 0 || cols % 32) return SIZE_MAX;
+  return (size_t)n_mats * (size_t)((rows + 15) / 16 * 16) * (size_t)cols * 2u;
+}
+
+moe_status moe_pack_weights(int64_t n_mats, int64_t rows, int64_t cols, const void* src, void* dst,
+                            size_t dst_bytes, void* stream) {
+  const size_t need = moe_packed_weights_bytes(n_mats, rows, cols);
+  if (need == SIZE_MAX) return fail(MOE_ERR_SHAPE, "pack: sizes must be >= 0 and cols a multiple of 32");
+  if (need == 0) return ok();
+  if (!src || !dst) return fail(MOE_ERR_NULL, "pack: src and dst are required");
+  if (misaligned(src) || misaligned(dst)) return fail(MOE_ERR_MISALIGNED, "pack: src and dst must be 16-byte aligned");
+  if (dst_bytes < need) return fail(MOE_ERR_WORKSPACE, "pack: dst has %zu bytes, %zu needed", dst_bytes, need);
+  MOE_TRY_HIP(launch_pack((const bf16_t*)src, n_mats, rows, cols, (bf16_t*)dst, (hipStream_t)stream), "pack weights");
+  return ok();
+}
 
 size_t moe_route_workspace_bytes(const moe_config* cfg, int64_t T) {
   if (check_cfg(cfg) != MOE_OK || check_tokens(cfg, T) != MOE_OK) return SIZE_MAX;
@@ -506,15 +534,25 @@ moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x, co
 
   // 1. router: linear layer + softmax over all E experts + top-K
   MOE_TRY(run_route(cfg, T, x, w->w_router, w->router_bias, idx, prob, nullptr, L.route, s));
-  // 2. permute pairs into expert segments; the shared expert's T rows follow them
-  MOE_TRY_HIP(launch_permute(idx, T, K, E, L.perm.rank, L.perm.counts, offsets_out, L.sorted_token, L.dest,
-                             L.offsets_ext, L.fused_shared ? (int32_t)T : 0, s),
-              "permute");
+  // 2. permute pairs into expert segments; the shared expert's T rows follow
+  //    them. Small batches do it, and the expert-GEMM tile table, in one block.
+  const int32_t extra = L.fused_shared ? (int32_t)T : 0;
+  const bool small = permute_small_fits(T, K, E);
+  if (small) {
+    MOE_TRY_HIP(launch_permute_small(idx, T, K, E, offsets_out, L.sorted_token, L.dest, L.offsets_ext, extra,
+                                     L.ffn.sched.tiles, L.ffn.sched.n_tiles, L.ffn.sched.max_tiles,
+                                     L.ffn.sched.block_rows, s),
+                "permute");
+  } else {
+    MOE_TRY_HIP(launch_permute(idx, T, K, E, L.perm.rank, L.perm.counts, offsets_out, L.sorted_token, L.dest,
+                               L.offsets_ext, extra, s),
+                "permute");
+  }
   // 3. expert FFNs: routed segments (rows gathered through sorted_token) and,
   //    when widths match, the shared expert as one more group over x itself
   const int n_groups = E + (L.fused_shared ? 1 : 0);
-  MOE_TRY(run_ffn(cfg, n_groups, E, P + (L.fused_shared ? T : 0), L.offsets_ext, x, T, L.sorted_token, P, w->w_gate,
-                  w->w_up, w->w_down, w->s_gate, w->s_up, w->s_down, cfg->d_expert, L.y, L.ffn, s));
+  MOE_TRY(run_ffn(cfg, n_groups, E, P + extra, L.offsets_ext, x, T, L.sorted_token, P, w->w_gate, w->w_up,
+                  w->w_down, w->s_gate, w->s_up, w->s_down, cfg->d_expert, L.y, L.ffn, s, small));
   if (shared && !L.fused_shared) {
     MOE_TRY(run_ffn(cfg, 1, 1, T, nullptr, x, T, nullptr, 0, w->s_gate, w->s_up, w->s_down, nullptr, nullptr,
                     nullptr, cfg->d_shared, L.y_shared, L.ffn_shared, s));

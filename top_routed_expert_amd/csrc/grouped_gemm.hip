@@ -27,7 +27,7 @@
 #define MOE_GU_NW_SMALL 1  // 16-column tiles per wave (gate and up each), 32-row tiles
 #endif
 #ifndef MOE_DN_NW_SMALL
-#define MOE_DN_NW_SMALL 2  // 16-column tiles per wave, down projection, 32-row tiles
+#define MOE_DN_NW_SMALL 1  // 16-column tiles per wave, down projection, 32-row tiles
 #endif
 #ifndef MOE_NS_LARGE
 #define MOE_NS_LARGE 4  // pipeline depth of the 128-row tiles
@@ -91,11 +91,11 @@ __device__ __forceinline__ int lds_off(int r, int c) { return r * KS + ((c ^ (r 
 
 // EPI: epilogue; MT: 16-row MFMA tiles per block; NW: 16-column weight tiles
 // per wave and operand; KSTEPS: 32-element MFMA steps per pipeline stage;
-// NS: pipeline depth. Loads of stage k+NS-1 are issued before stage k is
+// NS: pipeline depth; PK: weights in the packed fragment layout (below). Loads of stage k+NS-1 are issued before stage k is
 // multiplied, so NS-1 stages of weights (and A rows) are in flight per wave
 // while the matrix cores work; the ring lives in VGPRs and the loop is
 // unrolled by NS so every ring slot is a fixed register range.
-template <int EPI, int MT, int NW, int KSTEPS, int NS>
+template <int EPI, int MT, int NW, int KSTEPS, int NS, bool PK>
 __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
   constexpr int KS = 32 * KSTEPS;                       // contraction elements per stage
   constexpr int CPR = KS / 8;                           // 16-byte chunks per staged row
@@ -150,12 +150,23 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
   const int wcol0 = nb * BN + wave * NW * 16;
   const bf16_t* bg = group_b<bf16_t>(p, p.b0, p.b0_extra, t.group);
   const bf16_t* bu = EPI == EPI_SWIGLU ? group_b<bf16_t>(p, p.b1, p.b1_extra, t.group) : bg;
+  // Packed weights: the operand of a whole wave for one 16-column tile and
+  // one MFMA step is one contiguous 1 KB fragment, lane l at l*16 bytes
+  // (packed_offset); the tiles past the last one are clamped to it.
   const bf16_t* bptr[NBT];
 #pragma unroll
   for (int j = 0; j < NBT; ++j) {
-    int col = wcol0 + (j % NW) * 16 + (lane & 15);
-    col = col < p.N ? col : p.N - 1;
-    bptr[j] = (j < NW ? bg : bu) + (int64_t)col * Kdim + (int64_t)kbase * KS + (lane >> 4) * 8;
+    const bf16_t* base = j < NW ? bg : bu;
+    if constexpr (PK) {
+      int ct = (wcol0 + (j % NW) * 16) >> 4;
+      const int ct_last = (p.N + 15) / 16 - 1;
+      ct = ct < ct_last ? ct : ct_last;
+      bptr[j] = base + packed_offset(ct, kbase * KSTEPS, lane, Kdim);
+    } else {
+      int col = wcol0 + (j % NW) * 16 + (lane & 15);
+      col = col < p.N ? col : p.N - 1;
+      bptr[j] = base + (int64_t)col * Kdim + (int64_t)kbase * KS + (lane >> 4) * 8;
+    }
   }
 
   uint4 ra[NS][NA];
@@ -170,7 +181,8 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < NBT; ++j)
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) b[j][s] = *(const uint4*)(bptr[j] + ks * KS + s * 32);
+      for (int s = 0; s < KSTEPS; ++s)
+        b[j][s] = *(const uint4*)(bptr[j] + (PK ? (ks * KSTEPS + s) * PACKED_FRAG : ks * KS + s * 32));
 #pragma unroll
     for (int i = 0; i < NA; ++i) a[i] = *(const uint4*)(arow[i] + ks * KS);
   };
@@ -395,13 +407,16 @@ template <int EPI, int MT, int NW, int NS, int KSTEPS = 2>
 static hipError_t launch_fast(const GemmArgs& g, hipStream_t s) {
   const int n_nb = (g.N + 4 * NW * 16 - 1) / (4 * NW * 16);
   const int64_t blocks = ((int64_t)g.max_tiles * n_nb + 7) / 8 * 8;
-  gemm_bf16_mfma<EPI, MT, NW, KSTEPS, NS><<<dim3((unsigned)blocks, (unsigned)g.ksplit), 256, 0, s>>>(g);
+  const dim3 grid((unsigned)blocks, (unsigned)g.ksplit);
+  if (g.b_packed) gemm_bf16_mfma<EPI, MT, NW, KSTEPS, NS, true><<<grid, 256, 0, s>>>(g);
+  else gemm_bf16_mfma<EPI, MT, NW, KSTEPS, NS, false><<<grid, 256, 0, s>>>(g);
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm(int dtype, int epi, int block_rows, const GemmArgs& g, hipStream_t s) {
   if (g.max_tiles <= 0 || g.N <= 0) return hipSuccess;
   if (block_rows == 64) {
+    if (g.b_packed) return hipErrorInvalidValue;  // packed weights exist only on the bf16 MFMA path
     const int n_nb = (g.N + 63) / 64;
     const unsigned blocks = (unsigned)((int64_t)g.max_tiles * n_nb);
     if (dtype == MOE_BF16) {

@@ -25,7 +25,9 @@
 //
 // LDS rows are 64 bytes (four 16-byte chunks); chunk q of row r is stored
 // at position q ^ ((r >> 1) & 3), so the 16-byte MFMA operand reads of
-// consecutive rows spread over all banks.
+// consecutive rows spread over all banks. With packed weights (PK) each
+// 16-row group of B is one 1 KB fragment copied as it is (lane order), which
+// the operand reads take at 16 bytes per lane, conflict-free.
 #include "moe_internal.h"
 
 namespace moe {
@@ -51,7 +53,7 @@ constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
 
-template <int EPI>
+template <int EPI, bool PK>
 __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[BIG_NS][2][BIG_ROWS * BIG_KS];
 
@@ -111,8 +113,16 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
       col = nb * BN + row;
       base = Bg;
     }
-    col = col < p.N ? col : p.N - 1;
-    bsrc[i] = base + (int64_t)col * Kdim + q * 8;
+    if constexpr (PK) {
+      // the 16 rows of this instruction are one fragment column tile
+      int ct = (col - (row & 15)) >> 4;
+      const int ct_last = (p.N + 15) / 16 - 1;
+      ct = ct < ct_last ? ct : ct_last;
+      bsrc[i] = base + packed_offset(ct, 0, lane, Kdim);
+    } else {
+      col = col < p.N ? col : p.N - 1;
+      bsrc[i] = base + (int64_t)col * Kdim + q * 8;
+    }
   }
 
   auto issue_stage = [&](int slot, int ks) {
@@ -121,7 +131,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + koff),
                                        (lds_void_t*)&lds[slot][0][(wave * 64 + i * 16) * BIG_KS], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + koff),
+      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + (PK ? ks * PACKED_FRAG : koff)),
                                        (lds_void_t*)&lds[slot][1][(wave * 64 + i * 16) * BIG_KS], 16, 0, 0);
     }
   };
@@ -147,7 +157,8 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     const int row = wn * 128 + n * 16 + rr;
-    boff[n] = (uint32_t)(BIG_ROWS * BIG_KS + row * BIG_KS + ((rq ^ swz(row)) << 3)) * 2u;
+    boff[n] = PK ? (uint32_t)(BIG_ROWS * BIG_KS + (wn * 128 + n * 16) * BIG_KS) * 2u + (uint32_t)lane * 16u
+                 : (uint32_t)(BIG_ROWS * BIG_KS + row * BIG_KS + ((rq ^ swz(row)) << 3)) * 2u;
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)&lds[0][0][0];
   constexpr uint32_t SLOT_BYTES = 2u * BIG_ROWS * BIG_KS * 2u;
@@ -241,8 +252,13 @@ hipError_t launch_grouped_gemm_big(int epi, const GemmArgs& g, hipStream_t s) {
   const int BN = epi == EPI_SWIGLU ? BIG_ROWS / 2 : BIG_ROWS;
   const int n_nb = (g.N + BN - 1) / BN;
   const int64_t blocks = ((int64_t)g.max_tiles * n_nb + 7) / 8 * 8;
-  if (epi == EPI_SWIGLU) gemm_bf16_big<EPI_SWIGLU><<<(unsigned)blocks, 256, 0, s>>>(g);
-  else gemm_bf16_big<EPI_F32><<<(unsigned)blocks, 256, 0, s>>>(g);
+  if (g.b_packed) {
+    if (epi == EPI_SWIGLU) gemm_bf16_big<EPI_SWIGLU, true><<<(unsigned)blocks, 256, 0, s>>>(g);
+    else gemm_bf16_big<EPI_F32, true><<<(unsigned)blocks, 256, 0, s>>>(g);
+  } else {
+    if (epi == EPI_SWIGLU) gemm_bf16_big<EPI_SWIGLU, false><<<(unsigned)blocks, 256, 0, s>>>(g);
+    else gemm_bf16_big<EPI_F32, false><<<(unsigned)blocks, 256, 0, s>>>(g);
+  }
   return hipGetLastError();
 }
 

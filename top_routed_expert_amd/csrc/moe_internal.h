@@ -35,6 +35,17 @@ struct Tile {
   int32_t group, row0, row1, pad;
 };
 
+// Packed fragment layout of a bf16 weight matrix W [N, K] (K % 32 == 0):
+// W is cut into 16-row x 32-column fragments, fragment (ct, kb) covering rows
+// 16ct.. and columns 32kb.. . Each fragment is 1 KB stored in MFMA operand
+// order: lane l = c + 16q (c < 16, q < 4) holds W[16ct + c][32kb + 8q .. +8]
+// at byte 16l. Fragments are stored kb-fastest; rows past N are zero.
+// Element offset of lane l's 8 values of fragment (ct, kb):
+constexpr int PACKED_FRAG = 512;  // bf16 elements per fragment
+__host__ __device__ __forceinline__ int64_t packed_offset(int64_t ct, int64_t kb, int lane, int64_t K) {
+  return (ct * (K / 32) + kb) * PACKED_FRAG + lane * 8;
+}
+
 // Epilogues of the grouped GEMM.
 enum GemmEpilogue {
   EPI_SWIGLU = 0,  // two B operands (gate, up): out = dtype(silu(A Bg^T) * (A Bu^T))
@@ -62,6 +73,7 @@ struct GemmArgs {
   int32_t max_tiles;      // host-side upper bound of the tile count (grid size)
   void* out;              // [rows, ldo]
   int64_t ldo;
+  int32_t b_packed;       // B operands in the packed fragment layout (bf16 MFMA kernels only)
   const float* bias;      // EPI_F32: per-column bias or NULL
   int32_t ksplit;         // EPI_F32 only: the contraction is cut into ksplit slices;
   int64_t slice_stride;   //   slice s writes its partial sums to out + s*slice_stride
@@ -90,8 +102,19 @@ hipError_t launch_topk(const float* logits, int nsplit, int64_t T, int E, int K,
 hipError_t launch_permute(const int32_t* idx, int64_t T, int K, int E, int32_t* rank, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_token, int32_t* dest,
                           int32_t* offsets_ext, int32_t extra_rows, hipStream_t s);
+bool permute_small_fits(int64_t T, int K, int E);
+// Single-block permutation for small batches; also writes the tile table of
+// the expert GEMMs over E (+1 if extra_rows) groups when tiles != NULL.
+hipError_t launch_permute_small(const int32_t* idx, int64_t T, int K, int E, int32_t* offsets, int32_t* sorted_token,
+                                int32_t* dest, int32_t* offsets_ext, int32_t extra_rows, Tile* tiles,
+                                int32_t* n_tiles, int32_t max_tiles, int block_rows, hipStream_t s);
 hipError_t launch_gather_rows(const void* x, int64_t T, int D, int elem_bytes, const int32_t* sorted_token,
                               int64_t rows, void* x_perm, hipStream_t s);
+
+// pack.hip: n_mats row-major [rows, cols] bf16 matrices -> packed fragment
+// layout (rows rounded up to a multiple of 16, zero-filled), matrix after
+// matrix.
+hipError_t launch_pack(const bf16_t* src, int64_t n_mats, int64_t rows, int64_t cols, bf16_t* dst, hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(int out_dtype, int64_t T, int D, int K, const float* y_perm, int64_t n_perm_rows,

@@ -11,6 +11,8 @@
 //     pair its rank; the total is the expert's count. No atomics.
 //  2. place: every block rebuilds the exclusive scan of the E counts in LDS,
 //     then maps each pair to dest and writes sorted_token[dest] = t.
+// Small batches take a single-block path that also builds the tile table of
+// the expert GEMMs (one launch instead of three).
 #include "moe_internal.h"
 
 namespace moe {
@@ -141,7 +143,97 @@ __global__ void __launch_bounds__(256) gather_rows_bytes_kernel(const uint8_t* _
   for (int i = threadIdx.x; i < row_bytes; i += 256) x_perm[r * row_bytes + i] = x[t * row_bytes + i];
 }
 
+// Small batches (T*K <= 1024, E <= 1024): the whole permutation and the
+// expert-GEMM tile table in one block of 1024 threads. Counts come from LDS
+// atomics (order-independent); each pair's rank among the earlier pairs of
+// its expert is counted directly over the pairs before it, so the result is
+// the same stable permutation as the two-kernel path.
+__global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __restrict__ idx, int P, int K, int E,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ sorted_token,
+                                                             int32_t* __restrict__ dest,
+                                                             int32_t* __restrict__ offsets_ext, int32_t extra_rows,
+                                                             Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+                                                             int32_t max_tiles, int BM) {
+  __shared__ int s_idx[1024];
+  __shared__ int s_cnt[1025];
+  __shared__ int s_scan[1024];
+  const int tid = threadIdx.x;
+  const int e_mine = tid < P ? idx[tid] : -1;
+  s_idx[tid] = e_mine;
+  s_cnt[tid] = 0;
+  __syncthreads();
+  const bool valid = e_mine >= 0 && e_mine < E;
+  if (valid) atomicAdd(&s_cnt[e_mine], 1);
+  __syncthreads();
+  // exclusive scan of the counts (expert tid)
+  const int c = tid < E ? s_cnt[tid] : 0;
+  s_scan[tid] = c;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += v;
+    __syncthreads();
+  }
+  const int off_mine = s_scan[tid] - c;  // offset of expert tid
+  const int total = s_scan[1023];
+  __syncthreads();
+  if (tid < E) s_cnt[tid] = off_mine;  // s_cnt now holds offsets
+  if (tid == 0) s_cnt[E] = total;
+  __syncthreads();
+  if (tid <= E) {
+    if (offsets) offsets[tid] = s_cnt[tid];
+    if (offsets_ext) offsets_ext[tid] = s_cnt[tid];
+  }
+  if (tid == 0 && offsets_ext) offsets_ext[E + 1] = total + extra_rows;
+  // stable rank: earlier pairs routed to the same expert
+  if (tid < P) {
+    if (valid) {
+      int r = 0;
+      for (int j = 0; j < tid; ++j) r += s_idx[j] == e_mine;
+      const int d = s_cnt[e_mine] + r;
+      dest[tid] = d;
+      sorted_token[d] = tid / K;
+    } else {
+      dest[tid] = -1;
+    }
+  }
+  if (tiles == nullptr) return;
+  // tile table over the E routed groups and, with extra_rows, the shared group
+  const int n_groups = E + (extra_rows > 0 ? 1 : 0);
+  int seg0 = 0, seg1 = 0;
+  if (tid < n_groups) {
+    seg0 = tid < E ? s_cnt[tid] : total;
+    seg1 = tid < E ? s_cnt[tid + 1] : total + extra_rows;
+  }
+  const int mine = (seg1 - seg0 + BM - 1) / BM;
+  __syncthreads();
+  s_scan[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += v;
+    __syncthreads();
+  }
+  int slot = s_scan[tid] - mine;
+  for (int r = seg0; r < seg1; r += BM, ++slot)
+    if (slot < max_tiles) tiles[slot] = Tile{tid, r, r + BM < seg1 ? r + BM : seg1, 0};
+  if (tid == 1023) *n_tiles = s_scan[1023] < max_tiles ? s_scan[1023] : max_tiles;
+}
+
 }  // namespace
+
+bool permute_small_fits(int64_t T, int K, int E) { return T * K <= 1024 && E <= 1023; }
+
+hipError_t launch_permute_small(const int32_t* idx, int64_t T, int K, int E, int32_t* offsets, int32_t* sorted_token,
+                                int32_t* dest, int32_t* offsets_ext, int32_t extra_rows, Tile* tiles,
+                                int32_t* n_tiles, int32_t max_tiles, int block_rows, hipStream_t s) {
+  permute_small_kernel<<<1, 1024, 0, s>>>(idx, (int)(T * K), K, E, offsets, sorted_token, dest, offsets_ext,
+                                          extra_rows, tiles, n_tiles, max_tiles, block_rows);
+  return hipGetLastError();
+}
 
 hipError_t launch_permute(const int32_t* idx, int64_t T, int K, int E, int32_t* rank, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_token, int32_t* dest, int32_t* offsets_ext,

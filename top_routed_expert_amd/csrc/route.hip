@@ -16,25 +16,56 @@ namespace moe {
 
 namespace {
 
+// Wave-wide reductions with DPP lane moves (no LDS round trips): pairs in a
+// quad, then half-row and row mirrors give every lane of a 16-lane row the
+// row's result; row_bcast:15 / row_bcast:31 fold rows 0-1 and 2-3 so lane 63
+// ends with the wave's result, which readlane broadcasts.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, dpp32<0xb1, 0xf>(v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp32<0x4e, 0xf>(v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp32<0x141, 0xf>(v));  // row_half_mirror
+  v = op(v, dpp32<0x140, 0xf>(v));  // row_mirror
+  v = op(v, dpp32<0x142, 0xa>(v));  // row_bcast:15 into rows 1 and 3
+  v = op(v, dpp32<0x143, 0xc>(v));  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
 }
 
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ unsigned long long dpp64(unsigned long long v) {
+  const uint32_t lo = dpp32<CTRL, ROW_MASK>((uint32_t)v), hi = dpp32<CTRL, ROW_MASK>((uint32_t)(v >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+__device__ __forceinline__ unsigned long long max64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
+
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned long long w = __shfl_xor(v, o, 64);
-    v = w > v ? w : v;
-  }
-  return v;
+  v = max64(v, dpp64<0xb1, 0xf>(v));
+  v = max64(v, dpp64<0x4e, 0xf>(v));
+  v = max64(v, dpp64<0x141, 0xf>(v));
+  v = max64(v, dpp64<0x140, 0xf>(v));
+  v = max64(v, dpp64<0x142, 0xa>(v));
+  v = max64(v, dpp64<0x143, 0xc>(v));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((unsigned long long)hi << 32) | lo;
 }
 
 // Sum of nsplit partial logit arrays for one token, one block (4 waves) per

@@ -19,6 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 F32, BF16 = 0, 1
+LAYOUT_ROWS, LAYOUT_PACKED = 0, 1
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 _TORCH = {F32: torch.float32, BF16: torch.bfloat16}
 SIZE_MAX = ctypes.c_size_t(-1).value
@@ -33,7 +34,7 @@ class MoeError(RuntimeError):
 class MoeConfig(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("d_expert", ctypes.c_int32), ("d_shared", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -60,6 +61,8 @@ _SIGS = {
     "moe_expert_down": ([_CFG, _I32, _I64, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P], ctypes.c_int),
     "moe_combine": ([_CFG, _I64, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_layer_forward": ([_CFG, _I64, _P, ctypes.POINTER(MoeWeights), _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "moe_packed_weights_bytes": ([_I64, _I64, _I64], _SZ),
+    "moe_pack_weights": ([_I64, _I64, _I64, _P, _P, _SZ, _P], ctypes.c_int),
 }
 
 
@@ -96,11 +99,18 @@ class Config:
     d_shared: int
     dtype: torch.dtype = torch.bfloat16
     out_dtype: torch.dtype | None = None
+    packed: bool = False  # weight matrices in the packed fragment layout (pack_weights)
 
     def c(self) -> MoeConfig:
         out = self.out_dtype if self.out_dtype is not None else self.dtype
         return MoeConfig(self.d_model, self.n_experts, self.top_k, self.d_expert, self.d_shared,
-                         _DT[self.dtype], _DT[out])
+                         _DT[self.dtype], _DT[out], LAYOUT_PACKED if self.packed else LAYOUT_ROWS)
+
+    def wshape(self, *shape: int) -> tuple:
+        """Shape of a weight tensor whose row-major shape is `shape` (rows rounded up to 16 when packed)."""
+        if not self.packed:
+            return tuple(shape)
+        return (*shape[:-2], (shape[-2] + 15) // 16 * 16, shape[-1])
 
     @property
     def odtype(self) -> torch.dtype:
@@ -148,7 +158,7 @@ def route(cfg: Config, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tens
     gap = torch.empty((T,), dtype=torch.float32, device=dev) if want_gap else None
     ws = _workspace(lib().moe_route_workspace_bytes(ctypes.byref(c), T), dev)
     _check(lib().moe_route(ctypes.byref(c), T, _ptr(x, "x", cfg.dtype, (T, cfg.d_model)),
-                           _ptr(w_router, "w_router", cfg.dtype, (cfg.n_experts, cfg.d_model), dev),
+                           _ptr(w_router, "w_router", cfg.dtype, cfg.wshape(cfg.n_experts, cfg.d_model), dev),
                            _ptr(bias, "bias", torch.float32, (cfg.n_experts,), dev),
                            _ptr(idx, "idx"), _ptr(prob, "prob"), _ptr(gap, "gap"),
                            ws.data_ptr(), ws.numel(), _stream(dev)), "moe_route")
@@ -271,7 +281,7 @@ def weights_struct(cfg: Config, w: dict) -> MoeWeights:
     E, D, F, Fs = cfg.n_experts, cfg.d_model, cfg.d_expert, cfg.d_shared
     dev = w["w_router"].device
     s = MoeWeights()
-    s.w_router = _ptr(w["w_router"], "w_router", cfg.dtype, (E, D), dev)
+    s.w_router = _ptr(w["w_router"], "w_router", cfg.dtype, cfg.wshape(E, D), dev)
     s.router_bias = _ptr(w.get("bias"), "bias", torch.float32, (E,), dev)
     s.w_gate = _ptr(w["w_gate"], "w_gate", cfg.dtype, (E, F, D), dev)
     s.w_up = _ptr(w["w_up"], "w_up", cfg.dtype, (E, F, D), dev)
@@ -313,3 +323,32 @@ def layer_forward(cfg: Config, x: torch.Tensor, w: dict, out: torch.Tensor | Non
                                    _ptr(idx, "idx"), _ptr(prob, "prob"), _ptr(offs, "offsets"),
                                    ws.data_ptr(), ws.numel(), _stream(dev)), "moe_layer_forward")
     return (out, idx, prob, offs) if routing else out
+
+
+def packed_weights_bytes(n_mats: int, rows: int, cols: int) -> int:
+    """moe_packed_weights_bytes: bytes of n_mats packed [rows, cols] bf16 matrices."""
+    return lib().moe_packed_weights_bytes(n_mats, rows, cols)
+
+
+def pack_weights(w: torch.Tensor) -> torch.Tensor:
+    """moe_pack_weights: a bf16 [rows, cols] or [n, rows, cols] device tensor in the packed fragment
+    layout, returned as a tensor of shape [..., ceil(rows/16)*16, cols] (its bytes are the packed form)."""
+    if w.dim() not in (2, 3):
+        raise ValueError("pack_weights takes a [rows, cols] or [n, rows, cols] tensor")
+    n = w.shape[0] if w.dim() == 3 else 1
+    rows, cols = w.shape[-2], w.shape[-1]
+    nbytes = packed_weights_bytes(n, rows, cols)
+    if nbytes == SIZE_MAX:
+        raise ValueError(f"cannot pack [{rows}, {cols}]: cols must be a multiple of 32")
+    out = torch.empty((*w.shape[:-2], (rows + 15) // 16 * 16, cols), dtype=torch.bfloat16, device=w.device)
+    _check(lib().moe_pack_weights(n, rows, cols, _ptr(w, "w", torch.bfloat16), _ptr(out, "out"),
+                                  out.numel() * 2, _stream(w.device)), "moe_pack_weights")
+    return out
+
+
+_WEIGHT_KEYS = ("w_router", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")
+
+
+def pack_layer(w: dict) -> dict:
+    """A copy of a layer's weight dict with every weight matrix packed (for a Config with packed=True)."""
+    return {k: (pack_weights(v) if k in _WEIGHT_KEYS and v is not None else v) for k, v in w.items()}
