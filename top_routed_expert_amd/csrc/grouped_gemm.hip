@@ -73,16 +73,6 @@ __device__ __forceinline__ const T* group_b(const GemmArgs& p, const void* main,
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// f(std::integral_constant<int, I>{}) for I = B .. E-1: indices into register
-// arrays are constant expressions, so the arrays never need memory.
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
 // LDS offset (in bf16 elements) of 16-byte chunk `c` of staged row `r` (row
 // length KS): chunks are XOR-swizzled by (r & 7) so the 16-byte operand reads
 // of 8 consecutive rows hit distinct banks.

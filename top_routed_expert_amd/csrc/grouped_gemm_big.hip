@@ -14,12 +14,14 @@
 // sums of the same 64 columns and applies the SwiGLU in registers.
 //
 // Both operands go HBM/L2 -> LDS through direct loads (global_load_lds,
-// 16 bytes per lane, no VGPR staging) into a ring of NS = 4 stages of one
-// 32-element MFMA step each (16 KB of A + 16 KB of B per stage, 128 KB in
-// all). Waits are explicit: a wave waits for its own loads of stage k with
-// s_waitcnt vmcnt (loads complete in issue order; two younger stages stay
-// in flight), then one s_barrier makes every wave's stage-k loads visible
-// and ends every wave's reads of the slot about to be refilled. The
+// 16 bytes per lane, no VGPR staging) into a ring of NS = 5 stages of one
+// 32-element MFMA step each (16 KB of A + 16 KB of B per stage, all 160 KB
+// of LDS). The B operand of a stage is read from LDS into registers one
+// stage ahead (two register sets) and the A operand row tile by row tile in
+// the stage itself, so the LDS reads overlap the matrix-core work. Waits are explicit: a wave waits for its
+// own loads of a stage with s_waitcnt vmcnt (loads complete in issue order),
+// then one s_barrier per stage makes every wave's loads of that stage
+// visible and ends every wave's reads of the slot about to be refilled. The
 // barrier is issued as inline asm with a memory clobber: the compiler may
 // not move memory accesses across it and does not add a drain of its own.
 //
@@ -35,7 +37,7 @@ namespace moe {
 namespace {
 
 #ifndef MOE_BIG_NS
-#define MOE_BIG_NS 4
+#define MOE_BIG_NS 5
 #endif
 constexpr int BIG_NS = MOE_BIG_NS;  // ring stages
 constexpr int BIG_KS = 32;     // contraction elements per stage (one MFMA step)
@@ -162,57 +164,72 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)&lds[0][0][0];
   constexpr uint32_t SLOT_BYTES = 2u * BIG_ROWS * BIG_KS * 2u;
-  // Operand reads are issued as inline ds_read_b128 followed by an explicit
-  // lgkmcnt wait: the compiler cannot prove they do not alias the direct
-  // loads still in flight and would otherwise drain every load first.
-  // LDS reads complete in issue order: the eight B chunks first, then A row
-  // tile by row tile, and the multiplies of row tile m start as soon as its
-  // chunk is in (lgkmcnt(7 - m)). Each wait names the registers it guards,
-  // so no multiply can be scheduled above the wait that covers its operand.
-  auto compute = [&](int slot) {
-    u32x4 a[8], b[8];
+  // Operand reads are inline ds_read_b128: the compiler cannot prove they do
+  // not alias the direct loads in flight and would otherwise drain every
+  // load before each read.
+  auto read_b = [&](int slot, u32x4(&b)[8]) {
     const uint32_t sb = lds_base + (uint32_t)slot * SLOT_BYTES;
 #pragma unroll
     for (int n = 0; n < 8; ++n) asm volatile("ds_read_b128 %0, %1" : "=v"(b[n]) : "v"(sb + boff[n]));
+  };
+  auto read_a = [&](int slot, u32x4(&a)[8]) {
+    const uint32_t sb = lds_base + (uint32_t)slot * SLOT_BYTES;
 #pragma unroll
     for (int m = 0; m < 8; ++m) asm volatile("ds_read_b128 %0, %1" : "=v"(a[m]) : "v"(sb + aoff[m]));
-    asm volatile("s_waitcnt lgkmcnt(7)"
-                 : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(b[4]), "+v"(b[5]), "+v"(b[6]), "+v"(b[7]),
-                   "+v"(a[0]));
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      if (m == 1) asm volatile("s_waitcnt lgkmcnt(6)" : "+v"(a[1]));
-      if (m == 2) asm volatile("s_waitcnt lgkmcnt(5)" : "+v"(a[2]));
-      if (m == 3) asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(a[3]));
-      if (m == 4) asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(a[4]));
-      if (m == 5) asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(a[5]));
-      if (m == 6) asm volatile("s_waitcnt lgkmcnt(1)" : "+v"(a[6]));
-      if (m == 7) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[7]));
+  };
+  // Row tile m multiplies as soon as its A chunk is in: LDS reads complete in
+  // issue order, and the 8 A reads are issued before the 8 B reads of the
+  // next stage, so A chunk m has landed at lgkmcnt(15 - m). Each wait names
+  // the register it guards and a scheduling barrier closes every row tile,
+  // so no multiply moves above the wait that covers its operand.
+  auto multiply = [&](u32x4(&a)[8], const u32x4(&b)[8]) {
+    static_for<0, 8>([&](auto M) {
+      constexpr int m = decltype(M)::value;
+      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a[m]) : "n"(15 - m));
 #pragma unroll
       for (int n = 0; n < 8; ++n)
         acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_big(a[m]), as_bf16x8_big(b[n]), acc[m][n], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);  // keep each row tile's wait ahead of its own multiplies only
-    }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
-  // Prologue: stages 0..NS-2 in flight (clamped: stages past the end re-load
-  // the last stage; they are never read).
+  // Ring of NS slots holding stages k .. k+NS-1 while stage k is multiplied.
+  // Stages past the end re-load the last stage (never multiplied), so every
+  // iteration issues the same 8 direct loads per wave and one fixed wait
+  // count holds. The B operand is read one stage ahead (two register sets);
+  // the A operand is read in the stage that uses it.
+  //
+  // Iteration k: (1) wait until this wave's loads of stage k+1 have landed
+  // (at most the NS-3 younger stages outstanding); (2) lgkmcnt(0) + barrier:
+  // every wave's stage k+1 is visible, and every wave has finished reading
+  // stage k-1, so (3) its slot is refilled with stage k+NS-1; (4) the A
+  // chunks of stage k and then the B chunks of stage k+1 are read from LDS
+  // while (5) the matrix cores multiply stage k.
   const int last = nk - 1;
+  u32x4 a[8], b0[8], b1[8];
 #pragma unroll
   for (int s = 0; s < BIG_NS - 1; ++s) issue_stage(s, s < nk ? s : last);
-  // Every iteration issues the same 8 loads per wave, unconditionally, so
-  // one fixed wait count holds: when at most the 2 younger stages' loads are
-  // outstanding, this wave's stage k has landed. The barrier then publishes
-  // every wave's stage k and retires every wave's reads of slot (k-1)%NS,
-  // which the loads issued next refill.
-#pragma unroll 1
-  for (int k = 0; k < nk; ++k) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * (BIG_NS - 2)));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * (BIG_NS - 2)));
+  asm volatile("s_barrier" ::: "memory");
+  read_b(0, b0);
+  auto iteration = [&](int k, const u32x4(&b_cur)[8], u32x4(&b_next)[8]) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * (BIG_NS - 3)));
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     issue_stage((k + BIG_NS - 1) % BIG_NS, k + BIG_NS - 1 < nk ? k + BIG_NS - 1 : last);
-    compute(k % BIG_NS);
+    read_a(k % BIG_NS, a);
+    read_b((k + 1) % BIG_NS, b_next);
+    multiply(a, b_cur);
+  };
+  // nk is even (the contraction is a multiple of 64): two stages per trip,
+  // alternating the B register sets.
+#pragma unroll 1
+  for (int k = 0; k < nk; k += 2) {
+    iteration(k, b0, b1);
+    iteration(k + 1, b1, b0);
   }
-  // drain the loads of the clamped trailing stages before the block ends
+  // drain the trailing reads and the loads of the clamped stages before the block ends
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
   // Accumulator layout of a 16x16 MFMA tile: lane holds column (lane & 15),
@@ -245,10 +262,9 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
 
 }  // namespace
 
-bool big_tiles_fit(int Kdim) { return Kdim % BIG_KS == 0; }
-
 hipError_t launch_grouped_gemm_big(int epi, const GemmArgs& g, hipStream_t s) {
   if (g.max_tiles <= 0 || g.N <= 0) return hipSuccess;
+  if (g.Kdim % (2 * BIG_KS)) return hipErrorInvalidValue;  // the main loop takes two stages per trip
   const int BN = epi == EPI_SWIGLU ? BIG_ROWS / 2 : BIG_ROWS;
   const int n_nb = (g.N + BN - 1) / BN;
   const int64_t blocks = ((int64_t)g.max_tiles * n_nb + 7) / 8 * 8;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe.h"
 
 namespace moe {
@@ -29,6 +31,16 @@ __device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// f(std::integral_constant<int, I>{}) for I = B .. E-1: indices into register
+// arrays are constant expressions, so the arrays never need memory.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // One row segment of a grouped GEMM: rows [row0, row1) of group `group`.
 struct Tile {
