@@ -202,6 +202,7 @@ moe_status run_route(const moe_config* c, int64_t T, const void* x, const void* 
   g.ldo = c->n_experts;
   g.bias = bias;
   g.b_packed = packed(c);
+  g.b_reuse = 1;
   g.ksplit = route_ksplit(c, T);
   g.slice_stride = T * c->n_experts;
   MOE_TRY_HIP(launch_grouped_gemm(c->dtype, EPI_F32, BM, g, s), "router linear layer");

@@ -50,14 +50,27 @@ __global__ void __launch_bounds__(256) combine_kernel(int D, int K, const float*
   if ((D & 3) == 0) {
     for (int c = c0 + tid * 4; c < c1; c += 1024) {
       float4 acc = y_shared ? *(const float4*)(y_shared + t * D + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int k = 0; k < K; ++k) {
-        if (s_row[k] < 0) continue;
-        const float4 v = *(const float4*)(y_perm + s_row[k] * D + c);
-        const float w = s_p[k];
-        acc.x = fmaf(w, v.x, acc.x);
-        acc.y = fmaf(w, v.y, acc.y);
-        acc.z = fmaf(w, v.z, acc.z);
-        acc.w = fmaf(w, v.w, acc.w);
+      // eight rows per batch, all loads issued before the first add (a
+      // skipped pair reads row 0 and is not added); adds stay in k order
+      for (int k0 = 0; k0 < K; k0 += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int k = k0 + u;
+          const int64_t r = (k < K && s_row[k] >= 0) ? s_row[k] : 0;
+          v[u] = *(const float4*)(y_perm + r * D + c);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int k = k0 + u;
+          if (k < K && s_row[k] >= 0) {
+            const float w = s_p[k];
+            acc.x = fmaf(w, v[u].x, acc.x);
+            acc.y = fmaf(w, v[u].y, acc.y);
+            acc.z = fmaf(w, v[u].z, acc.z);
+            acc.w = fmaf(w, v[u].w, acc.w);
+          }
+        }
       }
       store4(out + t * D + c, acc);
     }

@@ -73,6 +73,21 @@ __device__ __forceinline__ const T* group_b(const GemmArgs& p, const void* main,
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// 16-byte load of weights. Non-temporal (NT) for the expert GEMMs: each
+// weight byte is used by one block only, so the loads stream past L2
+// instead of displacing the shared activation rows. Measured: decode
+// gate/up 0.634 -> 0.535 ms for the same bytes.
+template <bool NT>
+__device__ __forceinline__ uint4 load_b(const bf16_t* p) {
+  if constexpr (NT) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *(const uint4*)p;
+  }
+}
+
 // LDS offset (in bf16 elements) of 16-byte chunk `c` of staged row `r` (row
 // length KS): chunks are XOR-swizzled by (r & 7) so the 16-byte operand reads
 // of 8 consecutive rows hit distinct banks.
@@ -81,11 +96,13 @@ __device__ __forceinline__ int lds_off(int r, int c) { return r * KS + ((c ^ (r 
 
 // EPI: epilogue; MT: 16-row MFMA tiles per block; NW: 16-column weight tiles
 // per wave and operand; KSTEPS: 32-element MFMA steps per pipeline stage;
-// NS: pipeline depth; PK: weights in the packed fragment layout (below). Loads of stage k+NS-1 are issued before stage k is
+// NS: pipeline depth; PK: weights in the packed fragment layout (below);
+// NT: weights loaded non-temporally (load_stream; not for the router, whose
+// weights every row tile reads again). Loads of stage k+NS-1 are issued before stage k is
 // multiplied, so NS-1 stages of weights (and A rows) are in flight per wave
 // while the matrix cores work; the ring lives in VGPRs and the loop is
 // unrolled by NS so every ring slot is a fixed register range.
-template <int EPI, int MT, int NW, int KSTEPS, int NS, bool PK>
+template <int EPI, int MT, int NW, int KSTEPS, int NS, bool PK, bool NT>
 __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
   constexpr int KS = 32 * KSTEPS;                       // contraction elements per stage
   constexpr int CPR = KS / 8;                           // 16-byte chunks per staged row
@@ -172,7 +189,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
     for (int j = 0; j < NBT; ++j)
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
-        b[j][s] = *(const uint4*)(bptr[j] + (PK ? (ks * KSTEPS + s) * PACKED_FRAG : ks * KS + s * 32));
+        b[j][s] = load_b<NT>(bptr[j] + (PK ? (ks * KSTEPS + s) * PACKED_FRAG : ks * KS + s * 32));
 #pragma unroll
     for (int i = 0; i < NA; ++i) a[i] = *(const uint4*)(arow[i] + ks * KS);
   };
@@ -398,8 +415,13 @@ static hipError_t launch_fast(const GemmArgs& g, hipStream_t s) {
   const int n_nb = (g.N + 4 * NW * 16 - 1) / (4 * NW * 16);
   const int64_t blocks = ((int64_t)g.max_tiles * n_nb + 7) / 8 * 8;
   const dim3 grid((unsigned)blocks, (unsigned)g.ksplit);
-  if (g.b_packed) gemm_bf16_mfma<EPI, MT, NW, KSTEPS, NS, true><<<grid, 256, 0, s>>>(g);
-  else gemm_bf16_mfma<EPI, MT, NW, KSTEPS, NS, false><<<grid, 256, 0, s>>>(g);
+  if (g.b_reuse) {
+    if (g.b_packed) gemm_bf16_mfma<EPI, MT, NW, KSTEPS, NS, true, false><<<grid, 256, 0, s>>>(g);
+    else gemm_bf16_mfma<EPI, MT, NW, KSTEPS, NS, false, false><<<grid, 256, 0, s>>>(g);
+  } else {
+    if (g.b_packed) gemm_bf16_mfma<EPI, MT, NW, KSTEPS, NS, true, true><<<grid, 256, 0, s>>>(g);
+    else gemm_bf16_mfma<EPI, MT, NW, KSTEPS, NS, false, true><<<grid, 256, 0, s>>>(g);
+  }
   return hipGetLastError();
 }
 

@@ -42,6 +42,10 @@ namespace {
 constexpr int BIG_NS = MOE_BIG_NS;  // ring stages
 constexpr int BIG_KS = 32;     // contraction elements per stage (one MFMA step)
 constexpr int BIG_ROWS = 256;  // A rows and B (weight) rows per block tile
+// Cache policy of the weight loads: non-temporal. Every weight byte is used
+// by one block only (per row tile), so it should not push the activation
+// rows, which the column blocks of a row tile share, out of L2.
+constexpr int CPOL_NT = 2;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -134,7 +138,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
       __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + koff),
                                        (lds_void_t*)&lds[slot][0][(wave * 64 + i * 16) * BIG_KS], 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + (PK ? ks * PACKED_FRAG : koff)),
-                                       (lds_void_t*)&lds[slot][1][(wave * 64 + i * 16) * BIG_KS], 16, 0, 0);
+                                       (lds_void_t*)&lds[slot][1][(wave * 64 + i * 16) * BIG_KS], 16, 0, CPOL_NT);
     }
   };
 

@@ -86,6 +86,7 @@ struct GemmArgs {
   void* out;              // [rows, ldo]
   int64_t ldo;
   int32_t b_packed;       // B operands in the packed fragment layout (bf16 MFMA kernels only)
+  int32_t b_reuse;        // B is read again by many row tiles (router): keep it cacheable
   const float* bias;      // EPI_F32: per-column bias or NULL
   int32_t ksplit;         // EPI_F32 only: the contraction is cut into ksplit slices;
   int64_t slice_stride;   //   slice s writes its partial sums to out + s*slice_stride

@@ -143,11 +143,30 @@ __global__ void __launch_bounds__(256) gather_rows_bytes_kernel(const uint8_t* _
   for (int i = threadIdx.x; i < row_bytes; i += 256) x_perm[r * row_bytes + i] = x[t * row_bytes + i];
 }
 
-// Small batches (T*K <= 1024, E <= 1024): the whole permutation and the
+// Exclusive prefix sum over a block of 1024 threads (16 waves): wave scans,
+// then the 16 wave totals scanned by wave 0. s_tot holds 16 ints; *total
+// receives the sum. Two barriers; every thread of the block must call it.
+__device__ __forceinline__ int block1024_excl_scan(int v, int* s_tot, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v, lane);
+  if (lane == 63) s_tot[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < 16 ? s_tot[lane] : 0;
+    w = wave_incl_scan(w, lane);
+    if (lane < 16) s_tot[lane] = w;
+  }
+  __syncthreads();
+  *total = s_tot[15];
+  return (wave ? s_tot[wave - 1] : 0) + incl - v;
+}
+
+// Small batches (T*K <= 1024, E <= 1023): the whole permutation and the
 // expert-GEMM tile table in one block of 1024 threads. Counts come from LDS
 // atomics (order-independent); each pair's rank among the earlier pairs of
-// its expert is counted directly over the pairs before it, so the result is
-// the same stable permutation as the two-kernel path.
+// its expert is counted directly over the pairs before it (a wave-uniform
+// loop over 16-byte LDS reads), so the result is the same stable
+// permutation as the two-kernel path.
 __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __restrict__ idx, int P, int K, int E,
                                                              int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ sorted_token,
@@ -155,44 +174,43 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
                                                              int32_t* __restrict__ offsets_ext, int32_t extra_rows,
                                                              Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles,
                                                              int32_t max_tiles, int BM) {
-  __shared__ int s_idx[1024];
-  __shared__ int s_cnt[1025];
-  __shared__ int s_scan[1024];
-  const int tid = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) int s_idx[1024];
+  __shared__ int s_off[1025];
+  __shared__ int s_tot[16];
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int e_mine = tid < P ? idx[tid] : -1;
   s_idx[tid] = e_mine;
-  s_cnt[tid] = 0;
+  s_off[tid] = 0;
   __syncthreads();
   const bool valid = e_mine >= 0 && e_mine < E;
-  if (valid) atomicAdd(&s_cnt[e_mine], 1);
+  if (valid) atomicAdd(&s_off[e_mine], 1);
   __syncthreads();
   // exclusive scan of the counts (expert tid)
-  const int c = tid < E ? s_cnt[tid] : 0;
-  s_scan[tid] = c;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
-  }
-  const int off_mine = s_scan[tid] - c;  // offset of expert tid
-  const int total = s_scan[1023];
-  __syncthreads();
-  if (tid < E) s_cnt[tid] = off_mine;  // s_cnt now holds offsets
-  if (tid == 0) s_cnt[E] = total;
+  const int c = tid < E ? s_off[tid] : 0;
+  int total;
+  const int off_mine = block1024_excl_scan(c, s_tot, &total);
+  if (tid < E) s_off[tid] = off_mine;  // s_off now holds offsets
+  if (tid == 0) s_off[E] = total;
   __syncthreads();
   if (tid <= E) {
-    if (offsets) offsets[tid] = s_cnt[tid];
-    if (offsets_ext) offsets_ext[tid] = s_cnt[tid];
+    if (offsets) offsets[tid] = s_off[tid];
+    if (offsets_ext) offsets_ext[tid] = s_off[tid];
   }
   if (tid == 0 && offsets_ext) offsets_ext[E + 1] = total + extra_rows;
-  // stable rank: earlier pairs routed to the same expert
+  // stable rank: earlier pairs routed to the same expert. The loop bound is
+  // uniform per wave (the wave's last pair; 0 for waves past the last
+  // pair); 4 pairs per LDS read.
+  const int wave_end = wave * 64 < P ? min(P, (wave + 1) * 64) : 0;
+  int r = 0;
+#pragma unroll 8
+  for (int j0 = 0; j0 < wave_end; j0 += 4) {
+    const int4 q = *(const int4*)&s_idx[j0];
+    r += (j0 < tid && q.x == e_mine) + (j0 + 1 < tid && q.y == e_mine) + (j0 + 2 < tid && q.z == e_mine) +
+         (j0 + 3 < tid && q.w == e_mine);
+  }
   if (tid < P) {
     if (valid) {
-      int r = 0;
-      for (int j = 0; j < tid; ++j) r += s_idx[j] == e_mine;
-      const int d = s_cnt[e_mine] + r;
+      const int d = s_off[e_mine] + r;
       dest[tid] = d;
       sorted_token[d] = tid / K;
     } else {
@@ -204,23 +222,16 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
   const int n_groups = E + (extra_rows > 0 ? 1 : 0);
   int seg0 = 0, seg1 = 0;
   if (tid < n_groups) {
-    seg0 = tid < E ? s_cnt[tid] : total;
-    seg1 = tid < E ? s_cnt[tid + 1] : total + extra_rows;
+    seg0 = tid < E ? s_off[tid] : total;
+    seg1 = tid < E ? s_off[tid + 1] : total + extra_rows;
   }
   const int mine = (seg1 - seg0 + BM - 1) / BM;
-  __syncthreads();
-  s_scan[tid] = mine;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
-  }
-  int slot = s_scan[tid] - mine;
-  for (int r = seg0; r < seg1; r += BM, ++slot)
-    if (slot < max_tiles) tiles[slot] = Tile{tid, r, r + BM < seg1 ? r + BM : seg1, 0};
-  if (tid == 1023) *n_tiles = s_scan[1023] < max_tiles ? s_scan[1023] : max_tiles;
+  int n_all;
+  __syncthreads();  // s_tot is reused
+  int slot = block1024_excl_scan(mine, s_tot, &n_all);
+  for (int row = seg0; row < seg1; row += BM, ++slot)
+    if (slot < max_tiles) tiles[slot] = Tile{tid, row, row + BM < seg1 ? row + BM : seg1, 0};
+  if (tid == 1023) *n_tiles = n_all < max_tiles ? n_all : max_tiles;
 }
 
 }  // namespace

@@ -70,16 +70,34 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 
 // Sum of nsplit partial logit arrays for one token, one block (4 waves) per
 // token: wave w adds slices w, w+4, ... in order, then the four wave sums are
-// added in wave order. Result in LDS.
+// added in wave order. Result in LDS. All of a lane's loads for four slices
+// are issued before the first add, so the chain of dependent loads is short.
+template <int VPL>
 __device__ __forceinline__ void sum_partials(const float* __restrict__ logits, int nsplit, int64_t T, int E,
                                              int64_t t, float* s_logit, float* s_part) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t slice = T * (int64_t)E;
-  for (int e = lane; e < E; e += 64) {
-    float a = 0.f;
-    for (int s = wave; s < nsplit; s += 4) a += logits[s * slice + t * E + e];
-    s_part[wave * 1024 + e] = a;
+  float part[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) part[j] = 0.f;
+  const float* base = logits + t * E + lane;
+  for (int s0 = wave; s0 < nsplit; s0 += 16) {
+    float v[4][VPL];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = s0 + 4 * u;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) v[u][j] = (s < nsplit && lane + 64 * j < E) ? base[s * slice + 64 * j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < VPL; ++j)
+        if (s0 + 4 * u < nsplit) part[j] += v[u][j];
   }
+#pragma unroll
+  for (int j = 0; j < VPL; ++j)
+    if (lane + 64 * j < E) s_part[wave * 1024 + lane + 64 * j] = part[j];
   __syncthreads();
   for (int e = tid; e < E; e += 256)
     s_logit[e] = ((s_part[e] + s_part[1024 + e]) + s_part[2048 + e]) + s_part[3072 + e];
@@ -97,7 +115,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   const float* l;
   if (nsplit > 1) {  // one token per block: the four waves add the partial sums
     t = blockIdx.x;
-    sum_partials(logits, nsplit, T, E, t, s_logit, s_part);
+    sum_partials<VPL>(logits, nsplit, T, E, t, s_logit, s_part);
     if (threadIdx.x >= 64) return;
     l = s_logit;
   } else {           // one token per wave
