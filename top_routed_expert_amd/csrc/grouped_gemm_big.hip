@@ -150,36 +150,33 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // operand read of lane (r = lane & 15, q = lane >> 4) from a 16-row tile
+  // operand read of lane (r = lane & 15, q = lane >> 4) from a 16-row tile.
+  // LDS byte offsets of this lane's operand chunks inside a slot: the row
+  // swizzle depends on the row modulo 8 only, so row tile m (n) is the
+  // first one's offset + 1024 m (n), an immediate of the read instruction.
   const int rq = lane >> 4, rr = lane & 15;
-  // LDS byte offsets of this lane's operand chunks inside a slot (the row
-  // swizzle depends only on the row, which is fixed per lane and tile)
-  uint32_t aoff[8], boff[8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int row = wm * 128 + m * 16 + rr;
-    aoff[m] = (uint32_t)(row * BIG_KS + ((rq ^ swz(row)) << 3)) * 2u;
-  }
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const int row = wn * 128 + n * 16 + rr;
-    boff[n] = PK ? (uint32_t)(BIG_ROWS * BIG_KS + (wn * 128 + n * 16) * BIG_KS) * 2u + (uint32_t)lane * 16u
-                 : (uint32_t)(BIG_ROWS * BIG_KS + row * BIG_KS + ((rq ^ swz(row)) << 3)) * 2u;
-  }
+  const uint32_t aoff0 = (uint32_t)((wm * 128 + rr) * BIG_KS + ((rq ^ swz(wm * 128 + rr)) << 3)) * 2u;
+  const uint32_t boff0 = PK ? (uint32_t)(BIG_ROWS * BIG_KS + wn * 128 * BIG_KS) * 2u + (uint32_t)lane * 16u
+                            : (uint32_t)(BIG_ROWS * BIG_KS + (wn * 128 + rr) * BIG_KS + ((rq ^ swz(wn * 128 + rr)) << 3)) * 2u;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)&lds[0][0][0];
   constexpr uint32_t SLOT_BYTES = 2u * BIG_ROWS * BIG_KS * 2u;
   // Operand reads are inline ds_read_b128: the compiler cannot prove they do
   // not alias the direct loads in flight and would otherwise drain every
   // load before each read.
   auto read_b = [&](int slot, u32x4(&b)[8]) {
-    const uint32_t sb = lds_base + (uint32_t)slot * SLOT_BYTES;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) asm volatile("ds_read_b128 %0, %1" : "=v"(b[n]) : "v"(sb + boff[n]));
+    const uint32_t addr = lds_base + (uint32_t)slot * SLOT_BYTES + boff0;
+    // (explicit captures: clang does not capture names used only as asm operands)
+    static_for<0, 8>([&b, addr](auto N) {
+      constexpr int n = decltype(N)::value;
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(b[n]) : "v"(addr), "n"(n * 1024));
+    });
   };
   auto read_a = [&](int slot, u32x4(&a)[8]) {
-    const uint32_t sb = lds_base + (uint32_t)slot * SLOT_BYTES;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) asm volatile("ds_read_b128 %0, %1" : "=v"(a[m]) : "v"(sb + aoff[m]));
+    const uint32_t addr = lds_base + (uint32_t)slot * SLOT_BYTES + aoff0;
+    static_for<0, 8>([&a, addr](auto M) {
+      constexpr int m = decltype(M)::value;
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(a[m]) : "v"(addr), "n"(m * 1024));
+    });
   };
   // Row tile m multiplies as soon as its A chunk is in: LDS reads complete in
   // issue order, and the 8 A reads are issued before the 8 B reads of the
@@ -236,28 +233,62 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-  // Accumulator layout of a 16x16 MFMA tile: lane holds column (lane & 15),
-  // rows 4*(lane >> 4) + v.
-  const int64_t rbase = (int64_t)t.row0 + wm * 128 + (lane >> 4) * 4;
+  // Epilogue through LDS, one 16-row tile at a time: the wave writes its
+  // results into its own LDS rows (accumulator layout: lane holds column
+  // lane & 15 of each 16-column tile, rows 4*(lane >> 4) + v), then reads
+  // whole rows back 16 bytes per lane and stores them, so every store
+  // instruction writes full contiguous row runs instead of 32- or 64-byte
+  // pieces. The ring is no longer needed: one barrier ends every wave's
+  // reads of it first.
+  __syncthreads();
+  if constexpr (EPI == EPI_SWIGLU) {
+    // 16 rows x 64 bf16 columns per wave; rows padded to 72 elements
+    constexpr int LDW = 72;
+    bf16_t* wbuf = &lds[0][0][0] + wave * 16 * LDW;
+    const int col0 = nb * BN + wn * 64;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < 8; ++m) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t r = rbase + m * 16 + v;
-      if (r >= t.row1) continue;
-      if constexpr (EPI == EPI_SWIGLU) {
-        // weight tiles 0..3: gate of columns wn*64 + n*16; 4..7: up of the same columns
+      for (int n = 0; n < 4; ++n)
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const int col = nb * BN + wn * 64 + n * 16 + (lane & 15);
-          if (col < p.N)
-            ((bf16_t*)p.out)[r * p.ldo + col] = f32_to_bf16(silu(acc[m][n][v]) * acc[m][n + 4][v]);
-        }
-      } else {
+        for (int v = 0; v < 4; ++v)
+          wbuf[(4 * (lane >> 4) + v) * LDW + n * 16 + (lane & 15)] = f32_to_bf16(silu(acc[m][n][v]) * acc[m][n + 4][v]);
+      // 8 lanes per row (16 bytes each), 8 rows per pass, 2 passes
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const int col = nb * BN + wn * 128 + n * 16 + (lane & 15);
-          if (col < p.N) ((float*)p.out)[r * p.ldo + col] = acc[m][n][v] + (p.bias ? p.bias[col] : 0.f);
+      for (int pass = 0; pass < 2; ++pass) {
+        const int rr16 = pass * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+        const uint4 v = *(const uint4*)&wbuf[rr16 * LDW + c8];
+        const int64_t r = (int64_t)t.row0 + wm * 128 + m * 16 + rr16;
+        const int col = col0 + c8;
+        if (r < t.row1 && col < p.N) *(uint4*)&((bf16_t*)p.out)[r * p.ldo + col] = v;
+      }
+    }
+  } else {
+    // 16 rows x 128 fp32 columns per wave; rows padded to 132 floats
+    constexpr int LDW = 132;
+    float* wbuf = (float*)&lds[0][0][0] + wave * 16 * LDW;
+    const int col0 = nb * BN + wn * 128;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) wbuf[(4 * (lane >> 4) + v) * LDW + n * 16 + (lane & 15)] = acc[m][n][v];
+      // 32 lanes per row (16 bytes each), 2 rows per pass, 8 passes
+#pragma unroll
+      for (int pass = 0; pass < 8; ++pass) {
+        const int rr16 = pass * 2 + (lane >> 5), c4 = (lane & 31) * 4;
+        float4 v = *(const float4*)&wbuf[rr16 * LDW + c4];
+        const int64_t r = (int64_t)t.row0 + wm * 128 + m * 16 + rr16;
+        const int col = col0 + c4;
+        if (r < t.row1 && col < p.N) {
+          if (p.bias) {
+            v.x += p.bias[col];
+            v.y += p.bias[col + 1];
+            v.z += p.bias[col + 2];
+            v.w += p.bias[col + 3];
+          }
+          *(float4*)&((float*)p.out)[r * p.ldo + col] = v;
         }
       }
     }
@@ -269,6 +300,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
 hipError_t launch_grouped_gemm_big(int epi, const GemmArgs& g, hipStream_t s) {
   if (g.max_tiles <= 0 || g.N <= 0) return hipSuccess;
   if (g.Kdim % (2 * BIG_KS)) return hipErrorInvalidValue;  // the main loop takes two stages per trip
+  if (g.N % 8 || g.ldo % 8) return hipErrorInvalidValue;    // the epilogue stores 8 bf16 / 4 fp32 columns at once
   const int BN = epi == EPI_SWIGLU ? BIG_ROWS / 2 : BIG_ROWS;
   const int n_nb = (g.N + BN - 1) / BN;
   const int64_t blocks = ((int64_t)g.max_tiles * n_nb + 7) / 8 * 8;
