@@ -378,8 +378,9 @@ __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __rest
   for (int g = g0; g < g1; ++g) {
     int64_t a, b;
     seg(g, a, b);
+    const int first = slot, count = (int)((b - a + BM - 1) / BM);
     for (int64_t r = a; r < b; r += BM, ++slot)
-      if (slot < max_tiles) tiles[slot] = Tile{g, (int32_t)r, (int32_t)(r + BM < b ? r + BM : b), 0};
+      if (slot < max_tiles) tiles[slot] = Tile{g, (int32_t)r, (int32_t)(r + BM < b ? r + BM : b), first, count, 0, 0, 0};
   }
   if (tid == 1023) *n_tiles = min(s_scan[1023], max_tiles);
 }

@@ -42,6 +42,10 @@ namespace {
 constexpr int BIG_NS = MOE_BIG_NS;  // ring stages
 constexpr int BIG_KS = 32;     // contraction elements per stage (one MFMA step)
 constexpr int BIG_ROWS = 256;  // A rows and B (weight) rows per block tile
+#ifndef MOE_BIG_CHUNK
+#define MOE_BIG_CHUNK 16
+#endif
+constexpr int CHUNK = MOE_BIG_CHUNK;  // row tiles of one group that share weight columns in flight
 // Cache policy of the weight loads: non-temporal. Every weight byte is used
 // by one block only (per row tile), so it should not push the activation
 // rows, which the column blocks of a row tile share, out of L2.
@@ -71,9 +75,27 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
   const int slot = blockIdx.x >> 3;
   const int L = (blockIdx.x & 7) * per_xcd + slot;
   if (slot >= per_xcd || L >= active) return;
-  const int ti = L / n_nb, nb = L - ti * n_nb;
+  int ti = L / n_nb, nb = L - ti * n_nb;
   Tile t;
   if (p.tiles) {
+    // A group (expert) with several row tiles: its blocks run in chunks of
+    // up to CHUNK row tiles with the row tile fastest, so the blocks running
+    // together on an XCD read the same weight columns (read from HBM once,
+    // then from L2) instead of each row tile streaming all of the expert's
+    // weights again. Single-tile groups keep column blocks fastest. The
+    // group's blocks are L = first*n_nb .. (first+count)*n_nb - 1 either way.
+    const Tile g = p.tiles[ti];
+    const int first = g.first;
+    int count = g.count;
+    count = first + count <= n_tiles ? count : n_tiles - first;  // malformed table: stay in range
+    if (count > 1 && first >= 0 && first <= ti && ti < first + count) {
+      const int local = L - first * n_nb;
+      const int c = local / (CHUNK * n_nb);
+      const int wc = count - c * CHUNK < CHUNK ? count - c * CHUNK : CHUNK;
+      const int local2 = local - c * CHUNK * n_nb;
+      nb = local2 / wc;
+      ti = first + c * CHUNK + local2 % wc;
+    }
     t = p.tiles[ti];
   } else {
     t.group = 0;

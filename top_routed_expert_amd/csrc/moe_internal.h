@@ -43,8 +43,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // One row segment of a grouped GEMM: rows [row0, row1) of group `group`.
+// first/count: the group's tiles are first .. first+count-1 (consecutive).
 struct Tile {
-  int32_t group, row0, row1, pad;
+  int32_t group, row0, row1, first;
+  int32_t count, pad0, pad1, pad2;
 };
 
 // Packed fragment layout of a bf16 weight matrix W [N, K] (K % 32 == 0):

@@ -229,8 +229,9 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
   int n_all;
   __syncthreads();  // s_tot is reused
   int slot = block1024_excl_scan(mine, s_tot, &n_all);
+  const int first = slot;
   for (int row = seg0; row < seg1; row += BM, ++slot)
-    if (slot < max_tiles) tiles[slot] = Tile{tid, row, row + BM < seg1 ? row + BM : seg1, 0};
+    if (slot < max_tiles) tiles[slot] = Tile{tid, row, row + BM < seg1 ? row + BM : seg1, first, mine, 0, 0, 0};
   if (tid == 1023) *n_tiles = n_all < max_tiles ? n_all : max_tiles;
 }
 
