@@ -7,23 +7,31 @@
 // 256-weight-row tile halves the operand bytes per flop pulled from L2
 // relative to 128 x 256 tiles.
 //
-// Block: 4 waves in a 2 x 2 layout, each wave 128 rows x 128 weight rows =
-// 8 x 8 MFMA 16x16x32 tiles (256 fp32 accumulators per lane). For gate/up
-// the 256 weight rows of a block are [gate c0..c0+63, up c0..c0+63,
-// gate c0+64..c0+127, up c0+64..c0+127], so each wave holds the gate and up
-// sums of the same 64 columns and applies the SwiGLU in registers.
+// Work item: one (row tile, column block) pair. Block: 4 waves in a 2 x 2
+// layout, each wave 128 rows x 128 weight rows = 8 x 8 MFMA 16x16x32 tiles
+// (256 fp32 accumulators per lane). For gate/up the 256 weight rows of an
+// item are [gate c0..c0+63, up c0..c0+63, gate c0+64..c0+127, up
+// c0+64..c0+127], so each wave holds the gate and up sums of the same 64
+// columns and applies the SwiGLU in registers.
+//
+// Persistent blocks: one block per CU walks its share of the items. The
+// load stream runs on across items: the last stages of an item issue the
+// first stages of the next one, so items meet with no pipeline drain and
+// an item's epilogue (results through LDS to HBM) runs while the next
+// item's operands are already in flight.
 //
 // Both operands go HBM/L2 -> LDS through direct loads (global_load_lds,
-// 16 bytes per lane, no VGPR staging) into a ring of NS = 5 stages of one
-// 32-element MFMA step each (16 KB of A + 16 KB of B per stage, all 160 KB
-// of LDS). The B operand of a stage is read from LDS into registers one
-// stage ahead (two register sets) and the A operand row tile by row tile in
-// the stage itself, so the LDS reads overlap the matrix-core work. Waits are explicit: a wave waits for its
-// own loads of a stage with s_waitcnt vmcnt (loads complete in issue order),
-// then one s_barrier per stage makes every wave's loads of that stage
-// visible and ends every wave's reads of the slot about to be refilled. The
-// barrier is issued as inline asm with a memory clobber: the compiler may
-// not move memory accesses across it and does not add a drain of its own.
+// 16 bytes per lane, no VGPR staging) into a ring of NS = 4 stages of one
+// 32-element MFMA step each (16 KB of A + 16 KB of B per stage, 128 KB),
+// beside a 32 KB epilogue staging area. The B operand of a stage is read
+// from LDS into registers one stage ahead (two register sets) and the A
+// operand row tile by row tile in the stage itself, so the LDS reads overlap
+// the matrix-core work. Waits are explicit: a wave waits for its own loads
+// of a stage with s_waitcnt vmcnt (loads complete in issue order), then one
+// s_barrier per stage makes every wave's loads of that stage visible and
+// ends every wave's reads of the slot about to be refilled. The barrier is
+// issued as inline asm with a memory clobber: the compiler may not move
+// memory accesses across it and does not add a drain of its own.
 //
 // LDS rows are 64 bytes (four 16-byte chunks); chunk q of row r is stored
 // at position q ^ ((r >> 1) & 3), so the 16-byte MFMA operand reads of
@@ -37,19 +45,20 @@ namespace moe {
 namespace {
 
 #ifndef MOE_BIG_NS
-#define MOE_BIG_NS 5
+#define MOE_BIG_NS 4
 #endif
 constexpr int BIG_NS = MOE_BIG_NS;  // ring stages
 constexpr int BIG_KS = 32;     // contraction elements per stage (one MFMA step)
-constexpr int BIG_ROWS = 256;  // A rows and B (weight) rows per block tile
+constexpr int BIG_ROWS = 256;  // A rows and B (weight) rows per item
 #ifndef MOE_BIG_CHUNK
 #define MOE_BIG_CHUNK 16
 #endif
 constexpr int CHUNK = MOE_BIG_CHUNK;  // row tiles of one group that share weight columns in flight
 // Cache policy of the weight loads: non-temporal. Every weight byte is used
-// by one block only (per row tile), so it should not push the activation
+// by one item only (per row tile), so it should not push the activation
 // rows, which the column blocks of a row tile share, out of L2.
 constexpr int CPOL_NT = 2;
+static_assert(BIG_NS >= 3 && BIG_NS * 32 + 32 <= 160, "ring + staging must fit 160 KB of LDS");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -66,92 +75,114 @@ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
 template <int EPI, bool PK>
 __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) bf16_t lds[BIG_NS][2][BIG_ROWS * BIG_KS];
+  __shared__ __attribute__((aligned(16))) float stg[4][16 * 128];  // epilogue staging, 8 KB per wave
 
-  const int BN = EPI == EPI_SWIGLU ? BIG_ROWS / 2 : BIG_ROWS;  // output columns per block
+  const int BN = EPI == EPI_SWIGLU ? BIG_ROWS / 2 : BIG_ROWS;  // output columns per item
   const int n_nb = (p.N + BN - 1) / BN;
   const int n_tiles = p.tiles ? *p.n_tiles : (int)((p.dense_rows + BIG_ROWS - 1) / BIG_ROWS);
   const int active = n_tiles * n_nb;
+  // Hardware places block b on XCD b % 8. The active items, counted on the
+  // device, are split into 8 contiguous runs, one per XCD (column blocks
+  // fastest, so the items of one row tile share an L2); the XCD's blocks
+  // take its items in turn.
   const int per_xcd = (active + 7) >> 3;
-  const int slot = blockIdx.x >> 3;
-  const int L = (blockIdx.x & 7) * per_xcd + slot;
-  if (slot >= per_xcd || L >= active) return;
-  int ti = L / n_nb, nb = L - ti * n_nb;
-  Tile t;
-  if (p.tiles) {
-    // A group (expert) with several row tiles: its blocks run in chunks of
-    // up to CHUNK row tiles with the row tile fastest, so the blocks running
-    // together on an XCD read the same weight columns (read from HBM once,
-    // then from L2) instead of each row tile streaming all of the expert's
-    // weights again. Single-tile groups keep column blocks fastest. The
-    // group's blocks are L = first*n_nb .. (first+count)*n_nb - 1 either way.
-    const Tile g = p.tiles[ti];
-    const int first = g.first;
-    int count = g.count;
-    count = first + count <= n_tiles ? count : n_tiles - first;  // malformed table: stay in range
-    if (count > 1 && first >= 0 && first <= ti && ti < first + count) {
-      const int local = L - first * n_nb;
-      const int c = local / (CHUNK * n_nb);
-      const int wc = count - c * CHUNK < CHUNK ? count - c * CHUNK : CHUNK;
-      const int local2 = local - c * CHUNK * n_nb;
-      nb = local2 / wc;
-      ti = first + c * CHUNK + local2 % wc;
-    }
-    t = p.tiles[ti];
-  } else {
-    t.group = 0;
-    t.row0 = ti * BIG_ROWS;
-    t.row1 = (int32_t)((int64_t)t.row0 + BIG_ROWS < p.dense_rows ? t.row0 + BIG_ROWS : p.dense_rows);
-  }
+  const int L_begin = (blockIdx.x & 7) * per_xcd;
+  const int L_end = L_begin + per_xcd < active ? L_begin + per_xcd : active;
+  const int L_step = gridDim.x >> 3;
+  int L = L_begin + (blockIdx.x >> 3);
+  if (L >= L_end) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar: branches on it are uniform
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Kdim = p.Kdim, nk = Kdim / BIG_KS;
   const bf16_t* A = (const bf16_t*)p.a;
-  const bf16_t* Bg = p.b0 == nullptr ? nullptr
-                   : (t.group < p.n_main ? (const bf16_t*)p.b0 + (int64_t)t.group * p.b_stride
-                                         : (const bf16_t*)p.b0_extra);
-  const bf16_t* Bu = EPI == EPI_SWIGLU ? (t.group < p.n_main ? (const bf16_t*)p.b1 + (int64_t)t.group * p.b_stride
-                                                             : (const bf16_t*)p.b1_extra)
-                                       : Bg;
 
-  // Direct-load sources. Load instruction i (0..3) of this wave fills rows
-  // R = wave*64 + i*16 .. R+15 of a stage; lane l writes the 16 bytes at LDS
-  // position (row R + l/4, physical chunk l%4), i.e. logical chunk
-  // (l%4) ^ swz(row). Rows outside the tile read row 0 (never stored).
+  // Item L -> (row tile, column block). A group (expert) with several row
+  // tiles runs in chunks of up to CHUNK row tiles with the row tile
+  // fastest, so the items running together on an XCD read the same weight
+  // columns (read from HBM once, then from L2) instead of each row tile
+  // streaming all of the expert's weights again. Single-tile groups keep
+  // column blocks fastest. The group's items are L = first*n_nb ..
+  // (first+count)*n_nb - 1 either way.
+  auto map_item = [&](int L, Tile& t, int& nb) {
+    int ti = L / n_nb;
+    nb = L - ti * n_nb;
+    if (p.tiles) {
+      const Tile g = p.tiles[ti];
+      const int first = g.first;
+      int count = g.count;
+      count = first + count <= n_tiles ? count : n_tiles - first;  // malformed table: stay in range
+      if (count > 1 && first >= 0 && first <= ti && ti < first + count) {
+        const int local = L - first * n_nb;
+        const int c = local / (CHUNK * n_nb);
+        const int wc = count - c * CHUNK < CHUNK ? count - c * CHUNK : CHUNK;
+        const int local2 = local - c * CHUNK * n_nb;
+        nb = local2 / wc;
+        ti = first + c * CHUNK + local2 % wc;
+      }
+      t = p.tiles[ti];
+    } else {
+      t.group = 0;
+      t.row0 = ti * BIG_ROWS;
+      t.row1 = (int32_t)((int64_t)t.row0 + BIG_ROWS < p.dense_rows ? t.row0 + BIG_ROWS : p.dense_rows);
+    }
+  };
+
+  // Direct-load sources of an item. Load instruction i (0..3) of this wave
+  // fills rows R = wave*64 + i*16 .. R+15 of a stage; lane l writes the 16
+  // bytes at LDS position (row R + l/4, physical chunk l%4), i.e. logical
+  // chunk (l%4) ^ swz(row). Rows outside the tile read row 0 (never stored).
+  // Source rows of this wave's A loads for an item (gather read early:
+  // the loads of the next item's rows are issued at the start of the
+  // current item, so setting the sources inside the loop needs no load).
+  auto load_rows = [&](const Tile& t, int32_t(&rows)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = (int64_t)t.row0 + wave * 64 + i * 16 + (lane >> 2);
+      int64_t src = -1;
+      if (r < t.row1) {
+        src = r < p.n_gather ? (int64_t)p.gather[r] : r - p.n_gather;
+        if (src >= p.n_a_rows) src = -1;
+      }
+      rows[i] = (int32_t)(src >= 0 ? src : 0);
+    }
+  };
   const bf16_t* asrc[4];
   const bf16_t* bsrc[4];
+  auto set_sources = [&](const Tile& t, int nb, const int32_t(&rows)[4]) {
+    const bf16_t* Bg = t.group < p.n_main ? (const bf16_t*)p.b0 + (int64_t)t.group * p.b_stride
+                                          : (const bf16_t*)p.b0_extra;
+    const bf16_t* Bu = EPI == EPI_SWIGLU ? (t.group < p.n_main ? (const bf16_t*)p.b1 + (int64_t)t.group * p.b_stride
+                                                               : (const bf16_t*)p.b1_extra)
+                                         : Bg;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = wave * 64 + i * 16 + (lane >> 2);
-    const int q = (lane & 3) ^ swz(row);
-    const int64_t r = (int64_t)t.row0 + row;
-    int64_t src = -1;
-    if (r < t.row1) {
-      src = r < p.n_gather ? (int64_t)p.gather[r] : r - p.n_gather;
-      if (src >= p.n_a_rows) src = -1;
+    for (int i = 0; i < 4; ++i) {
+      const int row = wave * 64 + i * 16 + (lane >> 2);
+      const int q = (lane & 3) ^ swz(row);
+      asrc[i] = A + (int64_t)rows[i] * Kdim + q * 8;
+      // weight row `row` of the item
+      int col;
+      const bf16_t* base;
+      if constexpr (EPI == EPI_SWIGLU) {
+        const int seg = row >> 6;  // gate, up, gate, up
+        col = nb * BN + (seg >> 1) * 64 + (row & 63);
+        base = (seg & 1) ? Bu : Bg;
+      } else {
+        col = nb * BN + row;
+        base = Bg;
+      }
+      if constexpr (PK) {
+        // the 16 rows of this instruction are one fragment column tile
+        int ct = (col - (row & 15)) >> 4;
+        const int ct_last = (p.N + 15) / 16 - 1;
+        ct = ct < ct_last ? ct : ct_last;
+        bsrc[i] = base + packed_offset(ct, 0, lane, Kdim);
+      } else {
+        col = col < p.N ? col : p.N - 1;
+        bsrc[i] = base + (int64_t)col * Kdim + q * 8;
+      }
     }
-    asrc[i] = A + (src >= 0 ? src : 0) * Kdim + q * 8;
-    // weight row `row` of the block tile
-    int col;
-    const bf16_t* base;
-    if constexpr (EPI == EPI_SWIGLU) {
-      const int seg = row >> 6;                  // gate, up, gate, up
-      col = nb * BN + (seg >> 1) * 64 + (row & 63);
-      base = (seg & 1) ? Bu : Bg;
-    } else {
-      col = nb * BN + row;
-      base = Bg;
-    }
-    if constexpr (PK) {
-      // the 16 rows of this instruction are one fragment column tile
-      int ct = (col - (row & 15)) >> 4;
-      const int ct_last = (p.N + 15) / 16 - 1;
-      ct = ct < ct_last ? ct : ct_last;
-      bsrc[i] = base + packed_offset(ct, 0, lane, Kdim);
-    } else {
-      col = col < p.N ? col : p.N - 1;
-      bsrc[i] = base + (int64_t)col * Kdim + q * 8;
-    }
-  }
+  };
 
   auto issue_stage = [&](int slot, int ks) {
     const int koff = ks * BIG_KS;
@@ -167,10 +198,6 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
   // wave (wm, wn): rows wm*128 .., weight rows wn*128 ..
   const int wm = wave >> 1, wn = wave & 1;
   f32x4 acc[8][8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m)
-#pragma unroll
-    for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // operand read of lane (r = lane & 15, q = lane >> 4) from a 16-row tile.
   // LDS byte offsets of this lane's operand chunks inside a slot: the row
@@ -216,18 +243,102 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
     });
   };
 
-  // Ring of NS slots holding stages k .. k+NS-1 while stage k is multiplied.
-  // Stages past the end re-load the last stage (never multiplied), so every
-  // iteration issues the same 8 direct loads per wave and one fixed wait
-  // count holds. The B operand is read one stage ahead (two register sets);
-  // the A operand is read in the stage that uses it.
+  // Epilogue of an item through this wave's staging area, one 16-row tile
+  // at a time: the wave writes its results (accumulator layout: lane holds
+  // column lane & 15 of each 16-column tile, rows 4*(lane >> 4) + v), then
+  // reads whole rows back 16 bytes per lane and stores them, so every store
+  // instruction writes full contiguous row runs. The staging area is the
+  // wave's own, outside the ring, so no barrier is needed around it.
+  auto epilogue = [&](const Tile& t, int nb) {
+    if constexpr (EPI == EPI_SWIGLU) {
+      // 16 rows x 64 bf16 columns; rows padded to 72 elements
+      constexpr int LDW = 72;
+      bf16_t* wbuf = (bf16_t*)&stg[wave][0];
+      const int col0 = nb * BN + wn * 64;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            wbuf[(4 * (lane >> 4) + v) * LDW + n * 16 + (lane & 15)] = f32_to_bf16(silu(acc[m][n][v]) * acc[m][n + 4][v]);
+        // 8 lanes per row (16 bytes each), 8 rows per pass, 2 passes
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+          const int rr16 = pass * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+          const uint4 v = *(const uint4*)&wbuf[rr16 * LDW + c8];
+          const int64_t r = (int64_t)t.row0 + wm * 128 + m * 16 + rr16;
+          const int col = col0 + c8;
+          if (r < t.row1 && col < p.N) *(uint4*)&((bf16_t*)p.out)[r * p.ldo + col] = v;
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one row tile at a time (register pressure)
+      }
+    } else {
+      // 16 rows x 128 fp32 columns; 16-column groups XOR-swizzled by
+      // (row >> 2) & 3, so the four rows one write instruction covers land
+      // in different banks (no padding: the area is exactly 8 KB)
+      float* wbuf = &stg[wave][0];
+      const int col0 = nb * BN + wn * 128;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int row = 4 * (lane >> 4) + v;
+            wbuf[row * 128 + ((n ^ ((row >> 2) & 3)) << 4) + (lane & 15)] = acc[m][n][v];
+          }
+        // 32 lanes per row (16 bytes each), 2 rows per pass, 8 passes
+#pragma unroll
+        for (int pass = 0; pass < 8; ++pass) {
+          const int rr16 = pass * 2 + (lane >> 5), c4 = (lane & 31) * 4;
+          float4 v = *(const float4*)&wbuf[rr16 * 128 + (c4 ^ (((rr16 >> 2) & 3) << 4))];
+          const int64_t r = (int64_t)t.row0 + wm * 128 + m * 16 + rr16;
+          const int col = col0 + c4;
+          if (r < t.row1 && col < p.N) {
+            if (p.bias) {
+              v.x += p.bias[col];
+              v.y += p.bias[col + 1];
+              v.z += p.bias[col + 2];
+              v.w += p.bias[col + 3];
+            }
+            *(float4*)&((float*)p.out)[r * p.ldo + col] = v;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // The ring holds stages in one sequence running across this block's
+  // items: global stage s (item j, stage k: s = j*nk + k) lives in slot
+  // s % NS. While stage k of the current item is multiplied the ring holds
+  // stages k .. k+NS-1 of the sequence (landed or in flight); the B operand
+  // is read one stage ahead (two register sets), the A operand in the stage
+  // that uses it. After the last item, stages past its end re-load its last
+  // stage (never multiplied), so every iteration issues the same 8 direct
+  // loads per wave and one fixed wait count holds.
   //
   // Iteration k: (1) wait until this wave's loads of stage k+1 have landed
   // (at most the NS-3 younger stages outstanding); (2) lgkmcnt(0) + barrier:
   // every wave's stage k+1 is visible, and every wave has finished reading
-  // stage k-1, so (3) its slot is refilled with stage k+NS-1; (4) the A
-  // chunks of stage k and then the B chunks of stage k+1 are read from LDS
-  // while (5) the matrix cores multiply stage k.
+  // stage k-1, so (3) its slot is refilled with stage k+NS-1 (of this item,
+  // else of the next one); (4) the A chunks of stage k and then the B chunks
+  // of stage k+1 are read from LDS while (5) the matrix cores multiply stage
+  // k.
+  Tile t_cur, t_next;
+  int nb_cur, nb_next;
+  int32_t rows[4];
+  map_item(L, t_cur, nb_cur);
+  load_rows(t_cur, rows);
+  set_sources(t_cur, nb_cur, rows);
+  int L_next = L + L_step;
+  bool has_next = L_next < L_end;
+  if (has_next) {
+    map_item(L_next, t_next, nb_next);
+    load_rows(t_next, rows);
+  }
+  int base = 0;  // slot of the current item's stage 0
   const int last = nk - 1;
   u32x4 a[8], b0[8], b1[8];
 #pragma unroll
@@ -239,83 +350,43 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * (BIG_NS - 3)));
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    issue_stage((k + BIG_NS - 1) % BIG_NS, k + BIG_NS - 1 < nk ? k + BIG_NS - 1 : last);
-    read_a(k % BIG_NS, a);
-    read_b((k + 1) % BIG_NS, b_next);
+    const int ks = k + BIG_NS - 1;  // stage of the sequence to issue, counted from this item's start
+    if (ks == nk && has_next) set_sources(t_next, nb_next, rows);  // from here on the next item's stages
+    issue_stage((base + ks) % BIG_NS, ks < nk ? ks : (has_next ? ks - nk : last));
+    read_a((base + k) % BIG_NS, a);
+    read_b((base + k + 1) % BIG_NS, b_next);
     multiply(a, b_cur);
   };
-  // nk is even (the contraction is a multiple of 64): two stages per trip,
-  // alternating the B register sets.
+  for (;;) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // nk is even (the contraction is a multiple of 64): two stages per trip,
+    // alternating the B register sets; every item starts with b0.
 #pragma unroll 1
-  for (int k = 0; k < nk; k += 2) {
-    iteration(k, b0, b1);
-    iteration(k + 1, b1, b0);
+    for (int k = 0; k < nk; k += 2) {
+      iteration(k, b0, b1);
+      iteration(k + 1, b1, b0);
+    }
+    epilogue(t_cur, nb_cur);
+    if (!has_next) break;
+    base = (base + nk) % BIG_NS;
+    t_cur = t_next;
+    nb_cur = nb_next;
+    L_next += L_step;
+    has_next = L_next < L_end;
+    if (has_next) {
+      map_item(L_next, t_next, nb_next);
+      load_rows(t_next, rows);
+    }
   }
   // drain the trailing reads and the loads of the clamped stages before the block ends
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-
-  // Epilogue through LDS, one 16-row tile at a time: the wave writes its
-  // results into its own LDS rows (accumulator layout: lane holds column
-  // lane & 15 of each 16-column tile, rows 4*(lane >> 4) + v), then reads
-  // whole rows back 16 bytes per lane and stores them, so every store
-  // instruction writes full contiguous row runs instead of 32- or 64-byte
-  // pieces. The ring is no longer needed: one barrier ends every wave's
-  // reads of it first.
-  __syncthreads();
-  if constexpr (EPI == EPI_SWIGLU) {
-    // 16 rows x 64 bf16 columns per wave; rows padded to 72 elements
-    constexpr int LDW = 72;
-    bf16_t* wbuf = &lds[0][0][0] + wave * 16 * LDW;
-    const int col0 = nb * BN + wn * 64;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          wbuf[(4 * (lane >> 4) + v) * LDW + n * 16 + (lane & 15)] = f32_to_bf16(silu(acc[m][n][v]) * acc[m][n + 4][v]);
-      // 8 lanes per row (16 bytes each), 8 rows per pass, 2 passes
-#pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-        const int rr16 = pass * 8 + (lane >> 3), c8 = (lane & 7) * 8;
-        const uint4 v = *(const uint4*)&wbuf[rr16 * LDW + c8];
-        const int64_t r = (int64_t)t.row0 + wm * 128 + m * 16 + rr16;
-        const int col = col0 + c8;
-        if (r < t.row1 && col < p.N) *(uint4*)&((bf16_t*)p.out)[r * p.ldo + col] = v;
-      }
-    }
-  } else {
-    // 16 rows x 128 fp32 columns per wave; rows padded to 132 floats
-    constexpr int LDW = 132;
-    float* wbuf = (float*)&lds[0][0][0] + wave * 16 * LDW;
-    const int col0 = nb * BN + wn * 128;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-#pragma unroll
-      for (int n = 0; n < 8; ++n)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) wbuf[(4 * (lane >> 4) + v) * LDW + n * 16 + (lane & 15)] = acc[m][n][v];
-      // 32 lanes per row (16 bytes each), 2 rows per pass, 8 passes
-#pragma unroll
-      for (int pass = 0; pass < 8; ++pass) {
-        const int rr16 = pass * 2 + (lane >> 5), c4 = (lane & 31) * 4;
-        float4 v = *(const float4*)&wbuf[rr16 * LDW + c4];
-        const int64_t r = (int64_t)t.row0 + wm * 128 + m * 16 + rr16;
-        const int col = col0 + c4;
-        if (r < t.row1 && col < p.N) {
-          if (p.bias) {
-            v.x += p.bias[col];
-            v.y += p.bias[col + 1];
-            v.z += p.bias[col + 2];
-            v.w += p.bias[col + 3];
-          }
-          *(float4*)&((float*)p.out)[r * p.ldo + col] = v;
-        }
-      }
-    }
-  }
 }
+
+int g_cus = 0;  // compute units of the device (queried once)
 
 }  // namespace
 
@@ -323,9 +394,20 @@ hipError_t launch_grouped_gemm_big(int epi, const GemmArgs& g, hipStream_t s) {
   if (g.max_tiles <= 0 || g.N <= 0) return hipSuccess;
   if (g.Kdim % (2 * BIG_KS)) return hipErrorInvalidValue;  // the main loop takes two stages per trip
   if (g.N % 8 || g.ldo % 8) return hipErrorInvalidValue;    // the epilogue stores 8 bf16 / 4 fp32 columns at once
+  if (g_cus == 0) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    g_cus = cus > 8 ? cus : 8;
+  }
   const int BN = epi == EPI_SWIGLU ? BIG_ROWS / 2 : BIG_ROWS;
   const int n_nb = (g.N + BN - 1) / BN;
-  const int64_t blocks = ((int64_t)g.max_tiles * n_nb + 7) / 8 * 8;
+  // one block per CU (the kernel takes all of a CU's LDS), at most one per
+  // possible item, a multiple of 8 so every XCD gets the same number
+  int64_t blocks = ((int64_t)g.max_tiles * n_nb + 7) / 8 * 8;
+  const int64_t cap = (int64_t)g_cus / 8 * 8;
+  blocks = blocks < cap ? blocks : cap;
   if (g.b_packed) {
     if (epi == EPI_SWIGLU) gemm_bf16_big<EPI_SWIGLU, true><<<(unsigned)blocks, 256, 0, s>>>(g);
     else gemm_bf16_big<EPI_F32, true><<<(unsigned)blocks, 256, 0, s>>>(g);
