@@ -220,6 +220,34 @@ def test_layer_full_size(name, n_rows):
         assert load["skew"] > 10.0  # the Zipf-like bias makes the hottest expert >10x the mean load
 
 
+def test_layer_many_items_per_block():
+    """Many rows per expert with narrow layers: the 256x256 GEMM's blocks (one per CU) each take
+    several (row tile, column block) items in turn (the load stream continues from one item into
+    the next), and the shared expert's 64 row tiles run in several chunks of row tiles. Routing
+    and permutation in full, output rows sampled."""
+    spec = synth.spec("tiny", T=16384, D=256, E=16, K=2, F=512, Fs=512, dtype="bf16", seed=21)
+    L = device_layer(spec)
+    cfg = moe.config_for(spec, packed=True)
+    P = moe.pack_layer(L)
+    out, idx, prob, offs = moe.layer_forward(cfg, L["x"], P, routing=True)
+    torch.cuda.synchronize()
+    W = oracle_weights(L)
+    x_host = L["x"].cpu()
+    ref = O.route(x_host, W.router, spec.K, W.bias)
+    compare_routing(to_host(idx), to_host(prob), ref, x_host, W.router)
+    p_ref = O.permute(to_host(idx), spec.E)
+    assert np.array_equal(to_host(offs).astype(np.int64), p_ref["offsets"])
+    counts = np.diff(p_ref["offsets"])
+    rows_per_group = (spec.T * spec.K + spec.T) / (spec.E + 1)
+    assert rows_per_group >= 96 and counts.max() > 256  # 256-row tiles, groups of several tiles
+    rows = sample_rows(spec.T, 24, 77)
+    rows = rows[ref["gap"][rows] >= 1e-6]
+    rr = O.layer_rows(x_host, W, spec.K, rows)
+    cfg_rows = moe.config_for(spec)  # the fp32-output rerun inside check_outputs uses row-major weights
+    c32, c16 = check_outputs(spec, cfg_rows, L, out, rr["out_rows"], rows)
+    print(f"many items: rows={len(rows)} out_rel(before cast)={c32['rel']:.3e} out_rel(output)={c16['rel']:.3e}")
+
+
 def test_stage_permutation_full_prefill():
     """Standalone moe_permute at the prefill size equals the oracle's permutation exactly."""
     spec = synth.spec("prefill")
