@@ -79,6 +79,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="token-count sweep T = 1 .. 16384 at the decode/prefill shape (one JSON line per T)")
     ap.add_argument("--layout", default="packed", choices=["packed", "rows"],
                     help="weight layout the timed steps read (bf16 layers; converted once before timing)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -132,7 +134,7 @@ def layer_flops_bytes(spec, counts):
 
 def gate_up_kernel(rows: int, groups: int) -> str:
     """Name of the gate/up kernel the library picks for `rows` rows over `groups` groups (bf16)."""
-    if rows <= 32 * groups:
+    if rows <= 24 * groups:  # thresholds as gemm_block_rows
         return "gemm_bf16_mfma<EPI_SWIGLU>, 32-row tiles"
     if rows >= 96 * groups:
         return "gemm_bf16_big<EPI_SWIGLU>, 256x256 tiles"
@@ -207,6 +209,52 @@ def measure(spec, steps, warmup, flush_on, packed=True):
     return res
 
 
+SWEEP_T = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384]
+
+
+def tile_kernel(T, spec):
+    """Row tiles the expert GEMMs use for T tokens (mean rows per group decides), as the library picks."""
+    rows, groups = T * spec.K + (T if spec.Fs == spec.F else 0), spec.E + (1 if spec.Fs == spec.F else 0)
+    return 32 if rows <= 24 * groups else (256 if rows >= 96 * groups else 128)  # as gemm_block_rows
+
+
+def sweep(steps, warmup, flush_on):
+    """Token-count sweep of the layer at the decode/prefill shape (same weights): one JSON line per T."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import synth
+    import top_routed_expert_amd as moe
+
+    base = synth.spec("prefill", T=max(SWEEP_T))
+    L = synth.make_layer(base, "cuda")
+    cfg = moe.config_for(base, packed=True)
+    W = moe.pack_layer(L)
+    dev = L["x"].device
+    ws = moe.Workspace(cfg, max(SWEEP_T), dev)
+    wt = moe.weights_struct(cfg, W)
+    flush = Flusher(flush_on)
+    for T in SWEEP_T:
+        spec = dataclasses.replace(base, T=T)
+        x = L["x"][:T]
+        out = torch.empty((T, base.D), dtype=cfg.odtype, device=dev)
+        ms, _ = timed(lambda: moe.layer_forward(cfg, x, W, out=out, workspace=ws, weights=wt), steps, warmup, flush)
+        ms_step = float(np.mean(ms))
+        idx, _ = moe.route(cfg, x, W["w_router"], L["bias"])
+        offs, _, _ = moe.permute(cfg, idx)
+        counts = np.diff(offs.cpu().numpy())
+        flops, nbytes, touched = layer_flops_bytes(spec, counts)
+        print(json.dumps({"T": T, "ms_per_step": round(ms_step, 5), "ms_min": round(float(np.min(ms)), 5),
+                          "tokens_per_s": round(T / (ms_step * 1e-3), 1),
+                          "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+                          "mfma_frac": round(flops / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "gbs": round(nbytes / (ms_step * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(nbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "experts_touched": touched, "tile_rows": tile_kernel(T, spec)}), flush=True)
+
+
 def cpu_baseline(spec, L, n_tokens: int):
     """The oracle, as it stands, on the first n_tokens tokens of the workload (single thread)."""
     import numpy as np
@@ -246,6 +294,11 @@ def main():
 
     import synth
 
+    if args.sweep:
+        print(f"[bench] token-count sweep {SWEEP_T} at the prefill shape, steps={args.steps} warmup={args.warmup}",
+              file=sys.stderr, flush=True)
+        sweep(args.steps, args.warmup, not args.no_flush)
+        return
     spec = synth.spec(args.workload)
     print(f"[bench] workload={spec.name} T={spec.T} steps={args.steps} warmup={args.warmup}", file=sys.stderr,
           flush=True)

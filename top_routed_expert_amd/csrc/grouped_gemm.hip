@@ -29,6 +29,12 @@
 #ifndef MOE_DN_NW_SMALL
 #define MOE_DN_NW_SMALL 1  // 16-column tiles per wave, down projection, 32-row tiles
 #endif
+#ifndef MOE_ROWS_32
+#define MOE_ROWS_32 24  // mean rows per group up to which expert GEMMs use 32-row tiles (above ~24, many groups would need two)
+#endif
+#ifndef MOE_ROWS_256
+#define MOE_ROWS_256 96  // mean rows per group from which they use the 256 x 256 kernel
+#endif
 #ifndef MOE_NS_LARGE
 #define MOE_NS_LARGE 4  // pipeline depth of the 128-row tiles
 #endif
@@ -389,8 +395,8 @@ __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __rest
 
 int gemm_block_rows(bool fast, int64_t rows, int n_groups, bool allow_big) {
   if (!fast) return 64;
-  if (rows <= 32 * (int64_t)n_groups) return 32;
-  return allow_big && rows >= 96 * (int64_t)n_groups ? 256 : 128;
+  if (rows <= MOE_ROWS_32 * (int64_t)n_groups) return 32;
+  return allow_big && rows >= MOE_ROWS_256 * (int64_t)n_groups ? 256 : 128;
 }
 
 int router_ksplit(bool fast, int64_t T, int Kdim) {
