@@ -138,7 +138,7 @@ def gate_up_kernel(rows: int, groups: int) -> str:
         return "gemm_bf16_mfma<EPI_SWIGLU>, 32-row tiles"
     if rows >= 96 * groups:
         return "gemm_bf16_big<EPI_SWIGLU>, 256x256 tiles"
-    return "gemm_bf16_mfma<EPI_SWIGLU>, 128-row tiles"
+    return "gemm_bf16_mfma<EPI_SWIGLU>, %d-row tiles" % (64 if rows <= 48 * groups else 128)
 
 
 def measure(spec, steps, warmup, flush_on, packed=True):
@@ -215,7 +215,9 @@ SWEEP_T = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384]
 def tile_kernel(T, spec):
     """Row tiles the expert GEMMs use for T tokens (mean rows per group decides), as the library picks."""
     rows, groups = T * spec.K + (T if spec.Fs == spec.F else 0), spec.E + (1 if spec.Fs == spec.F else 0)
-    return 32 if rows <= 24 * groups else (256 if rows >= 96 * groups else 128)  # as gemm_block_rows
+    if rows <= 24 * groups:  # thresholds as gemm_block_rows
+        return 32
+    return 256 if rows >= 96 * groups else (64 if rows <= 48 * groups else 128)
 
 
 def sweep(steps, warmup, flush_on):

@@ -22,9 +22,9 @@ pytestmark = pytest.mark.gpu
 
 # Small layers that the oracle finishes in seconds; they span several row and
 # column tiles with ragged tails and exercise every kernel variant:
-#   bf16 fast path with 256-row tiles (many rows per expert), 128-row tiles
-#   and 32-row tiles (few rows per expert; also with the shared expert fused
-#   as one more group spanning two tiles), the generic path (fp32, or widths not multiple of
+#   bf16 fast path with 256-row tiles (many rows per expert), 128-, 64- and
+#   32-row tiles (few rows per expert; also with the shared expert fused as
+#   one more group spanning two tiles), the generic path (fp32, or widths not multiple of
 #   64), a shared expert of another width (not fused), no shared expert,
 #   fp32 output, K = E, a single expert.
 SMALL = {
@@ -32,6 +32,7 @@ SMALL = {
     "bf16_tiles128": synth.spec("tiny", T=300, D=512, E=16, K=4, F=256, Fs=256, dtype="bf16", seed=1),
     "bf16_tiles32": synth.spec("tiny", T=37, D=256, E=16, K=6, F=192, Fs=128, dtype="bf16", seed=2),
     "bf16_tiles32_fused": synth.spec("tiny", T=37, D=256, E=64, K=6, F=192, Fs=192, dtype="bf16", seed=9),
+    "bf16_tiles64": synth.spec("tiny", T=150, D=256, E=16, K=4, F=192, Fs=192, dtype="bf16", seed=10),
     "bf16_tiles256": synth.spec("tiny", T=600, D=512, E=8, K=2, F=320, Fs=320, dtype="bf16", seed=8),
     "bf16_generic_widths": synth.spec("tiny", T=50, D=200, E=12, K=3, F=72, Fs=72, dtype="bf16", seed=3),
     "bf16_no_shared": synth.spec("tiny", T=129, D=384, E=24, K=8, F=128, Fs=0, dtype="bf16", seed=4),

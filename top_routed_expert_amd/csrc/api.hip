@@ -126,12 +126,14 @@ PermuteWs carve_permute(Arena& a, const moe_config* c, int64_t T) {
 struct SchedWs {
   Tile* tiles;
   int32_t* n_tiles;
+  bool fast;  // bf16 matrix-core kernels (else the generic 64 x 64 kernel)
   int block_rows;
   int32_t max_tiles;
 };
 SchedWs carve_sched(Arena& a, const moe_config* c, int n_groups, int64_t n_rows, int d_ff) {
   SchedWs w;
-  w.block_rows = gemm_block_rows(fast_path(c->dtype, c->d_model, d_ff), n_rows, n_groups, true);
+  w.fast = fast_path(c->dtype, c->d_model, d_ff);
+  w.block_rows = gemm_block_rows(w.fast, n_rows, n_groups, true);
   w.max_tiles = (int32_t)gemm_max_tiles(n_rows, n_groups, w.block_rows);
   w.tiles = a.take<Tile>(w.max_tiles);
   w.n_tiles = a.take<int32_t>(1);
@@ -205,7 +207,7 @@ moe_status run_route(const moe_config* c, int64_t T, const void* x, const void* 
   g.b_reuse = 1;
   g.ksplit = route_ksplit(c, T);
   g.slice_stride = T * c->n_experts;
-  MOE_TRY_HIP(launch_grouped_gemm(c->dtype, EPI_F32, BM, g, s), "router linear layer");
+  MOE_TRY_HIP(launch_grouped_gemm(c->dtype, fast, EPI_F32, BM, g, s), "router linear layer");
   MOE_TRY_HIP(launch_topk(ws.logits, g.ksplit, T, c->n_experts, c->top_k, idx, prob, gap, s), "router top-k");
   return MOE_OK;
 }
@@ -248,7 +250,7 @@ moe_status run_gate_up(const moe_config* c, const SchedWs& ws, bool build, int n
   g.out = h;
   g.ldo = d_ff;
   g.b_packed = packed(c);
-  MOE_TRY_HIP(launch_grouped_gemm(c->dtype, EPI_SWIGLU, ws.block_rows, g, s), "expert gate/up projection");
+  MOE_TRY_HIP(launch_grouped_gemm(c->dtype, ws.fast, EPI_SWIGLU, ws.block_rows, g, s), "expert gate/up projection");
   return MOE_OK;
 }
 
@@ -268,7 +270,7 @@ moe_status run_down(const moe_config* c, const SchedWs& ws, bool build, int n_gr
   g.out = y;
   g.ldo = c->d_model;
   g.b_packed = packed(c);
-  MOE_TRY_HIP(launch_grouped_gemm(c->dtype, EPI_F32, ws.block_rows, g, s), "expert down projection");
+  MOE_TRY_HIP(launch_grouped_gemm(c->dtype, ws.fast, EPI_F32, ws.block_rows, g, s), "expert down projection");
   return MOE_OK;
 }
 

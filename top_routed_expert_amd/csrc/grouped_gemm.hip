@@ -32,6 +32,9 @@
 #ifndef MOE_ROWS_32
 #define MOE_ROWS_32 24  // mean rows per group up to which expert GEMMs use 32-row tiles (above ~24, many groups would need two)
 #endif
+#ifndef MOE_ROWS_64
+#define MOE_ROWS_64 48  // ... up to which 64-row tiles (then 128-row tiles)
+#endif
 #ifndef MOE_ROWS_256
 #define MOE_ROWS_256 96  // mean rows per group from which they use the 256 x 256 kernel
 #endif
@@ -396,7 +399,8 @@ __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __rest
 int gemm_block_rows(bool fast, int64_t rows, int n_groups, bool allow_big) {
   if (!fast) return 64;
   if (rows <= MOE_ROWS_32 * (int64_t)n_groups) return 32;
-  return allow_big && rows >= MOE_ROWS_256 * (int64_t)n_groups ? 256 : 128;
+  if (allow_big && rows >= MOE_ROWS_256 * (int64_t)n_groups) return 256;
+  return rows <= MOE_ROWS_64 * (int64_t)n_groups ? 64 : 128;
 }
 
 int router_ksplit(bool fast, int64_t T, int Kdim) {
@@ -432,9 +436,9 @@ static hipError_t launch_fast(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_gemm(int dtype, int epi, int block_rows, const GemmArgs& g, hipStream_t s) {
+hipError_t launch_grouped_gemm(int dtype, bool fast, int epi, int block_rows, const GemmArgs& g, hipStream_t s) {
   if (g.max_tiles <= 0 || g.N <= 0) return hipSuccess;
-  if (block_rows == 64) {
+  if (!fast) {
     if (g.b_packed) return hipErrorInvalidValue;  // packed weights exist only on the bf16 MFMA path
     const int n_nb = (g.N + 63) / 64;
     const unsigned blocks = (unsigned)((int64_t)g.max_tiles * n_nb);
@@ -448,6 +452,10 @@ hipError_t launch_grouped_gemm(int dtype, int epi, int block_rows, const GemmArg
     return hipGetLastError();
   }
   if (block_rows == 256) return launch_grouped_gemm_big(epi, g, s);
+  if (block_rows == 64) {
+    if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 4, 2, MOE_NS_SMALL>(g, s);
+    return launch_fast<EPI_F32, 4, 2, MOE_NS_SMALL>(g, s);
+  }
   const bool narrow = g.N <= 512;  // router-sized outputs: 64 columns per block
   if (block_rows == 32) {
     if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 2, MOE_GU_NW_SMALL, MOE_NS_SMALL>(g, s);

@@ -96,15 +96,15 @@ struct GemmArgs {
 
 // Launchers (grouped_gemm.hip). `dtype` is MOE_BF16 or MOE_F32 for A/B; the
 // SwiGLU output has the same dtype; EPI_F32 output is fp32.
-// Row-tile height: 32, 128 or (expert GEMMs with many rows per group,
-// `allow_big`) 256 on the bf16 MFMA path (`fast`), 64 otherwise.
+// Row-tile height on the bf16 MFMA path (`fast`): 32, 64, 128 or (expert
+// GEMMs with many rows per group, `allow_big`) 256; 64 on the generic path.
 int gemm_block_rows(bool fast, int64_t rows, int n_groups, bool allow_big);
 // Contraction slices of the router GEMM for T tokens (1 unless T is small).
 int router_ksplit(bool fast, int64_t T, int Kdim);
 int64_t gemm_max_tiles(int64_t n_rows, int n_groups, int block_rows);
 hipError_t launch_build_tiles(const int32_t* offsets, int n_groups, int64_t n_rows, int block_rows,
                               Tile* tiles, int32_t* n_tiles, int32_t max_tiles, hipStream_t s);
-hipError_t launch_grouped_gemm(int dtype, int epi, int block_rows, const GemmArgs& g, hipStream_t s);
+hipError_t launch_grouped_gemm(int dtype, bool fast, int epi, int block_rows, const GemmArgs& g, hipStream_t s);
 // grouped_gemm_big.hip: 256 x 256 block tiles (block_rows == 256).
 hipError_t launch_grouped_gemm_big(int epi, const GemmArgs& g, hipStream_t s);
 
