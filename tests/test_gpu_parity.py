@@ -221,12 +221,21 @@ def test_layer_full_size(name, n_rows):
         assert load["skew"] > 10.0  # the Zipf-like bias makes the hottest expert >10x the mean load
 
 
-def test_layer_many_items_per_block():
+MANY_ITEMS = {
+    "d256_f512": synth.spec("tiny", T=16384, D=256, E=16, K=2, F=512, Fs=512, dtype="bf16", seed=21),
+    # the shortest contractions the 256x256 kernel takes (128: two A stages per item) and an odd
+    # number of A stages per item (192: three), so the two A slots alternate across items
+    "d128_f192": synth.spec("tiny", T=32768, D=128, E=8, K=2, F=192, Fs=192, dtype="bf16", seed=22),
+}
+
+
+@pytest.mark.parametrize("name", list(MANY_ITEMS))
+def test_layer_many_items_per_block(name):
     """Many rows per expert with narrow layers: the 256x256 GEMM's blocks (one per CU) each take
     several (row tile, column block) items in turn (the load stream continues from one item into
-    the next), and the shared expert's 64 row tiles run in several chunks of row tiles. Routing
+    the next), and the shared expert's row tiles run in several chunks of row tiles. Routing
     and permutation in full, output rows sampled."""
-    spec = synth.spec("tiny", T=16384, D=256, E=16, K=2, F=512, Fs=512, dtype="bf16", seed=21)
+    spec = MANY_ITEMS[name]
     L = device_layer(spec)
     cfg = moe.config_for(spec, packed=True)
     P = moe.pack_layer(L)

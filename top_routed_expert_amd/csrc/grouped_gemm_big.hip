@@ -21,23 +21,29 @@
 // item's operands are already in flight.
 //
 // Both operands go HBM/L2 -> LDS through direct loads (global_load_lds,
-// 16 bytes per lane, no VGPR staging) into a ring of NS = 4 stages of one
-// 32-element MFMA step each (16 KB of A + 16 KB of B per stage, 128 KB),
-// beside a 32 KB epilogue staging area. The B operand of a stage is read
-// from LDS into registers one stage ahead (two register sets) and the A
-// operand row tile by row tile in the stage itself, so the LDS reads overlap
-// the matrix-core work. Waits are explicit: a wave waits for its own loads
-// of a stage with s_waitcnt vmcnt (loads complete in issue order), then one
-// s_barrier per stage makes every wave's loads of that stage visible and
-// ends every wave's reads of the slot about to be refilled. The barrier is
-// issued as inline asm with a memory clobber: the compiler may not move
-// memory accesses across it and does not add a drain of its own.
+// 16 bytes per lane, no VGPR staging). The weights (B) stream from HBM
+// through a ring of NS = 4 stages of one 32-element MFMA step (16 KB each).
+// The gathered activation rows (A) come mostly from L2 and move in stages
+// of two MFMA steps, 128 bytes of each row (32 KB per stage, two slots):
+// a 64-byte piece of a row uses half of a 128-byte cache line, and fetching
+// whole lines raises the per-CU fetch rate of the gathered rows by about
+// 40%. With a 32 KB epilogue staging area that fills the 160 KB of LDS.
+// The B operand of a step is read from LDS into registers one step ahead
+// (two register sets) and the A operand row tile by row tile in the step
+// itself, so the LDS reads overlap the matrix-core work. Waits are
+// explicit: a wave waits for its own loads with s_waitcnt vmcnt (loads
+// complete in issue order), then one s_barrier per step makes every wave's
+// loads visible and ends every wave's reads of the slots about to be
+// refilled. The barrier is issued as inline asm with a memory clobber: the
+// compiler may not move memory accesses across it and does not add a drain
+// of its own.
 //
-// LDS rows are 64 bytes (four 16-byte chunks); chunk q of row r is stored
-// at position q ^ ((r >> 1) & 3), so the 16-byte MFMA operand reads of
-// consecutive rows spread over all banks. With packed weights (PK) each
-// 16-row group of B is one 1 KB fragment copied as it is (lane order), which
-// the operand reads take at 16 bytes per lane, conflict-free.
+// A rows in LDS are 128 bytes (eight 16-byte chunks); chunk q of row r is
+// stored at position q ^ ((r >> 1) & 7), so the 16-byte MFMA operand reads
+// of 16 consecutive rows cover all banks once. B rows without packing are
+// 64 bytes with chunk q at q ^ ((r >> 1) & 3). With packed weights (PK)
+// each 16-row group of B is one 1 KB fragment copied as it is (lane order),
+// which the operand reads take at 16 bytes per lane, conflict-free.
 #include "moe_internal.h"
 
 namespace moe {
@@ -47,8 +53,9 @@ namespace {
 #ifndef MOE_BIG_NS
 #define MOE_BIG_NS 4
 #endif
-constexpr int BIG_NS = MOE_BIG_NS;  // ring stages
-constexpr int BIG_KS = 32;     // contraction elements per stage (one MFMA step)
+constexpr int BIG_NS = MOE_BIG_NS;  // B ring stages
+constexpr int BIG_KS = 32;     // contraction elements per B stage (one MFMA step)
+constexpr int A_KS = 64;       // contraction elements per A stage (two MFMA steps)
 constexpr int BIG_ROWS = 256;  // A rows and B (weight) rows per item
 #ifndef MOE_BIG_CHUNK
 #define MOE_BIG_CHUNK 16
@@ -58,7 +65,7 @@ constexpr int CHUNK = MOE_BIG_CHUNK;  // row tiles of one group that share weigh
 // by one item only (per row tile), so it should not push the activation
 // rows, which the column blocks of a row tile share, out of L2.
 constexpr int CPOL_NT = 2;
-static_assert(BIG_NS >= 3 && BIG_NS * 32 + 32 <= 160, "ring + staging must fit 160 KB of LDS");
+static_assert(BIG_NS >= 4 && 2 * 32 + BIG_NS * 16 + 32 <= 160, "rings + staging must fit 160 KB of LDS");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -70,11 +77,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8_big(u32x4 v) { return __builtin_bit_
 // vector-memory operations and leaving the other counters unconstrained.
 constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }   // 64-byte B rows
+__device__ __forceinline__ int swzA(int row) { return (row >> 1) & 7; }  // 128-byte A rows
 
 template <int EPI, bool PK>
 __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[BIG_NS][2][BIG_ROWS * BIG_KS];
+  __shared__ __attribute__((aligned(16))) bf16_t ldsA[2][BIG_ROWS * A_KS];
+  __shared__ __attribute__((aligned(16))) bf16_t ldsB[BIG_NS][BIG_ROWS * BIG_KS];
   __shared__ __attribute__((aligned(16))) float stg[4][16 * 128];  // epilogue staging, 8 KB per wave
 
   const int BN = EPI == EPI_SWIGLU ? BIG_ROWS / 2 : BIG_ROWS;  // output columns per item
@@ -128,17 +137,20 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
     }
   };
 
-  // Direct-load sources of an item. Load instruction i (0..3) of this wave
-  // fills rows R = wave*64 + i*16 .. R+15 of a stage; lane l writes the 16
-  // bytes at LDS position (row R + l/4, physical chunk l%4), i.e. logical
-  // chunk (l%4) ^ swz(row). Rows outside the tile read row 0 (never stored).
+  // Direct-load sources of an item. A load instruction i (0..7) of this
+  // wave fills rows R = wave*64 + i*8 .. R+7 of an A stage; lane l writes
+  // the 16 bytes at LDS position (row R + l/8, physical chunk l%8), i.e.
+  // logical chunk (l%8) ^ swzA(row). B load instruction i (0..3) fills
+  // weight rows R = wave*64 + i*16 .. R+15 of a B stage: the fragment of
+  // those rows (packed) or row R + l/4, chunk (l%4) ^ swz(row) (rows).
+  // Rows outside the tile read row 0 (never stored).
   // Source rows of this wave's A loads for an item (gather read early:
   // the loads of the next item's rows are issued at the start of the
   // current item, so setting the sources inside the loop needs no load).
-  auto load_rows = [&](const Tile& t, int32_t(&rows)[4]) {
+  auto load_rows = [&](const Tile& t, int32_t(&rows)[8]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t r = (int64_t)t.row0 + wave * 64 + i * 16 + (lane >> 2);
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = (int64_t)t.row0 + wave * 64 + i * 8 + (lane >> 3);
       int64_t src = -1;
       if (r < t.row1) {
         src = r < p.n_gather ? (int64_t)p.gather[r] : r - p.n_gather;
@@ -147,9 +159,18 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
       rows[i] = (int32_t)(src >= 0 ? src : 0);
     }
   };
-  const bf16_t* asrc[4];
+  // A sources as 16-byte-unit offsets from A (the launcher checks that
+  // n_a_rows * Kdim / 8 fits in 32 bits), B sources as pointers.
+  uint32_t aoff[8];
   const bf16_t* bsrc[4];
-  auto set_sources = [&](const Tile& t, int nb, const int32_t(&rows)[4]) {
+  auto set_a_sources = [&](const int32_t(&rows)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = wave * 64 + i * 8 + (lane >> 3);
+      aoff[i] = (uint32_t)rows[i] * (uint32_t)(Kdim >> 3) + (uint32_t)((lane & 7) ^ swzA(row));
+    }
+  };
+  auto set_b_sources = [&](const Tile& t, int nb) {
     const bf16_t* Bg = t.group < p.n_main ? (const bf16_t*)p.b0 + (int64_t)t.group * p.b_stride
                                           : (const bf16_t*)p.b0_extra;
     const bf16_t* Bu = EPI == EPI_SWIGLU ? (t.group < p.n_main ? (const bf16_t*)p.b1 + (int64_t)t.group * p.b_stride
@@ -159,7 +180,6 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
     for (int i = 0; i < 4; ++i) {
       const int row = wave * 64 + i * 16 + (lane >> 2);
       const int q = (lane & 3) ^ swz(row);
-      asrc[i] = A + (int64_t)rows[i] * Kdim + q * 8;
       // weight row `row` of the item
       int col;
       const bf16_t* base;
@@ -184,15 +204,17 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
     }
   };
 
-  auto issue_stage = [&](int slot, int ks) {
-    const int koff = ks * BIG_KS;
+  auto issue_a = [&](int slot, int ja) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + koff),
-                                       (lds_void_t*)&lds[slot][0][(wave * 64 + i * 16) * BIG_KS], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + (PK ? ks * PACKED_FRAG : koff)),
-                                       (lds_void_t*)&lds[slot][1][(wave * 64 + i * 16) * BIG_KS], 16, 0, CPOL_NT);
-    }
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(A + (uint64_t)aoff[i] * 8u + ja * A_KS),
+                                       (lds_void_t*)&ldsA[slot][(wave * 64 + i * 8) * A_KS], 16, 0, 0);
+  };
+  auto issue_b = [&](int slot, int ks) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + (PK ? ks * PACKED_FRAG : ks * BIG_KS)),
+                                       (lds_void_t*)&ldsB[slot][(wave * 64 + i * 16) * BIG_KS], 16, 0, CPOL_NT);
   };
 
   // wave (wm, wn): rows wm*128 .., weight rows wn*128 ..
@@ -201,30 +223,34 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
 
   // operand read of lane (r = lane & 15, q = lane >> 4) from a 16-row tile.
   // LDS byte offsets of this lane's operand chunks inside a slot: the row
-  // swizzle depends on the row modulo 8 only, so row tile m (n) is the
-  // first one's offset + 1024 m (n), an immediate of the read instruction.
+  // swizzles depend on the row modulo 16 only, so A row tile m is the first
+  // one's offset + 2048 m and B row tile n the first one's + 1024 n, an
+  // immediate of the read instruction. The two MFMA steps of an A stage read
+  // logical chunks q and q + 4 of a row.
   const int rq = lane >> 4, rr = lane & 15;
-  const uint32_t aoff0 = (uint32_t)((wm * 128 + rr) * BIG_KS + ((rq ^ swz(wm * 128 + rr)) << 3)) * 2u;
-  const uint32_t boff0 = PK ? (uint32_t)(BIG_ROWS * BIG_KS + wn * 128 * BIG_KS) * 2u + (uint32_t)lane * 16u
-                            : (uint32_t)(BIG_ROWS * BIG_KS + (wn * 128 + rr) * BIG_KS + ((rq ^ swz(wn * 128 + rr)) << 3)) * 2u;
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)&lds[0][0][0];
-  constexpr uint32_t SLOT_BYTES = 2u * BIG_ROWS * BIG_KS * 2u;
+  const uint32_t aoffA0 = (uint32_t)((wm * 128 + rr) * A_KS + ((rq ^ swzA(rr)) << 3)) * 2u;
+  const uint32_t aoffA1 = (uint32_t)((wm * 128 + rr) * A_KS + (((rq + 4) ^ swzA(rr)) << 3)) * 2u;
+  const uint32_t boff0 = PK ? (uint32_t)(wn * 128 * BIG_KS) * 2u + (uint32_t)lane * 16u
+                            : (uint32_t)((wn * 128 + rr) * BIG_KS + ((rq ^ swz(wn * 128 + rr)) << 3)) * 2u;
+  const uint32_t ldsA_base = (uint32_t)(uintptr_t)(lds_void_t*)&ldsA[0][0];
+  const uint32_t ldsB_base = (uint32_t)(uintptr_t)(lds_void_t*)&ldsB[0][0];
+  constexpr uint32_t SLOT_A = BIG_ROWS * A_KS * 2u, SLOT_B = BIG_ROWS * BIG_KS * 2u;
   // Operand reads are inline ds_read_b128: the compiler cannot prove they do
   // not alias the direct loads in flight and would otherwise drain every
   // load before each read.
   auto read_b = [&](int slot, u32x4(&b)[8]) {
-    const uint32_t addr = lds_base + (uint32_t)slot * SLOT_BYTES + boff0;
+    const uint32_t addr = ldsB_base + (uint32_t)slot * SLOT_B + boff0;
     // (explicit captures: clang does not capture names used only as asm operands)
     static_for<0, 8>([&b, addr](auto N) {
       constexpr int n = decltype(N)::value;
       asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(b[n]) : "v"(addr), "n"(n * 1024));
     });
   };
-  auto read_a = [&](int slot, u32x4(&a)[8]) {
-    const uint32_t addr = lds_base + (uint32_t)slot * SLOT_BYTES + aoff0;
+  auto read_a = [&](int slot, int sub, u32x4(&a)[8]) {
+    const uint32_t addr = ldsA_base + (uint32_t)slot * SLOT_A + (sub ? aoffA1 : aoffA0);
     static_for<0, 8>([&a, addr](auto M) {
       constexpr int m = decltype(M)::value;
-      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(a[m]) : "v"(addr), "n"(m * 1024));
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(a[m]) : "v"(addr), "n"(m * 2048));
     });
   };
   // Row tile m multiplies as soon as its A chunk is in: LDS reads complete in
@@ -310,51 +336,67 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
     }
   };
 
-  // The ring holds stages in one sequence running across this block's
-  // items: global stage s (item j, stage k: s = j*nk + k) lives in slot
-  // s % NS. While stage k of the current item is multiplied the ring holds
-  // stages k .. k+NS-1 of the sequence (landed or in flight); the B operand
-  // is read one stage ahead (two register sets), the A operand in the stage
-  // that uses it. After the last item, stages past its end re-load its last
-  // stage (never multiplied), so every iteration issues the same 8 direct
-  // loads per wave and one fixed wait count holds.
+  // Each ring holds stages in one sequence running across this block's
+  // items. B: global step s (item j, step k: s = j*nk + k) lives in slot
+  // s % NS; while step k of the current item is multiplied the B ring holds
+  // steps k .. k+NS-1 (landed or in flight). A: global A stage (item j,
+  // stage h: j*nk/2 + h, covering steps 2h and 2h+1) lives in slot
+  // (stage % 2); while stage h is multiplied stage h+1 is in flight. The B
+  // operand is read one step ahead (two register sets), the A operand in the
+  // step that uses it. After the last item, stages past its end re-load its
+  // last stage (never multiplied), so every trip issues the same loads and
+  // fixed wait counts hold.
   //
-  // Iteration k: (1) wait until this wave's loads of stage k+1 have landed
-  // (at most the NS-3 younger stages outstanding); (2) lgkmcnt(0) + barrier:
-  // every wave's stage k+1 is visible, and every wave has finished reading
-  // stage k-1, so (3) its slot is refilled with stage k+NS-1 (of this item,
-  // else of the next one); (4) the A chunks of stage k and then the B chunks
-  // of stage k+1 are read from LDS while (5) the matrix cores multiply stage
-  // k.
+  // Step k: (1) wait until this wave's loads of B step k+1 (and, for even
+  // k, of A stage k/2) have landed; (2) lgkmcnt(0) + barrier: every wave's
+  // loads are visible and every wave has finished reading B step k-1 (and,
+  // for even k, A stage k/2-1), so (3) those slots are refilled: for even k
+  // A stage k/2+1 (8 loads per lane), then B step k+NS-1 (4 loads), of this
+  // item or else of the next one; (4) the A chunks of step k and then the
+  // B chunks of step k+1 are read from LDS while (5) the matrix cores
+  // multiply step k. Loads issued in order per wave: even step k: A(k/2+1),
+  // B(k+3); odd step: B(k+3). At even k the loads younger than those waited
+  // for are B(k+2) (4); at odd k, A(k/2+1) and B(k+2) of step k-1 (12).
+  static_assert(BIG_NS == 4, "the wait counts below assume a four-step B ring");
+  const int nh = nk >> 1;  // A stages per item
   Tile t_cur, t_next;
   int nb_cur, nb_next;
-  int32_t rows[4];
+  int32_t rows[8];
   map_item(L, t_cur, nb_cur);
   load_rows(t_cur, rows);
-  set_sources(t_cur, nb_cur, rows);
+  set_a_sources(rows);
+  set_b_sources(t_cur, nb_cur);
   int L_next = L + L_step;
   bool has_next = L_next < L_end;
   if (has_next) {
     map_item(L_next, t_next, nb_next);
     load_rows(t_next, rows);
   }
-  int base = 0;  // slot of the current item's stage 0
-  const int last = nk - 1;
+  int baseA = 0, baseB = 0;  // slots of the current item's first A stage and first B step
+  const int lastA = nh - 1, lastB = nk - 1;
   u32x4 a[8], b0[8], b1[8];
+  issue_a(0, 0);
 #pragma unroll
-  for (int s = 0; s < BIG_NS - 1; ++s) issue_stage(s, s < nk ? s : last);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * (BIG_NS - 2)));
+  for (int s = 0; s < BIG_NS - 1; ++s) issue_b(s, s);  // nk >= 4: steps 0..2 exist
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));             // A stage 0, B step 0
   asm volatile("s_barrier" ::: "memory");
   read_b(0, b0);
-  auto iteration = [&](int k, const u32x4(&b_cur)[8], u32x4(&b_next)[8]) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(8 * (BIG_NS - 3)));
+  auto step = [&](int k, auto ODD, const u32x4(&b_cur)[8], u32x4(&b_next)[8]) {
+    constexpr bool odd = decltype(ODD)::value;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(odd ? 12 : 4));
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    const int ks = k + BIG_NS - 1;  // stage of the sequence to issue, counted from this item's start
-    if (ks == nk && has_next) set_sources(t_next, nb_next, rows);  // from here on the next item's stages
-    issue_stage((base + ks) % BIG_NS, ks < nk ? ks : (has_next ? ks - nk : last));
-    read_a((base + k) % BIG_NS, a);
-    read_b((base + k + 1) % BIG_NS, b_next);
+    const int h = k >> 1;
+    if constexpr (!odd) {
+      const int ha = h + 1;  // A stage to issue, counted from this item's start
+      if (ha == nh && has_next) set_a_sources(rows);  // from here on the next item's A stages
+      issue_a((baseA + ha) & 1, ha < nh ? ha : (has_next ? ha - nh : lastA));
+    }
+    const int ks = k + BIG_NS - 1;  // B step to issue, counted from this item's start
+    if (ks == nk && has_next) set_b_sources(t_next, nb_next);
+    issue_b((baseB + ks) % BIG_NS, ks < nk ? ks : (has_next ? ks - nk : lastB));
+    read_a((baseA + h) & 1, odd ? 1 : 0, a);
+    read_b((baseB + k + 1) % BIG_NS, b_next);
     multiply(a, b_cur);
   };
   for (;;) {
@@ -362,16 +404,18 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
     for (int m = 0; m < 8; ++m)
 #pragma unroll
       for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // nk is even (the contraction is a multiple of 64): two stages per trip,
-    // alternating the B register sets; every item starts with b0.
+    // nk is even (the contraction is a multiple of 64): one A stage, two
+    // steps per trip, alternating the B register sets; every item starts
+    // with b0.
 #pragma unroll 1
     for (int k = 0; k < nk; k += 2) {
-      iteration(k, b0, b1);
-      iteration(k + 1, b1, b0);
+      step(k, std::false_type{}, b0, b1);
+      step(k + 1, std::true_type{}, b1, b0);
     }
     epilogue(t_cur, nb_cur);
     if (!has_next) break;
-    base = (base + nk) % BIG_NS;
+    baseA = (baseA + nh) & 1;
+    baseB = (baseB + nk) % BIG_NS;
     t_cur = t_next;
     nb_cur = nb_next;
     L_next += L_step;
@@ -392,7 +436,10 @@ int g_cus = 0;  // compute units of the device (queried once)
 
 hipError_t launch_grouped_gemm_big(int epi, const GemmArgs& g, hipStream_t s) {
   if (g.max_tiles <= 0 || g.N <= 0) return hipSuccess;
-  if (g.Kdim % (2 * BIG_KS)) return hipErrorInvalidValue;  // the main loop takes two stages per trip
+  // the main loop takes one A stage (two steps) per trip; the B ring's
+  // hand-over to the next item needs at least NS - 1 steps per item
+  if (g.Kdim % A_KS || g.Kdim < 2 * A_KS) return hipErrorInvalidValue;
+  if ((uint64_t)g.n_a_rows * (uint64_t)g.Kdim / 8u > 0xffffffffull) return hipErrorInvalidValue;  // 32-bit A offsets
   if (g.N % 8 || g.ldo % 8) return hipErrorInvalidValue;    // the epilogue stores 8 bf16 / 4 fp32 columns at once
   if (g_cus == 0) {
     int dev = 0, cus = 0;
