@@ -202,7 +202,9 @@ moe_status run_route(const moe_config* c, int64_t T, const void* x, const void* 
   g.N = c->n_experts;
   g.Kdim = c->d_model;
   g.dense_rows = T;
-  const int BM = gemm_block_rows(fast, T, 1, false);
+  // the router is one group read by every row tile: up to 32 tokens take
+  // one 32-row tile, more follow the expert GEMMs' rule
+  const int BM = fast && T <= 32 ? 32 : gemm_block_rows(fast, T, 1, false);
   g.max_tiles = (int32_t)((T + BM - 1) / BM);
   g.out = ws.logits;
   g.ldo = c->n_experts;

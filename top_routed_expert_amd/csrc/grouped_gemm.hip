@@ -452,11 +452,11 @@ hipError_t launch_grouped_gemm(int dtype, bool fast, int epi, int block_rows, co
     return hipGetLastError();
   }
   if (block_rows == 256) return launch_grouped_gemm_big(epi, g, s);
+  const bool narrow = g.N <= 512;  // router-sized outputs: 64 columns per block
   if (block_rows == 64) {
     if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 4, 2, MOE_NS_SMALL>(g, s);
-    return launch_fast<EPI_F32, 4, 2, MOE_NS_SMALL>(g, s);
+    return narrow ? launch_fast<EPI_F32, 4, 1, MOE_NS_SMALL>(g, s) : launch_fast<EPI_F32, 4, 2, MOE_NS_SMALL>(g, s);
   }
-  const bool narrow = g.N <= 512;  // router-sized outputs: 64 columns per block
   if (block_rows == 32) {
     if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 2, MOE_GU_NW_SMALL, MOE_NS_SMALL>(g, s);
     return narrow ? launch_fast<EPI_F32, 2, 1, MOE_NS_SMALL>(g, s)
