@@ -1,0 +1,115 @@
+"""Bounds check of the 256x256 expert GEMM without a GPU.
+
+The kernel source (top_routed_expert_amd/csrc/grouped_gemm_big.hip) is turned
+into host C++: HIP keywords and builtins become plain functions (tests/emul/
+shim.h), the inline-asm LDS reads become checked reads, the kernel launches
+become loops that run every lane of every block in turn. tests/emul/driver.cpp
+builds the launch arguments the way the library does, with exact-size buffers,
+and the whole thing runs under AddressSanitizer: any global load, store or
+table read outside its buffer, or any LDS access outside its array, fails the
+run. The matrix-core arithmetic is not emulated (the GPU parity tests cover the
+values); this test covers the index arithmetic, at shapes that take the
+multi-item hand-over, the chunked order of multi-tile groups, odd A-stage counts
+and the shortest contraction the kernel accepts.
+"""
+from __future__ import annotations
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "top_routed_expert_amd", "csrc")
+EMUL = os.path.join(ROOT, "tests", "emul")
+
+
+def _clang() -> str | None:
+    for cand in ("/opt/rocm/llvm/bin/clang++", shutil.which("clang++")):
+        if cand and os.path.exists(cand):
+            return cand
+    return None
+
+
+def host_source(kernel_src: str) -> str:
+    """The kernel source rewritten for the host build (see the module docstring)."""
+    s = kernel_src.replace('#include "moe_internal.h"', '#include "emul_internal.h"')
+    s = s.replace("typedef __attribute__((address_space(3))) void lds_void_t;", "typedef void lds_void_t;")
+    s, k0 = re.subn(r"\(uint32_t\)\(uintptr_t\)\(lds_void_t\*\)&(\w+)\[0\]\[0\]",
+                    lambda m: f"emul_lds_base((void*)&{m.group(1)}, sizeof({m.group(1)}))", s)
+    s, k1 = re.subn(r'asm volatile\("ds_read_b128 %0, %1 offset:%2" : "=v"\(([^)]*)\) : "v"\((\w+)\), '
+                    r'"n"\(([^)]*)\)\);',
+                    lambda m: (f"{m.group(1)} = emul_ds_read<std::remove_reference_t<decltype({m.group(1)})>>"
+                               f"({m.group(2)} + ({m.group(3)}));"), s)
+    s, _ = re.subn(r'asm volatile\("s_waitcnt lgkmcnt\(%1\)" : "\+v"\([^)]*\) : "n"\([^)]*\)\);', ";", s)
+    s, _ = re.subn(r'asm volatile\("[^"]*" ::: "memory"\);', ";", s)
+    s, k4 = re.subn(r"(gemm_bf16_big<[^>]*>)<<<\(unsigned\)blocks, 256, 0, s>>>\(g\);",
+                    lambda m: f"emul_launch({m.group(1)}, (unsigned)blocks, g);", s)
+    left = re.findall(r"asm volatile.*|<<<.*>>>", s)
+    assert k0 >= 1 and k1 >= 2 and k4 == 4 and not left, (k0, k1, k4, left)
+    return s
+
+
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
+    cc = _clang()
+    if cc is None:
+        pytest.skip("clang++ with AddressSanitizer is needed")
+    d = tmp_path_factory.mktemp("emul")
+    hdr = open(os.path.join(CSRC, "moe_internal.h")).read().replace("#include <hip/hip_runtime.h>",
+                                                                    '#include "shim.h"')
+    open(d / "emul_internal.h", "w").write(hdr)
+    open(d / "emul_big.cpp", "w").write(host_source(open(os.path.join(CSRC, "grouped_gemm_big.hip")).read()))
+    exe = d / "driver"
+    cmd = [cc, "-std=c++17", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer", "-pthread",
+           "-I", str(d), "-I", EMUL, "-I", os.path.join(ROOT, "include"), os.path.join(EMUL, "driver.cpp"),
+           "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    if r.returncode != 0 and "asan" in r.stderr.lower() and "cannot find" in r.stderr.lower():
+        pytest.skip("no AddressSanitizer runtime for the host compiler")
+    assert r.returncode == 0, r.stderr[-3000:]
+    return str(exe)
+
+
+SHAPES = {
+    # several items per block for gate/up, the shortest contraction (128) and three A stages (192)
+    "multi_item_short_k": (32768, 8, 2, 128, 192, 192, 2, 0),
+    # an odd number of A stages in the down projection (320 = 5 x 64)
+    "odd_a_stages": (600, 8, 2, 512, 320, 320, 3, 0),
+    # hot experts with many row tiles (chunked order), many experts
+    "skewed": (4096, 64, 8, 512, 256, 256, 4, 1),
+    # the decode/prefill widths with fewer tokens
+    "wide": (512, 16, 8, 4096, 1280, 1280, 5, 0),
+}
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_big_gemm_accesses_stay_in_bounds(driver, name):
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0")
+    r = subprocess.run([driver, *map(str, SHAPES[name])], capture_output=True, text=True, timeout=600, env=env)
+    assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-4000:])
+    assert r.stdout.count(" ok") == 4, r.stdout
+
+
+def test_planted_offset_is_caught(driver, tmp_path):
+    """The check itself: an A row offset one row too far must be reported."""
+    src = open(os.path.join(CSRC, "grouped_gemm_big.hip")).read()
+    planted = src.replace("aoff[i] = (uint32_t)rows[i] * (uint32_t)(Kdim >> 3)",
+                          "aoff[i] = (uint32_t)(rows[i] + 1) * (uint32_t)(Kdim >> 3)")
+    assert planted != src
+    d = os.path.dirname(driver)
+    work = tmp_path / "planted"
+    work.mkdir()
+    shutil.copy(os.path.join(d, "emul_internal.h"), work / "emul_internal.h")
+    open(work / "emul_big.cpp", "w").write(host_source(planted))
+    exe = work / "driver"
+    r = subprocess.run([_clang(), "-std=c++17", "-O1", "-g", "-fsanitize=address", "-pthread", "-I", str(work),
+                        "-I", EMUL, "-I", os.path.join(ROOT, "include"), os.path.join(EMUL, "driver.cpp"), "-o",
+                        str(exe)], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0")
+    r = subprocess.run([str(exe), "600", "8", "2", "512", "320", "320", "3"], capture_output=True, text=True,
+                       timeout=300, env=env)
+    assert r.returncode != 0 and "heap-buffer-overflow" in r.stderr
