@@ -79,6 +79,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--dynamic-k", action="store_true",
+                    help="dynamic top-k (4 or 8 per token) vs fixed top-8 at decode and prefill, one JSON line each")
     ap.add_argument("--sweep", action="store_true",
                     help="token-count sweep T = 1 .. 16384 at the decode/prefill shape (one JSON line per T)")
     ap.add_argument("--layout", default="packed", choices=["packed", "rows"],
@@ -126,7 +128,8 @@ def layer_flops_bytes(spec, counts):
     T, D, E, K, F, Fs = spec.T, spec.D, spec.E, spec.K, spec.F, spec.Fs
     es = 2 if spec.dtype == "bf16" else 4
     touched = int((np.asarray(counts) > 0).sum())
-    flops = 2 * T * D * E + 2 * T * K * 3 * D * F + 2 * T * 3 * D * Fs
+    pairs = int(np.asarray(counts).sum())  # T*K, or fewer under dynamic top-k
+    flops = 2 * T * D * E + 2 * pairs * 3 * D * F + 2 * T * 3 * D * Fs
     wbytes = (touched * 3 * D * F + 3 * D * Fs + E * D) * es
     abytes = T * D * es * 2  # x in, out
     return flops, wbytes + abytes, touched
@@ -257,6 +260,44 @@ def sweep(steps, warmup, flush_on):
                           "experts_touched": touched, "tile_rows": tile_kernel(T, spec)}), flush=True)
 
 
+def dynamic_topk(steps, warmup, flush_on):
+    """Dynamic top-k (4 or 8 experts per token, seeded, about half each) against fixed top-8 at the
+    decode and prefill workloads: one JSON line per (workload, mode), whole-layer figures."""
+    import numpy as np
+    import torch
+
+    import synth
+    import top_routed_expert_amd as moe
+
+    for name in ("decode", "prefill"):
+        spec = synth.spec(name)
+        L = synth.make_layer(spec, "cuda")
+        cfg = moe.config_for(spec, packed=True)
+        W = moe.pack_layer(L)
+        del L["w_gate"], L["w_up"], L["w_down"]
+        dev = L["x"].device
+        ws = moe.Workspace(cfg, spec.T, dev)
+        wt = moe.weights_struct(cfg, W)
+        out = torch.empty((spec.T, spec.D), dtype=cfg.odtype, device=dev)
+        flush = Flusher(flush_on)
+        k_dyn = synth.dynamic_k(spec, device=dev)
+        for mode, k in (("fixed top-8", None), ("dynamic top-4/8", k_dyn)):
+            ms, _ = timed(lambda: moe.layer_forward(cfg, L["x"], W, out=out, workspace=ws, weights=wt,
+                                                    k_per_token=k), steps, warmup, flush)
+            ms_step = float(np.mean(ms))
+            idx, _ = moe.route(cfg, L["x"], W["w_router"], L["bias"], k_per_token=k)
+            offs, _, _ = moe.permute(cfg, idx)
+            counts = np.diff(offs.cpu().numpy())
+            flops, nbytes, touched = layer_flops_bytes(spec, counts)
+            print(json.dumps({"workload": name, "T": spec.T, "mode": mode, "pairs": int(counts.sum()),
+                              "ms_per_step": round(ms_step, 5), "tokens_per_s": round(spec.T / (ms_step * 1e-3), 1),
+                              "experts_touched": touched,
+                              "mfma_frac": round(flops / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "hbm_frac": round(nbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
+        del W, L, ws
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(spec, L, n_tokens: int):
     """The oracle, as it stands, on the first n_tokens tokens of the workload (single thread)."""
     import numpy as np
@@ -296,6 +337,11 @@ def main():
 
     import synth
 
+    if args.dynamic_k:
+        print(f"[bench] dynamic top-k vs fixed top-8, steps={args.steps} warmup={args.warmup}", file=sys.stderr,
+              flush=True)
+        dynamic_topk(args.steps, args.warmup, not args.no_flush)
+        return
     if args.sweep:
         print(f"[bench] token-count sweep {SWEEP_T} at the prefill shape, steps={args.steps} warmup={args.warmup}",
               file=sys.stderr, flush=True)

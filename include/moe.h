@@ -145,6 +145,22 @@ moe_status moe_route(const moe_config* cfg, int64_t T, const void* x, const void
                      const float* bias, int32_t* topk_idx, float* topk_prob, float* gap,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* Router with a per-token number of experts (dynamic top-k: page "Step3.5
+ * Flash 大模型技术深度解析", section 8.2, picks 4 experts for simple inputs
+ * and 8 for complex ones; page "Step 3.5 Flash动态稀疏MoE架构解析与优化实践",
+ * section 2.1, 2-3 for short texts and up to 8 for long ones).
+ *   k_per_token [T] int32 (device) or NULL (= moe_route): token t keeps its
+ *              k_t = k_per_token[t] most probable experts, clamped to
+ *              [0, K]; its slots j >= k_t get topk_idx -1 and topk_prob 0
+ *   gap        as moe_route, at the token's own cut: p of its k_t-th choice
+ *              minus p of the next (+inf when k_t == 0 or k_t == E)
+ * Every other argument as moe_route. moe_permute, moe_combine and the
+ * grouped expert entry points take pairs with expert -1 as "no expert":
+ * no row, dest -1, nothing added. */
+moe_status moe_route_dynamic(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                             const float* bias, const int32_t* k_per_token, int32_t* topk_idx,
+                             float* topk_prob, float* gap, void* ws, size_t ws_bytes, void* stream);
+
 /* Permutation of the T*K (token, choice) pairs into per-expert segments
  * (the grouping that lets every expert run its FFN as one dense block;
  * section 3.2.2 step 2). Pairs are taken in token-major order and kept in
@@ -223,6 +239,17 @@ moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x,
                              const moe_weights* w, void* out, int32_t* topk_idx_out,
                              float* topk_prob_out, int32_t* offsets_out, void* ws,
                              size_t ws_bytes, void* stream);
+
+/* The whole layer with a per-token number of experts (see
+ * moe_route_dynamic): k_per_token [T] int32 (device) or NULL (= fixed K).
+ * Token t's output is the shared expert plus its k_t routed experts;
+ * offsets_out[E] is the number of routed pairs. Same workspace as
+ * moe_layer_forward. */
+moe_status moe_layer_forward_dynamic(const moe_config* cfg, int64_t T, const void* x,
+                                     const moe_weights* w, const int32_t* k_per_token, void* out,
+                                     int32_t* topk_idx_out, float* topk_prob_out,
+                                     int32_t* offsets_out, void* ws, size_t ws_bytes,
+                                     void* stream);
 
 /* Static text for a status code. */
 const char* moe_status_string(moe_status s);

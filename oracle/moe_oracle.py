@@ -30,7 +30,15 @@ notes):
      are those float32 values;
   R6 no capacity limit: every (token, choice) pair is processed (dropless);
   R7 an optional per-expert router bias is added to the logits before the
-     softmax.
+     softmax;
+  R12 (numbered as in the design notes) dynamic top-k (page "Step3.5 Flash
+     大模型技术深度解析", section 8.2: 4 experts for simple inputs, 8 for
+     complex ones; page "Step 3.5 Flash动态稀疏MoE架构解析与优化实践", section
+     2.1: fewer experts for short texts, up to 8 for long ones): token t keeps
+     the first k_t of its choices in the same order (k_t clamped to [0, K]),
+     with the same unrenormalised probabilities; its remaining slots hold
+     expert -1 with probability 0 and contribute nothing; the shared expert
+     is unchanged.
 """
 from __future__ import annotations
 
@@ -66,16 +74,30 @@ def softmax(logits: np.ndarray) -> np.ndarray:
     return w / w.sum(axis=1, keepdims=True)
 
 
-def select_topk(p32: np.ndarray, k: int):
+def select_topk(p32: np.ndarray, k: int, k_per_token=None):
     """The k most probable experts per token (3.2.2, step 2; R5).
 
     Order: float32 probability descending, then expert index ascending.
     Returns (idx int32 [T,k], prob float32 [T,k], gap float64 [T]) where gap
     is p of the k-th choice minus p of the (k+1)-th (inf when k == E).
+    With k_per_token (R12), token t keeps its first k_t = clip(k_per_token[t],
+    0, k) choices; slots j >= k_t hold idx -1 and prob 0, and gap is taken at
+    k_t (inf when k_t is 0 or E).
     """
     order = np.argsort(-p32, axis=1, kind="stable")
     idx = order[:, :k].astype(np.int32)
     prob = np.take_along_axis(p32, order[:, :k], axis=1).astype(np.float32)
+    if k_per_token is not None:
+        T, E = p32.shape
+        kt = np.clip(np.asarray(k_per_token, dtype=np.int64).reshape(-1), 0, k)
+        gap = np.full(T, np.inf)
+        for t in range(T):
+            n = int(kt[t])
+            idx[t, n:] = -1
+            prob[t, n:] = 0.0
+            if 0 < n < E:
+                gap[t] = float(p32[t, order[t, n - 1]]) - float(p32[t, order[t, n]])
+        return idx, prob, gap
     if k < p32.shape[1]:
         nxt = np.take_along_axis(p32, order[:, k:k + 1], axis=1)[:, 0]
         gap = prob[:, -1].astype(np.float64) - nxt.astype(np.float64)
@@ -84,12 +106,13 @@ def select_topk(p32: np.ndarray, k: int):
     return idx, prob, gap
 
 
-def route(x, w_router, k: int, bias=None) -> dict:
-    """Router: logits -> softmax (fp64) -> float32 probabilities -> top-k."""
+def route(x, w_router, k: int, bias=None, k_per_token=None) -> dict:
+    """Router: logits -> softmax (fp64) -> float32 probabilities -> top-k
+    (top-k_t per token with k_per_token, R12)."""
     logits = router_logits(x, w_router, bias)
     p64 = softmax(logits)
     p32 = p64.astype(np.float32)
-    idx, prob, gap = select_topk(p32, k)
+    idx, prob, gap = (select_topk(p32, k) if k_per_token is None else select_topk(p32, k, k_per_token))
     return dict(logits=logits, p64=p64, p32=p32, idx=idx, prob=prob, gap=gap)
 
 
@@ -100,19 +123,23 @@ def permute(idx: np.ndarray, n_experts: int) -> dict:
 
     Pairs are taken in token-major order (t, then choice k); a stable sort on
     the expert id lays each expert's pairs out contiguously, in token order.
+    Pairs with an expert id outside [0, E) (slot without an expert, R12) get
+    no row.
       counts[e]        number of pairs routed to e
-      offsets[e]       first row of e's segment (exclusive scan), offsets[E] = T*k
+      offsets[e]       first row of e's segment (exclusive scan), offsets[E] =
+                       number of pairs with an expert (T*k without R12)
       sorted_token[r]  token of permuted row r
-      dest[t*k + j]    permuted row of pair (t, j)
+      dest[t*k + j]    permuted row of pair (t, j), -1 without an expert
     """
     T, k = idx.shape
     flat = idx.reshape(-1).astype(np.int64)
-    order = np.argsort(flat, kind="stable")
-    counts = np.bincount(flat, minlength=n_experts).astype(np.int64)
+    pairs = np.nonzero((flat >= 0) & (flat < n_experts))[0]
+    order = pairs[np.argsort(flat[pairs], kind="stable")]
+    counts = np.bincount(flat[pairs], minlength=n_experts).astype(np.int64)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
     sorted_token = (order // k).astype(np.int64)
-    dest = np.empty(T * k, dtype=np.int64)
-    dest[order] = np.arange(T * k)
+    dest = np.full(T * k, -1, dtype=np.int64)
+    dest[order] = np.arange(len(order))
     return dict(counts=counts, offsets=offsets, sorted_token=sorted_token, dest=dest)
 
 
@@ -159,7 +186,8 @@ def combine(ys, y_perm, dest, prob) -> np.ndarray:
     out = np.zeros((T, y_perm.shape[1])) if ys is None else as_f64(ys).copy()
     d = np.asarray(dest).reshape(T, k)
     for j in range(k):
-        out += prob[:, j:j + 1] * y_perm[d[:, j]]
+        ok = d[:, j] >= 0                 # pairs without an expert add nothing (R12)
+        out[ok] += prob[ok, j:j + 1] * y_perm[d[ok, j]]
     return out
 
 
@@ -191,10 +219,11 @@ class LayerWeights:
         return cls(L["w_router"], expert, shared, L.get("bias"))
 
 
-def layer_forward(x, W: LayerWeights, k: int) -> dict:
-    """The whole layer on all tokens: route, permute, experts, combine."""
+def layer_forward(x, W: LayerWeights, k: int, k_per_token=None) -> dict:
+    """The whole layer on all tokens: route, permute, experts, combine
+    (per-token expert counts with k_per_token, R12)."""
     xr = as_f64(x)
-    r = route(xr, W.router, k, W.bias)
+    r = route(xr, W.router, k, W.bias) if k_per_token is None else route(xr, W.router, k, W.bias, k_per_token)
     E = r["p32"].shape[1]
     p = permute(r["idx"], E)
     x_perm = xr[p["sorted_token"]]
@@ -205,7 +234,7 @@ def layer_forward(x, W: LayerWeights, k: int) -> dict:
     return dict(**r, **p, y_perm=y_perm, ys=ys, out=out)
 
 
-def layer_rows(x, W: LayerWeights, k: int, rows) -> dict:
+def layer_rows(x, W: LayerWeights, k: int, rows, k_per_token=None) -> dict:
     """The layer's output for selected tokens only, with routing for all tokens.
 
     Routing and the permutation are computed for every token (they are
@@ -214,20 +243,21 @@ def layer_rows(x, W: LayerWeights, k: int, rows) -> dict:
     out_rows[i] is the output of token rows[i].
     """
     xr = as_f64(x)
-    r = route(xr, W.router, k, W.bias)
+    r = route(xr, W.router, k, W.bias) if k_per_token is None else route(xr, W.router, k, W.bias, k_per_token)
     E = r["p32"].shape[1]
     p = permute(r["idx"], E)
     rows = np.asarray(rows, dtype=np.int64)
     idx = r["idx"][rows]                                  # [R, k]
     y_sel = np.zeros((len(rows), k, xr.shape[1]))
-    for e in np.unique(idx):
+    for e in np.unique(idx[idx >= 0]):      # slots without an expert stay zero (R12)
         ri, kj = np.nonzero(idx == e)
         y_sel[ri, kj] = swiglu_ffn(xr[rows[ri]], *W.expert(int(e)))
     sh = W.shared()
     out = np.zeros((len(rows), xr.shape[1])) if sh is None else swiglu_ffn(xr[rows], *sh)
     prob = as_f64(r["prob"][rows])
     for j in range(k):
-        out += prob[:, j:j + 1] * y_sel[:, j]
+        ok = idx[:, j] >= 0
+        out[ok] += prob[ok, j:j + 1] * y_sel[ok, j]
     return dict(**r, **p, rows=rows, out_rows=out)
 
 

@@ -154,7 +154,7 @@ def spec(name: str, **over) -> LayerSpec:
 
 
 # stream ids: one per tensor, one per expert matrix, so any expert regenerates alone
-TID_X, TID_ROUTER = 0, 1
+TID_X, TID_ROUTER, TID_KDYN = 0, 1, 2
 
 
 def tid_expert(e: int, which: int) -> int:
@@ -187,6 +187,19 @@ def make_expert(s: LayerSpec, e: int, device="cpu"):
     u = draw((F, s.D), s.seed, tid_expert(e, 1), 1.0 / math.sqrt(s.D), s.torch_dtype, device)
     d = draw((s.D, F), s.seed, tid_expert(e, 2), 1.0 / math.sqrt(F), s.torch_dtype, device)
     return g, u, d
+
+
+def dynamic_k(s: LayerSpec, choices=None, device="cpu") -> torch.Tensor:
+    """Per-token expert counts of a dynamic top-k run, int32 [T].
+
+    Token t takes choices[q_t % len(choices)], q_t being element t of the
+    level stream (seed, TID_KDYN). Default choices (K // 2, K): the pages'
+    simple and complex inputs (4 and 8 experts at K = 8; page "Step3.5 Flash
+    大模型技术深度解析", section 8.2), in about equal numbers.
+    """
+    choices = tuple(choices) if choices is not None else (s.K // 2, s.K)
+    q = levels(s.seed, TID_KDYN, 0, s.T, "cpu")
+    return torch.tensor(choices, dtype=torch.int32)[q % len(choices)].to(device)
 
 
 def make_layer(s: LayerSpec, device="cpu") -> dict:

@@ -107,7 +107,7 @@ def compare_routing(idx_gpu, prob_gpu, ref, x, w_router) -> dict:
     rel = dp / np.maximum(pref[keep], 1e-30)
     return dict(near_ties=int((~keep).sum()), prob_err=float(dp.max()) if dp.size else 0.0,
                 prob_rel=float(rel.max()) if rel.size else 0.0,
-                bound_use=float((dp / bound).max()) if dp.size else 0.0)
+                bound_use=float(np.max(dp / np.where(bound > 0, bound, 1.0))) if dp.size else 0.0)
 
 
 def compare_permutation(offs, st, dest, ref) -> None:

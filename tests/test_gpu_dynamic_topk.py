@@ -1,0 +1,138 @@
+"""Dynamic top-k on the GPU (moe_route_dynamic, moe_layer_forward_dynamic) against the oracle.
+
+Token t keeps its k_t most probable experts (reading R12 of the oracle); slots
+past k_t hold expert -1 with probability 0 and get no row. Small layers are
+compared in full over every kernel path (fp32 generic, bf16 32/64/128/256-row
+tiles, single-block and two-kernel permutation, fused and separate shared
+expert, no shared expert), with k_t drawn from {0, K/2, K}; the decode and
+prefill workloads with the pages' 4-or-8 split on all routing results and on
+sampled output rows. With k_t = K everywhere the dynamic entry points must
+reproduce the fixed-K ones bit for bit.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import top_routed_expert_amd as moe
+from moe_testutil import compare_bf16_out, compare_out, compare_routing, device_layer, oracle_weights, out_tol, \
+    to_host
+from oracle import moe_oracle as O
+from test_gpu_parity import SMALL, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+CASES = ["tiny", "bf16_tiles32", "bf16_tiles32_fused", "bf16_tiles64", "bf16_tiles128", "bf16_tiles256",
+         "bf16_generic_widths", "bf16_no_shared", "bf16_k_equals_e"]
+
+
+def k_draw(spec):
+    return synth.dynamic_k(spec, (0, max(1, spec.K // 2), spec.K), "cuda")
+
+
+def run_dynamic(spec, L, k, rows=None, packed=False):
+    """Layer with per-token k on the GPU; routing checked in full, output on `rows` (all if None)."""
+    cfg = moe.config_for(spec, packed=packed)
+    Lw = moe.pack_layer(L) if packed else L
+    out, idx, prob, offs = moe.layer_forward(cfg, L["x"], Lw, routing=True, k_per_token=k)
+    torch.cuda.synchronize()
+    W = oracle_weights(L)
+    kh = to_host(k)
+    x_host = L["x"].cpu()
+    ref = O.route(x_host, W.router, spec.K, W.bias, kh)
+    r = compare_routing(to_host(idx), to_host(prob), ref, x_host, W.router)
+    gi = to_host(idx)
+    assert np.array_equal(gi < 0, np.arange(spec.K)[None, :] >= np.clip(kh, 0, spec.K)[:, None]), \
+        "slots past k_t must hold -1"
+    assert np.all(to_host(prob)[gi < 0] == 0)
+    p_ref = O.permute(gi, spec.E)
+    assert np.array_equal(to_host(offs).astype(np.int64), p_ref["offsets"])
+    assert int(to_host(offs)[-1]) == int(np.clip(kh, 0, spec.K).sum())
+    keep = np.nonzero(ref["gap"] >= 1e-6)[0]
+    rows = keep if rows is None else np.intersect1d(rows, keep)
+    rr = O.layer_rows(x_host, W, spec.K, rows, kh)
+    sel = lambda a: to_host(a[torch.from_numpy(rows).to(a.device)])
+    if spec.dtype == "bf16":
+        out32 = moe.layer_forward(dataclasses.replace(cfg, out_dtype=torch.float32), L["x"], Lw, k_per_token=k)
+        c32 = compare_out(sel(out32), rr["out_rows"], 2e-2, "out (fp32 before the final cast)")
+        assert torch.equal(out, out32.to(torch.bfloat16)), "bf16 output is not the rounding of the fp32 output"
+        c16 = compare_bf16_out(sel(out), rr["out_rows"])
+    else:
+        c32 = c16 = compare_out(sel(out), rr["out_rows"], out_tol(spec))
+    return r, c32, c16
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_dynamic_topk_small(name):
+    spec = SMALL[name]
+    L = device_layer(spec)
+    r, c32, c16 = run_dynamic(spec, L, k_draw(spec))
+    print(f"{name}: near_ties={r['near_ties']} out_rel(before cast)={c32['rel']:.3e} out_rel={c16['rel']:.3e}")
+
+
+@pytest.mark.parametrize("name", ["bf16_tiles32", "bf16_tiles256", "tiny"])
+def test_dynamic_topk_with_k_everywhere_equals_fixed(name):
+    spec = SMALL[name]
+    L = device_layer(spec)
+    cfg = moe.config_for(spec)
+    k = torch.full((spec.T,), spec.K, dtype=torch.int32, device="cuda")
+    a = moe.layer_forward(cfg, L["x"], L, routing=True)
+    b = moe.layer_forward(cfg, L["x"], L, routing=True, k_per_token=k)
+    torch.cuda.synchronize()
+    for what, u, v in zip(("out", "topk_idx", "topk_prob", "offsets"), a, b):
+        assert torch.equal(u, v), f"{name}: {what} differs"
+
+
+def test_dynamic_topk_edge_counts():
+    """k_t = 0 for every token (the shared expert alone) and values outside [0, K] (clamped)."""
+    spec = SMALL["bf16_tiles32"]
+    L = device_layer(spec)
+    cfg = moe.config_for(spec)
+    zero = torch.zeros(spec.T, dtype=torch.int32, device="cuda")
+    out, idx, prob, offs = moe.layer_forward(cfg, L["x"], L, routing=True, k_per_token=zero)
+    shared = moe.grouped_ffn(cfg, torch.tensor([0, spec.T], dtype=torch.int32, device="cuda"), L["x"],
+                             L["s_gate"][None], L["s_up"][None], L["s_down"][None])
+    torch.cuda.synchronize()
+    assert torch.all(idx == -1) and torch.all(prob == 0) and int(offs[-1]) == 0
+    assert torch.equal(out, shared.to(torch.bfloat16)), "k_t = 0: output must be the shared expert's, rounded"
+    wild = torch.tensor([(-3 + 5 * t) % (spec.K + 5) - 2 for t in range(spec.T)], dtype=torch.int32, device="cuda")
+    clamped = wild.clamp(0, spec.K)
+    a = moe.layer_forward(cfg, L["x"], L, routing=True, k_per_token=wild)
+    b = moe.layer_forward(cfg, L["x"], L, routing=True, k_per_token=clamped)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_dynamic_route_gap():
+    """moe_route_dynamic alone: ids, probabilities and the gap at each token's own cut."""
+    spec = SMALL["bf16_tiles128"]
+    L = device_layer(spec)
+    cfg = moe.config_for(spec)
+    k = k_draw(spec)
+    idx, prob, gap = moe.route(cfg, L["x"], L["w_router"], L["bias"], want_gap=True, k_per_token=k)
+    torch.cuda.synchronize()
+    W = oracle_weights(L)
+    ref = O.route(L["x"].cpu(), W.router, spec.K, W.bias, to_host(k))
+    compare_routing(to_host(idx), to_host(prob), ref, L["x"].cpu(), W.router)
+    g = to_host(gap)
+    fin = np.isfinite(ref["gap"])
+    assert np.array_equal(np.isinf(g), ~fin)
+    keep = fin & (ref["gap"] >= 1e-6)
+    assert np.allclose(g[keep], ref["gap"][keep], atol=2e-7)
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_dynamic_topk_full_size(name):
+    """The pages' split (4 experts for simple inputs, 8 for complex ones) at the full workload sizes."""
+    spec = synth.spec(name)
+    print(f"dynamic top-k, full size: {name}", flush=True)
+    L = device_layer(spec)
+    k = synth.dynamic_k(spec, device="cuda")
+    rows = sample_rows(spec.T, 24, 5)
+    r, c32, c16 = run_dynamic(spec, L, k, rows, packed=True)
+    print(f"{name}: near_ties={r['near_ties']} out_rel(before cast)={c32['rel']:.3e} out_rel={c16['rel']:.3e}")

@@ -282,6 +282,75 @@ def pin_layer_special_cases():
     assert np.allclose(rr["out_rows"], base["out"][[0, 5, 11]], rtol=1e-12, atol=1e-13)
 
 
+def pin_dynamic_topk_route():
+    """R12 by brute force: token t's first k_t choices are the brute-force top-k_t, then -1 / 0."""
+    for seed, (T, D, E, K) in enumerate([(7, 4, 9, 4), (5, 6, 6, 6), (6, 3, 12, 8)]):
+        rng = np.random.default_rng(300 + seed)
+        x, wr = rng.standard_normal((T, D)), rng.standard_normal((E, D))
+        kt = rng.integers(-1, K + 2, size=T)           # out-of-range values are clamped
+        kt[0], kt[-1] = 0, K
+        r = O.route(x, wr, K, None, kt)
+        for t in range(T):
+            n = min(max(int(kt[t]), 0), K)
+            bi, bp = brute_route([x[t].tolist()], wr.tolist(), n) if n else (np.zeros((1, 0)), np.zeros((1, 0)))
+            assert np.array_equal(r["idx"][t, :n], bi[0]), (seed, t)
+            assert np.array_equal(r["prob"][t, :n], bp[0].astype(np.float32)), (seed, t)
+            assert np.all(r["idx"][t, n:] == -1) and np.all(r["prob"][t, n:] == 0), (seed, t)
+            if n == 0 or n == E:
+                assert np.isinf(r["gap"][t])
+            else:
+                _, b_next = brute_route([x[t].tolist()], wr.tolist(), n + 1)
+                assert r["gap"][t] == float(bp[0][-1]) - float(b_next[0][-1])
+
+
+def pin_dynamic_topk_permute():
+    """Pairs without an expert get no row: brute-force per-expert walk, dest -1."""
+    rng = np.random.default_rng(41)
+    for T, E, K in [(9, 5, 3), (13, 7, 4), (6, 4, 4)]:
+        idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+        kt = rng.integers(0, K + 1, size=T)
+        for t in range(T):
+            idx[t, kt[t]:] = -1
+        p = O.permute(idx, E)
+        off, st, de = brute_permute(idx, E)
+        valid = idx.reshape(-1) >= 0
+        assert np.array_equal(p["offsets"], off) and np.array_equal(p["sorted_token"], st)
+        assert np.all(p["dest"][~valid] == -1)
+        assert np.array_equal(p["dest"][valid], np.array([d for d in de if d is not None]))
+        assert p["offsets"][-1] == kt.sum() == valid.sum()
+        assert np.array_equal(np.sort(p["dest"][valid]), np.arange(valid.sum()))
+
+
+def pin_dynamic_topk_layer():
+    rng = np.random.default_rng(23)
+    T, D, E, K, F = 14, 6, 7, 4, 3
+    L = rand_layer(rng, T, D, E, K, F, F)
+    W = O.LayerWeights.from_dict(L)
+    ys = O.swiglu_ffn(L["x"], L["s_gate"], L["s_up"], L["s_down"])
+    # no routed experts at all: the shared expert alone, exactly
+    r0 = O.layer_forward(L["x"], W, K, np.zeros(T, dtype=np.int64))
+    assert np.array_equal(r0["out"], ys)
+    # a token with k_t experts gets the same output as the fixed top-k_t layer
+    kt = np.array([2, K] * (T // 2))
+    rd = O.layer_forward(L["x"], W, K, kt)
+    r2, rk = O.layer_forward(L["x"], W, 2), O.layer_forward(L["x"], W, K)
+    assert np.allclose(rd["out"][kt == 2], r2["out"][kt == 2], rtol=1e-12, atol=1e-13)
+    assert np.allclose(rd["out"][kt == K], rk["out"][kt == K], rtol=1e-12, atol=1e-13)
+    # all experts identical: out = ys + (sum of the token's k_t probabilities) FFN(x)
+    Li = dict(L, w_gate=np.repeat(L["w_gate"][:1], E, 0), w_up=np.repeat(L["w_up"][:1], E, 0),
+              w_down=np.repeat(L["w_down"][:1], E, 0))
+    kt = rng.integers(0, K + 1, size=T)
+    ri = O.layer_forward(L["x"], O.LayerWeights.from_dict(Li), K, kt)
+    f0 = O.swiglu_ffn(L["x"], L["w_gate"][0], L["w_up"][0], L["w_down"][0])
+    psum = np.array([math.fsum(float(v) for v in ri["p32"][t][np.argsort(-ri["p32"][t], kind="stable")[:kt[t]]])
+                     for t in range(T)])
+    assert np.allclose(ri["out"], ys + psum[:, None] * f0, rtol=1e-12, atol=1e-13)
+    # sampled rows agree with the full layer
+    rr = O.layer_rows(L["x"], W, K, [1, 6, 13], kt)
+    rf = O.layer_forward(L["x"], W, K, kt)
+    assert np.allclose(rr["out_rows"], rf["out"][[1, 6, 13]], rtol=1e-12, atol=1e-13)
+
+
 def pin_page_constants():
     """The page's structural numbers, and the width reading they force."""
     g = json.load(open(os.path.join(GOLDEN, "step35_layer_constants.json")))["values"]
@@ -306,7 +375,8 @@ def pin_page_constants():
 
 PINS = [pin_route_bruteforce, pin_route_ties, pin_route_properties, pin_route_bias, pin_permute,
         pin_ffn_closed_form, pin_ffn_bruteforce, pin_layer_worked_example,
-        pin_layer_special_cases, pin_page_constants]
+        pin_layer_special_cases, pin_dynamic_topk_route, pin_dynamic_topk_permute, pin_dynamic_topk_layer,
+        pin_page_constants]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -316,12 +386,14 @@ def test_pin(pin):
 
 # --------------------------------------------------------- planted mistakes ---
 
-def _renormalised(p32, k):
-    idx, prob, gap = _orig["select_topk"](p32, k)
-    return idx, (prob / prob.sum(axis=1, keepdims=True)).astype(np.float32), gap
+def _renormalised(p32, k, k_per_token=None):
+    idx, prob, gap = (_orig["select_topk"](p32, k) if k_per_token is None else
+                      _orig["select_topk"](p32, k, k_per_token))
+    tot = prob.sum(axis=1, keepdims=True)
+    return idx, np.where(tot > 0, prob / np.where(tot > 0, tot, 1), 0).astype(np.float32), gap
 
 
-def _ties_high(p32, k):
+def _ties_high(p32, k, k_per_token=None):
     E = p32.shape[1]
     order = E - 1 - np.argsort(-p32[:, ::-1], axis=1, kind="stable")
     idx = order[:, :k].astype(np.int32)
@@ -329,7 +401,7 @@ def _ties_high(p32, k):
     return idx, prob, np.zeros(p32.shape[0])
 
 
-def _softmax_after_topk(x, w_router, k, bias=None):
+def _softmax_after_topk(x, w_router, k, bias=None, k_per_token=None):
     l = O.router_logits(x, w_router, bias)
     order = np.argsort(-l, axis=1, kind="stable")[:, :k]
     top = np.take_along_axis(l, order, axis=1)
@@ -369,6 +441,8 @@ def _unstable_permute(idx, n_experts):
     for t in range(T):
         for j in range(k):
             e = idx[t, j]
+            if e < 0:
+                continue
             rows = [r for r in pos[t] if off[e] <= r < off[e + 1]]
             de[t * k + j] = rows[0]
     return dict(p, sorted_token=st, dest=de)
@@ -402,6 +476,22 @@ def _transposed_down(x_rows, w_gate, w_up, w_down):
     return h @ wd.reshape(wd.shape[1], wd.shape[0])   # plausible reshape-for-transpose slip
 
 
+def _dynamic_k_ignored(p32, k, k_per_token=None):
+    return _orig["select_topk"](p32, k)
+
+
+def _dropped_slot_kept(p32, k, k_per_token=None):
+    if k_per_token is None:
+        return _orig["select_topk"](p32, k)
+    idx, prob, gap = _orig["select_topk"](p32, k, k_per_token)
+    full, _, _ = _orig["select_topk"](p32, k)
+    return np.where(idx < 0, full, idx).astype(np.int32), prob, gap   # expert kept, weight 0
+
+
+def _no_expert_as_expert0(idx, n_experts):
+    return _orig["permute"](np.where(np.asarray(idx) < 0, 0, idx), n_experts)
+
+
 _orig = {n: getattr(O, n) for n in ("select_topk", "swiglu_ffn", "permute", "combine",
                                     "router_logits", "softmax", "silu", "route")}
 
@@ -418,6 +508,9 @@ MUTANTS = {
     "shared_expert_dropped": ("combine", _drop_shared),
     "router_bias_dropped": ("router_logits", _drop_bias),
     "down_projection_transposed": ("swiglu_ffn", _transposed_down),
+    "dynamic_k_ignored": ("select_topk", _dynamic_k_ignored),
+    "dropped_slot_keeps_expert": ("select_topk", _dropped_slot_kept),
+    "no_expert_routed_to_expert_0": ("permute", _no_expert_as_expert0),
 }
 
 

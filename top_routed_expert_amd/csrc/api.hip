@@ -178,11 +178,11 @@ LayerWs carve_layer(Arena& a, const moe_config* c, int64_t T) {
   w.perm = carve_permute(a, c, T);
   w.idx = a.take<int32_t>(P);
   w.prob = a.take<float>(P);
-  w.offsets_ext = a.take<int32_t>(c->n_experts + 2);
+  w.offsets_ext = a.take<int32_t>(c->n_experts + 3);
   w.sorted_token = a.take<int32_t>(P);
   w.dest = a.take<int32_t>(P);
   const int64_t rows = P + (w.fused_shared ? T : 0);
-  w.ffn = carve_ffn(a, c, c->n_experts + (w.fused_shared ? 1 : 0), rows, c->d_expert);
+  w.ffn = carve_ffn(a, c, c->n_experts + (w.fused_shared ? 2 : 0), rows, c->d_expert);
   if (shared && !w.fused_shared) w.ffn_shared = carve_ffn(a, c, 1, T, c->d_shared);
   w.y = a.take<float>((P + (shared ? T : 0)) * c->d_model);
   w.y_shared = shared ? w.y + P * c->d_model : nullptr;
@@ -192,7 +192,7 @@ LayerWs carve_layer(Arena& a, const moe_config* c, int64_t T) {
 // ---- launch sequences ----
 
 moe_status run_route(const moe_config* c, int64_t T, const void* x, const void* w_router, const float* bias,
-                     int32_t* idx, float* prob, float* gap, const RouteWs& ws, hipStream_t s) {
+                     const int32_t* k_tok, int32_t* idx, float* prob, float* gap, const RouteWs& ws, hipStream_t s) {
   const bool fast = fast_path(c->dtype, c->d_model, 64);
   GemmArgs g{};
   g.a = x;
@@ -214,17 +214,19 @@ moe_status run_route(const moe_config* c, int64_t T, const void* x, const void* 
   g.ksplit = route_ksplit(c, T);
   g.slice_stride = T * c->n_experts;
   MOE_TRY_HIP(launch_grouped_gemm(c->dtype, fast, EPI_F32, BM, g, s), "router linear layer");
-  MOE_TRY_HIP(launch_topk(ws.logits, g.ksplit, T, c->n_experts, c->top_k, idx, prob, gap, s), "router top-k");
+  MOE_TRY_HIP(launch_topk(ws.logits, g.ksplit, T, c->n_experts, c->top_k, k_tok, idx, prob, gap, s),
+              "router top-k");
   return MOE_OK;
 }
 
 // Row tiles of a grouped launch: from `offsets` (built on the device when
 // `build` is set), or dense rows of a single group when offsets is NULL.
 moe_status fill_tiles(GemmArgs& g, const SchedWs& ws, const int32_t* offsets, int n_groups, int64_t n_rows,
-                      bool build, hipStream_t s) {
+                      bool build, int skip_group, hipStream_t s) {
   g.ksplit = 1;
   if (offsets && build)
-    MOE_TRY_HIP(launch_build_tiles(offsets, n_groups, n_rows, ws.block_rows, ws.tiles, ws.n_tiles, ws.max_tiles, s),
+    MOE_TRY_HIP(launch_build_tiles(offsets, n_groups, n_rows, ws.block_rows, ws.tiles, ws.n_tiles, ws.max_tiles,
+                                   skip_group, s),
                 "tile schedule");
   g.tiles = offsets ? ws.tiles : nullptr;
   g.n_tiles = offsets ? ws.n_tiles : nullptr;
@@ -238,9 +240,9 @@ moe_status fill_tiles(GemmArgs& g, const SchedWs& ws, const int32_t* offsets, in
 moe_status run_gate_up(const moe_config* c, const SchedWs& ws, bool build, int n_groups, int n_main, int64_t n_rows,
                        const int32_t* offsets, const void* x, int64_t n_x_rows, const int32_t* gather,
                        int64_t n_gather, const void* w_gate, const void* w_up, const void* s_gate, const void* s_up,
-                       int d_ff, void* h, hipStream_t s) {
+                       int d_ff, void* h, hipStream_t s, int skip_group = -1) {
   GemmArgs g{};
-  MOE_TRY(fill_tiles(g, ws, offsets, n_groups, n_rows, build, s));
+  MOE_TRY(fill_tiles(g, ws, offsets, n_groups, n_rows, build, skip_group, s));
   g.a = x;
   g.n_a_rows = n_x_rows;
   g.gather = gather;
@@ -264,7 +266,7 @@ moe_status run_down(const moe_config* c, const SchedWs& ws, bool build, int n_gr
                     const int32_t* offsets, const void* h, const void* w_down, const void* s_down, int d_ff, float* y,
                     hipStream_t s) {
   GemmArgs g{};
-  MOE_TRY(fill_tiles(g, ws, offsets, n_groups, n_rows, build, s));
+  MOE_TRY(fill_tiles(g, ws, offsets, n_groups, n_rows, build, -1, s));
   g.a = h;
   g.n_a_rows = n_rows;
   g.b0 = w_down;
@@ -284,9 +286,10 @@ moe_status run_down(const moe_config* c, const SchedWs& ws, bool build, int n_gr
 moe_status run_ffn(const moe_config* c, int n_groups, int n_main, int64_t n_rows, const int32_t* offsets,
                    const void* x, int64_t n_x_rows, const int32_t* gather, int64_t n_gather, const void* w_gate,
                    const void* w_up, const void* w_down, const void* s_gate, const void* s_up, const void* s_down,
-                   int d_ff, float* y, const FfnWs& ws, hipStream_t s, bool tiles_ready = false) {
+                   int d_ff, float* y, const FfnWs& ws, hipStream_t s, bool tiles_ready = false,
+                   int skip_group = -1) {
   MOE_TRY(run_gate_up(c, ws.sched, !tiles_ready, n_groups, n_main, n_rows, offsets, x, n_x_rows, gather, n_gather,
-                      w_gate, w_up, s_gate, s_up, d_ff, ws.h, s));
+                      w_gate, w_up, s_gate, s_up, d_ff, ws.h, s, skip_group));
   MOE_TRY(run_down(c, ws.sched, false, n_groups, n_main, n_rows, offsets, ws.h, w_down, s_down, d_ff, y, s));
   return MOE_OK;
 }
@@ -368,8 +371,9 @@ size_t moe_layer_workspace_bytes(const moe_config* cfg, int64_t T) {
   return a.off;
 }
 
-moe_status moe_route(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const float* bias,
-                     int32_t* topk_idx, float* topk_prob, float* gap, void* ws, size_t ws_bytes, void* stream) {
+moe_status moe_route_dynamic(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                             const float* bias, const int32_t* k_per_token, int32_t* topk_idx, float* topk_prob,
+                             float* gap, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(check_cfg(cfg));
   MOE_TRY(check_tokens(cfg, T));
   if (T == 0) return ok();
@@ -378,13 +382,14 @@ moe_status moe_route(const moe_config* cfg, int64_t T, const void* x, const void
   if (misaligned(x) || misaligned(w_router) || misaligned(bias) || misaligned(topk_idx) || misaligned(topk_prob) ||
       misaligned(gap) || misaligned(ws))
     return fail(MOE_ERR_MISALIGNED, "moe_route: a pointer is not 16-byte aligned");
+  if (misaligned(k_per_token)) return fail(MOE_ERR_MISALIGNED, "moe_route: k_per_token is not 16-byte aligned");
   if (cfg->dtype == MOE_BF16 && cfg->d_model % 8)
     return fail(MOE_ERR_UNSUPPORTED, "bf16 rows need d_model % 8 == 0");
   const size_t need = moe_route_workspace_bytes(cfg, T);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_route needs %zu workspace bytes, got %zu", need, ws_bytes);
   Arena a(ws);
   const RouteWs w = carve_route(a, cfg, T);
-  MOE_TRY(run_route(cfg, T, x, w_router, bias, topk_idx, topk_prob, gap, w, (hipStream_t)stream));
+  MOE_TRY(run_route(cfg, T, x, w_router, bias, k_per_token, topk_idx, topk_prob, gap, w, (hipStream_t)stream));
   return ok();
 }
 
@@ -510,9 +515,10 @@ moe_status moe_combine(const moe_config* cfg, int64_t T, const float* y_perm, co
   return ok();
 }
 
-moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w, void* out,
-                             int32_t* topk_idx_out, float* topk_prob_out, int32_t* offsets_out, void* ws,
-                             size_t ws_bytes, void* stream) {
+moe_status moe_layer_forward_dynamic(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w,
+                                     const int32_t* k_per_token, void* out, int32_t* topk_idx_out,
+                                     float* topk_prob_out, int32_t* offsets_out, void* ws, size_t ws_bytes,
+                                     void* stream) {
   MOE_TRY(check_cfg(cfg));
   MOE_TRY(check_tokens(cfg, T));
   if (T == 0) return ok();
@@ -525,7 +531,8 @@ moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x, co
   if (misaligned(x) || misaligned(out) || misaligned(w->w_router) || misaligned(w->router_bias) ||
       misaligned(w->w_gate) || misaligned(w->w_up) || misaligned(w->w_down) ||
       (shared && (misaligned(w->s_gate) || misaligned(w->s_up) || misaligned(w->s_down))) ||
-      misaligned(topk_idx_out) || misaligned(topk_prob_out) || misaligned(offsets_out) || misaligned(ws))
+      misaligned(topk_idx_out) || misaligned(topk_prob_out) || misaligned(offsets_out) || misaligned(ws) ||
+      misaligned(k_per_token))
     return fail(MOE_ERR_MISALIGNED, "moe_layer_forward: a pointer is not 16-byte aligned");
   if (cfg->dtype == MOE_BF16 && (cfg->d_model % 8 || cfg->d_expert % 8 || (shared && cfg->d_shared % 8)))
     return fail(MOE_ERR_UNSUPPORTED, "bf16 rows need d_model, d_expert, d_shared multiples of 8");
@@ -542,9 +549,11 @@ moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x, co
   float* prob = topk_prob_out ? topk_prob_out : L.prob;
 
   // 1. router: linear layer + softmax over all E experts + top-K
-  MOE_TRY(run_route(cfg, T, x, w->w_router, w->router_bias, idx, prob, nullptr, L.route, s));
-  // 2. permute pairs into expert segments; the shared expert's T rows follow
-  //    them. Small batches do it, and the expert-GEMM tile table, in one block.
+  MOE_TRY(run_route(cfg, T, x, w->w_router, w->router_bias, k_per_token, idx, prob, nullptr, L.route, s));
+  // 2. permute pairs into expert segments; the shared expert's T rows start at
+  //    row T*K (pairs without an expert, under dynamic top-k, leave the rows
+  //    between the routed segments and T*K unused). Small batches do it, and
+  //    the expert-GEMM tile table, in one block.
   const int32_t extra = L.fused_shared ? (int32_t)T : 0;
   const bool small = permute_small_fits(T, K, E);
   if (small) {
@@ -559,9 +568,11 @@ moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x, co
   }
   // 3. expert FFNs: routed segments (rows gathered through sorted_token) and,
   //    when widths match, the shared expert as one more group over x itself
-  const int n_groups = E + (L.fused_shared ? 1 : 0);
+  //    (group E+1; group E, the unused rows, gets no tiles)
+  const int n_groups = E + (L.fused_shared ? 2 : 0);
   MOE_TRY(run_ffn(cfg, n_groups, E, P + extra, L.offsets_ext, x, T, L.sorted_token, P, w->w_gate, w->w_up,
-                  w->w_down, w->s_gate, w->s_up, w->s_down, cfg->d_expert, L.y, L.ffn, s, small));
+                  w->w_down, w->s_gate, w->s_up, w->s_down, cfg->d_expert, L.y, L.ffn, s, small,
+                  L.fused_shared ? E : -1));
   if (shared && !L.fused_shared) {
     MOE_TRY(run_ffn(cfg, 1, 1, T, nullptr, x, T, nullptr, 0, w->s_gate, w->s_up, w->s_down, nullptr, nullptr,
                     nullptr, cfg->d_shared, L.y_shared, L.ffn_shared, s));
@@ -569,6 +580,18 @@ moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x, co
   // 4. weighted combine: shared + sum_k prob * routed, one rounding to out_dtype
   MOE_TRY_HIP(launch_combine(cfg->out_dtype, T, D, K, L.y, P, L.dest, prob, L.y_shared, out, s), "combine");
   return ok();
+}
+
+moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w, void* out,
+                             int32_t* topk_idx_out, float* topk_prob_out, int32_t* offsets_out, void* ws,
+                             size_t ws_bytes, void* stream) {
+  return moe_layer_forward_dynamic(cfg, T, x, w, nullptr, out, topk_idx_out, topk_prob_out, offsets_out, ws, ws_bytes,
+                                   stream);
+}
+
+moe_status moe_route(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const float* bias,
+                     int32_t* topk_idx, float* topk_prob, float* gap, void* ws, size_t ws_bytes, void* stream) {
+  return moe_route_dynamic(cfg, T, x, w_router, bias, nullptr, topk_idx, topk_prob, gap, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

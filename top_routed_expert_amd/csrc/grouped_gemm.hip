@@ -358,7 +358,8 @@ __global__ void __launch_bounds__(256) gemm_generic(GemmArgs p) {
 // non-decreasing, so malformed offsets cannot address rows out of range.
 __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __restrict__ offsets, int n_groups,
                                                            int64_t n_rows, int BM, Tile* __restrict__ tiles,
-                                                           int32_t* __restrict__ n_tiles, int32_t max_tiles) {
+                                                           int32_t* __restrict__ n_tiles, int32_t max_tiles,
+                                                           int skip_group) {
   __shared__ int32_t s_scan[1024];
   const int tid = threadIdx.x;
   const int per = (n_groups + 1023) / 1024;
@@ -368,6 +369,7 @@ __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __rest
     b = offsets[g + 1];
     a = a < 0 ? 0 : (a > n_rows ? n_rows : a);
     b = b < a ? a : (b > n_rows ? n_rows : b);
+    if (g == skip_group) b = a;  // a group with no work (rows of pairs without an expert)
   };
   int mine = 0;
   for (int g = g0; g < g1; ++g) {
@@ -416,8 +418,9 @@ int64_t gemm_max_tiles(int64_t n_rows, int n_groups, int block_rows) {
 }
 
 hipError_t launch_build_tiles(const int32_t* offsets, int n_groups, int64_t n_rows, int block_rows, Tile* tiles,
-                              int32_t* n_tiles, int32_t max_tiles, hipStream_t s) {
-  build_tiles_kernel<<<1, 1024, 0, s>>>(offsets, n_groups, n_rows, block_rows, tiles, n_tiles, max_tiles);
+                              int32_t* n_tiles, int32_t max_tiles, int skip_group, hipStream_t s) {
+  build_tiles_kernel<<<1, 1024, 0, s>>>(offsets, n_groups, n_rows, block_rows, tiles, n_tiles, max_tiles,
+                                        skip_group);
   return hipGetLastError();
 }
 

@@ -102,24 +102,33 @@ int gemm_block_rows(bool fast, int64_t rows, int n_groups, bool allow_big);
 // Contraction slices of the router GEMM for T tokens (1 unless T is small).
 int router_ksplit(bool fast, int64_t T, int Kdim);
 int64_t gemm_max_tiles(int64_t n_rows, int n_groups, int block_rows);
+// Tiles of groups g = 0 .. n_groups-1 over rows [offsets[g], offsets[g+1]);
+// group skip_group (if >= 0) gets none.
 hipError_t launch_build_tiles(const int32_t* offsets, int n_groups, int64_t n_rows, int block_rows,
-                              Tile* tiles, int32_t* n_tiles, int32_t max_tiles, hipStream_t s);
+                              Tile* tiles, int32_t* n_tiles, int32_t max_tiles, int skip_group, hipStream_t s);
 hipError_t launch_grouped_gemm(int dtype, bool fast, int epi, int block_rows, const GemmArgs& g, hipStream_t s);
 // grouped_gemm_big.hip: 256 x 256 block tiles (block_rows == 256).
 hipError_t launch_grouped_gemm_big(int epi, const GemmArgs& g, hipStream_t s);
 
 // route.hip
 // Logits are the sum of nsplit partial arrays [nsplit][T][E], added in slice order.
-hipError_t launch_topk(const float* logits, int nsplit, int64_t T, int E, int K, int32_t* idx, float* prob,
-                       float* gap, hipStream_t s);
+// k_tok (optional): token t keeps its first k_tok[t] (clamped to [0, K])
+// choices; later slots get idx -1 and prob 0.
+hipError_t launch_topk(const float* logits, int nsplit, int64_t T, int E, int K, const int32_t* k_tok, int32_t* idx,
+                       float* prob, float* gap, hipStream_t s);
 
-// permute.hip
+// permute.hip. Pairs with idx outside [0, E) get dest -1 and no row.
+// offsets_ext [E+3] (optional), the row groups of the fused expert launch:
+// the E routed segments (ending at the valid pair count V), then [V, T*K)
+// (rows of pairs without an expert: no tiles), then the extra_rows rows
+// from T*K on (the shared expert).
 hipError_t launch_permute(const int32_t* idx, int64_t T, int K, int E, int32_t* rank, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_token, int32_t* dest,
                           int32_t* offsets_ext, int32_t extra_rows, hipStream_t s);
 bool permute_small_fits(int64_t T, int K, int E);
 // Single-block permutation for small batches; also writes the tile table of
-// the expert GEMMs over E (+1 if extra_rows) groups when tiles != NULL.
+// the expert GEMMs over the groups of offsets_ext (E, or E+2 with
+// extra_rows) when tiles != NULL.
 hipError_t launch_permute_small(const int32_t* idx, int64_t T, int K, int E, int32_t* offsets, int32_t* sorted_token,
                                 int32_t* dest, int32_t* offsets_ext, int32_t extra_rows, Tile* tiles,
                                 int32_t* n_tiles, int32_t max_tiles, int block_rows, hipStream_t s);

@@ -111,7 +111,10 @@ __global__ void __launch_bounds__(256) permute_place_kernel(const int32_t* __res
       if (offsets) offsets[e] = s_off[e];
       if (offsets_ext) offsets_ext[e] = s_off[e];
     }
-    if (offsets_ext && tid == 0) offsets_ext[E + 1] = s_off[E] + extra_rows;
+    if (offsets_ext && tid == 0) {  // rows of pairs without an expert, then the extra rows
+      offsets_ext[E + 1] = (int32_t)P;
+      offsets_ext[E + 2] = (int32_t)P + extra_rows;
+    }
   }
   for (int64_t j = (int64_t)blockIdx.x * 256 + tid; j < P; j += (int64_t)gridDim.x * 256) {
     const int e = idx[j];
@@ -161,7 +164,7 @@ __device__ __forceinline__ int block1024_excl_scan(int v, int* s_tot, int* total
   return (wave ? s_tot[wave - 1] : 0) + incl - v;
 }
 
-// Small batches (T*K <= 1024, E <= 1023): the whole permutation and the
+// Small batches (T*K <= 1024, E <= 1022): the whole permutation and the
 // expert-GEMM tile table in one block of 1024 threads. Counts come from LDS
 // atomics (order-independent); each pair's rank among the earlier pairs of
 // its expert is counted directly over the pairs before it (a wave-uniform
@@ -196,7 +199,10 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
     if (offsets) offsets[tid] = s_off[tid];
     if (offsets_ext) offsets_ext[tid] = s_off[tid];
   }
-  if (tid == 0 && offsets_ext) offsets_ext[E + 1] = total + extra_rows;
+  if (tid == 0 && offsets_ext) {  // rows of pairs without an expert, then the extra rows
+    offsets_ext[E + 1] = P;
+    offsets_ext[E + 2] = P + extra_rows;
+  }
   // stable rank: earlier pairs routed to the same expert. The loop bound is
   // uniform per wave (the wave's last pair; 0 for waves past the last
   // pair); 4 pairs per LDS read.
@@ -218,12 +224,15 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
     }
   }
   if (tiles == nullptr) return;
-  // tile table over the E routed groups and, with extra_rows, the shared group
-  const int n_groups = E + (extra_rows > 0 ? 1 : 0);
+  // tile table over the E routed groups and, with extra_rows, group E (rows
+  // of pairs without an expert: no tiles) and group E+1 (the extra rows)
   int seg0 = 0, seg1 = 0;
-  if (tid < n_groups) {
-    seg0 = tid < E ? s_off[tid] : total;
-    seg1 = tid < E ? s_off[tid + 1] : total + extra_rows;
+  if (tid < E) {
+    seg0 = s_off[tid];
+    seg1 = s_off[tid + 1];
+  } else if (tid == E + 1 && extra_rows > 0) {
+    seg0 = P;
+    seg1 = P + extra_rows;
   }
   const int mine = (seg1 - seg0 + BM - 1) / BM;
   int n_all;
@@ -237,7 +246,7 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
 
 }  // namespace
 
-bool permute_small_fits(int64_t T, int K, int E) { return T * K <= 1024 && E <= 1023; }
+bool permute_small_fits(int64_t T, int K, int E) { return T * K <= 1024 && E <= 1022; }
 
 hipError_t launch_permute_small(const int32_t* idx, int64_t T, int K, int E, int32_t* offsets, int32_t* sorted_token,
                                 int32_t* dest, int32_t* offsets_ext, int32_t extra_rows, Tile* tiles,

@@ -106,7 +106,8 @@ __device__ __forceinline__ void sum_partials(const float* __restrict__ logits, i
 
 template <int VPL>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int nsplit, int64_t T, int E,
-                                                   int K, int32_t* __restrict__ idx, float* __restrict__ prob,
+                                                   int K, const int32_t* __restrict__ k_tok,
+                                                   int32_t* __restrict__ idx, float* __restrict__ prob,
                                                    float* __restrict__ gap) {
   __shared__ float s_logit[1024];
   __shared__ float s_part[4096];
@@ -151,17 +152,23 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     key[j] = e < (unsigned)E ? ((unsigned long long)__float_as_uint(p) << 32) | (0xffffffffu - e) : 0ull;
   }
 
+  // this token's number of experts: K, or k_tok[t] clamped to [0, K]
+  int kt = K;
+  if (k_tok) {
+    kt = k_tok[t];
+    kt = kt < 0 ? 0 : (kt > K ? K : kt);
+  }
   float p_last = 0.f;
-  for (int r = 0; r <= K; ++r) {
-    if (r == K && K == E) break;
+  for (int r = 0; r <= kt; ++r) {
+    if (r == kt && kt == E) break;
     unsigned long long best = key[0];
 #pragma unroll
     for (int j = 1; j < VPL; ++j) best = key[j] > best ? key[j] : best;
     best = wave_max_u64(best);
     const unsigned e = 0xffffffffu - (unsigned)(best & 0xffffffffu);
     const float p = __uint_as_float((unsigned)(best >> 32));
-    if (r == K) {
-      if (gap && lane == 0) gap[t] = p_last - p;
+    if (r == kt) {
+      if (gap && lane == 0) gap[t] = kt > 0 ? p_last - p : INFINITY;
       break;
     }
     if (lane == 0) {
@@ -173,17 +180,23 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     for (int j = 0; j < VPL; ++j)
       if ((unsigned)(lane + 64 * j) == e) key[j] = 0ull;
   }
-  if (K == E && gap && lane == 0) gap[t] = INFINITY;
+  if (kt == E && gap && lane == 0) gap[t] = INFINITY;
+  // slots past the token's own count: no expert
+  if (lane == 0)
+    for (int r = kt; r < K; ++r) {
+      idx[t * K + r] = -1;
+      prob[t * K + r] = 0.f;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_topk(const float* logits, int nsplit, int64_t T, int E, int K, int32_t* idx, float* prob,
-                       float* gap, hipStream_t s) {
+hipError_t launch_topk(const float* logits, int nsplit, int64_t T, int E, int K, const int32_t* k_tok, int32_t* idx,
+                       float* prob, float* gap, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)(nsplit > 1 ? T : (T + 3) / 4);
   const int vpl = (E + 63) / 64;
-#define MOE_TOPK(V) topk_kernel<V><<<blocks, 256, 0, s>>>(logits, nsplit, T, E, K, idx, prob, gap)
+#define MOE_TOPK(V) topk_kernel<V><<<blocks, 256, 0, s>>>(logits, nsplit, T, E, K, k_tok, idx, prob, gap)
   if (vpl <= 1) MOE_TOPK(1);
   else if (vpl <= 2) MOE_TOPK(2);
   else if (vpl <= 3) MOE_TOPK(3);

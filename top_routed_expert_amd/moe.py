@@ -53,6 +53,7 @@ _SIGS = {
     "moe_grouped_ffn_workspace_bytes": ([_CFG, _I32, _I64, _I32], _SZ),
     "moe_layer_workspace_bytes": ([_CFG, _I64], _SZ),
     "moe_route": ([_CFG, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "moe_route_dynamic": ([_CFG, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "moe_permute": ([_CFG, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "moe_grouped_ffn": ([_CFG, _I32, _I64, _P, _P, _I64, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P], ctypes.c_int),
     "moe_expert_workspace_bytes": ([_CFG, _I32, _I64, _I32], _SZ),
@@ -61,6 +62,8 @@ _SIGS = {
     "moe_expert_down": ([_CFG, _I32, _I64, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P], ctypes.c_int),
     "moe_combine": ([_CFG, _I64, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "moe_layer_forward": ([_CFG, _I64, _P, ctypes.POINTER(MoeWeights), _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "moe_layer_forward_dynamic": ([_CFG, _I64, _P, ctypes.POINTER(MoeWeights), _P, _P, _P, _P, _P, _P, _SZ, _P],
+                                  ctypes.c_int),
     "moe_packed_weights_bytes": ([_I64, _I64, _I64], _SZ),
     "moe_pack_weights": ([_I64, _I64, _I64, _P, _P, _SZ, _P], ctypes.c_int),
 }
@@ -148,8 +151,9 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def route(cfg: Config, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor | None = None,
-          want_gap: bool = False):
-    """moe_route: returns (topk_idx [T,K] int32, topk_prob [T,K] fp32[, gap [T] fp32])."""
+          want_gap: bool = False, k_per_token: torch.Tensor | None = None):
+    """moe_route (moe_route_dynamic with k_per_token [T] int32): returns
+    (topk_idx [T,K] int32, topk_prob [T,K] fp32[, gap [T] fp32])."""
     T = x.shape[0]
     dev = x.device
     c = cfg.c()
@@ -157,11 +161,12 @@ def route(cfg: Config, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tens
     prob = torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev)
     gap = torch.empty((T,), dtype=torch.float32, device=dev) if want_gap else None
     ws = _workspace(lib().moe_route_workspace_bytes(ctypes.byref(c), T), dev)
-    _check(lib().moe_route(ctypes.byref(c), T, _ptr(x, "x", cfg.dtype, (T, cfg.d_model)),
-                           _ptr(w_router, "w_router", cfg.dtype, cfg.wshape(cfg.n_experts, cfg.d_model), dev),
-                           _ptr(bias, "bias", torch.float32, (cfg.n_experts,), dev),
-                           _ptr(idx, "idx"), _ptr(prob, "prob"), _ptr(gap, "gap"),
-                           ws.data_ptr(), ws.numel(), _stream(dev)), "moe_route")
+    _check(lib().moe_route_dynamic(ctypes.byref(c), T, _ptr(x, "x", cfg.dtype, (T, cfg.d_model)),
+                                   _ptr(w_router, "w_router", cfg.dtype, cfg.wshape(cfg.n_experts, cfg.d_model), dev),
+                                   _ptr(bias, "bias", torch.float32, (cfg.n_experts,), dev),
+                                   _ptr(k_per_token, "k_per_token", torch.int32, (T,), dev),
+                                   _ptr(idx, "idx"), _ptr(prob, "prob"), _ptr(gap, "gap"),
+                                   ws.data_ptr(), ws.numel(), _stream(dev)), "moe_route")
     return (idx, prob, gap) if want_gap else (idx, prob)
 
 
@@ -303,8 +308,10 @@ class Workspace:
 
 
 def layer_forward(cfg: Config, x: torch.Tensor, w: dict, out: torch.Tensor | None = None,
-                  routing: bool = False, workspace: Workspace | None = None, weights: MoeWeights | None = None):
-    """moe_layer_forward: out [T, D]; with routing=True also (topk_idx, topk_prob, offsets)."""
+                  routing: bool = False, workspace: Workspace | None = None, weights: MoeWeights | None = None,
+                  k_per_token: torch.Tensor | None = None):
+    """moe_layer_forward (moe_layer_forward_dynamic with k_per_token [T] int32): out [T, D];
+    with routing=True also (topk_idx, topk_prob, offsets)."""
     T = x.shape[0]
     dev = x.device
     c = cfg.c()
@@ -318,10 +325,17 @@ def layer_forward(cfg: Config, x: torch.Tensor, w: dict, out: torch.Tensor | Non
         idx = torch.empty((T, cfg.top_k), dtype=torch.int32, device=dev)
         prob = torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev)
         offs = torch.empty((cfg.n_experts + 1,), dtype=torch.int32, device=dev)
-    _check(lib().moe_layer_forward(ctypes.byref(c), T, _ptr(x, "x", cfg.dtype, (T, cfg.d_model), dev),
-                                   ctypes.byref(wt), _ptr(out, "out", cfg.odtype, (T, cfg.d_model), dev),
-                                   _ptr(idx, "idx"), _ptr(prob, "prob"), _ptr(offs, "offsets"),
-                                   ws.data_ptr(), ws.numel(), _stream(dev)), "moe_layer_forward")
+    if k_per_token is None:
+        _check(lib().moe_layer_forward(ctypes.byref(c), T, _ptr(x, "x", cfg.dtype, (T, cfg.d_model), dev),
+                                       ctypes.byref(wt), _ptr(out, "out", cfg.odtype, (T, cfg.d_model), dev),
+                                       _ptr(idx, "idx"), _ptr(prob, "prob"), _ptr(offs, "offsets"),
+                                       ws.data_ptr(), ws.numel(), _stream(dev)), "moe_layer_forward")
+    else:
+        _check(lib().moe_layer_forward_dynamic(
+            ctypes.byref(c), T, _ptr(x, "x", cfg.dtype, (T, cfg.d_model), dev), ctypes.byref(wt),
+            _ptr(k_per_token, "k_per_token", torch.int32, (T,), dev),
+            _ptr(out, "out", cfg.odtype, (T, cfg.d_model), dev), _ptr(idx, "idx"), _ptr(prob, "prob"),
+            _ptr(offs, "offsets"), ws.data_ptr(), ws.numel(), _stream(dev)), "moe_layer_forward_dynamic")
     return (out, idx, prob, offs) if routing else out
 
 
