@@ -79,6 +79,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--ep-share", action="store_true",
+                    help="one GPU's expert-parallel share (36 experts, 8 ranks x 8192 tokens), one JSON line")
     ap.add_argument("--dynamic-k", action="store_true",
                     help="dynamic top-k (4 or 8 per token) vs fixed top-8 at decode and prefill, one JSON line each")
     ap.add_argument("--sweep", action="store_true",
@@ -298,6 +300,73 @@ def dynamic_topk(steps, warmup, flush_on):
         torch.cuda.empty_cache()
 
 
+def ep_share(steps, warmup, flush_on, n_src=8, n_groups=8, group=0):
+    """One GPU's share under expert parallelism at the prefill shape: 8 source ranks x 8192 tokens
+    route and permute their own tokens; group 0's 36 experts run on the rows they would send it
+    (receive plan, gate/up on the receive buffer in place, down, outputs back in receive order).
+    One JSON line; the per-group balance statistics of the same routing are reported beside it."""
+    import numpy as np
+    import torch
+
+    import synth
+    import top_routed_expert_amd as moe
+
+    spec = synth.spec("prefill", T=n_src * 8192)
+    L = synth.make_layer(spec, "cuda")
+    cfg = moe.config_for(spec, packed=True)
+    W = moe.pack_layer(L)
+    del L["w_gate"], L["w_up"], L["w_down"]
+    Tl, El = spec.T // n_src, spec.E // n_groups
+    idx, _, stats = moe.route_group_stats(cfg, L["x"], W["w_router"], n_groups, L["bias"])
+    chunks, counts = [], []
+    for r in range(n_src):
+        sl = slice(r * Tl, (r + 1) * Tl)
+        offs, _, _, xp = moe.permute(cfg, idx[sl].contiguous(), L["x"][sl].contiguous())
+        oh = offs.cpu().numpy().astype(np.int64)
+        chunks.append(xp[oh[group * El]:oh[(group + 1) * El]])
+        counts.append(np.diff(oh)[group * El:(group + 1) * El])
+        del xp
+    recv = torch.cat(chunks).contiguous()
+    del chunks
+    n = recv.shape[0]
+    cnt = torch.from_numpy(np.stack(counts).astype(np.int32)).cuda()
+    local = moe.Config(spec.D, El, spec.K, spec.F, 0, cfg.dtype, cfg.out_dtype, True)
+    sl = slice(group * El, (group + 1) * El)
+    wg, wu, wd = W["w_gate"][sl], W["w_up"][sl], W["w_down"][sl]
+    h = torch.empty((n, spec.F), dtype=cfg.dtype, device="cuda")
+    y = torch.empty((n, spec.D), dtype=torch.float32, device="cuda")
+    y_recv = torch.empty_like(y)
+    gws = torch.empty(moe.lib().moe_expert_workspace_bytes(__import__("ctypes").byref(local.c()), El, n, spec.F),
+                      dtype=torch.uint8, device="cuda")
+    plan = {}
+
+    def share():
+        plan["p"] = moe.ep_receive_plan(cnt, n)
+        offsets, gather, scatter = plan["p"]
+        moe.expert_gate_up(local, offsets, recv, wg, wu, gather=gather, n_rows=n, h=h, ws=gws)
+        moe.expert_down(local, offsets, h, wd, y=y, ws=gws)
+        moe.gather_rows(y, scatter, out=y_recv)
+
+    flush = Flusher(flush_on)
+    ms, _ = timed(share, steps, warmup, flush)
+    offsets, gather, _ = plan["p"]
+    gemm = lambda: (moe.expert_gate_up(local, offsets, recv, wg, wu, gather=gather, n_rows=n, h=h, ws=gws),
+                    moe.expert_down(local, offsets, h, wd, y=y, ws=gws))
+    gms, _ = timed(gemm, steps, warmup, flush)
+    ms_step, g_ms = float(np.mean(ms)), float(np.mean(gms))
+    flops = 2 * n * 3 * spec.D * spec.F
+    st = stats.cpu().numpy()
+    f, pg = st[n_groups:] / st[n_groups:].sum(), st[:n_groups] / spec.T
+    return dict(workload=f"ep share: group {group} of {n_groups} ({El} experts), {n_src} ranks x {Tl} tokens",
+                rows=n, rows_per_expert=round(n / El, 1), ms_per_step=round(ms_step, 5),
+                rows_per_s=round(n / (ms_step * 1e-3), 1), gemm_ms=round(g_ms, 5),
+                gemm_tflops=round(flops / (g_ms * 1e-3) / 1e12, 1),
+                gemm_mfma_frac=round(flops / (g_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                share_mfma_frac=round(flops / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                l_ep=round(float(n_groups * np.sum(f * pg)), 5),
+                group_pair_fraction=[round(float(v), 5) for v in f])
+
+
 def cpu_baseline(spec, L, n_tokens: int):
     """The oracle, as it stands, on the first n_tokens tokens of the workload (single thread)."""
     import numpy as np
@@ -337,6 +406,10 @@ def main():
 
     import synth
 
+    if args.ep_share:
+        print(f"[bench] expert-parallel share, steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+        print(json.dumps(ep_share(args.steps, args.warmup, not args.no_flush)), flush=True)
+        return
     if args.dynamic_k:
         print(f"[bench] dynamic top-k vs fixed top-8, steps={args.steps} warmup={args.warmup}", file=sys.stderr,
               flush=True)

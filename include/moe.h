@@ -251,6 +251,52 @@ moe_status moe_layer_forward_dynamic(const moe_config* cfg, int64_t T, const voi
                                      int32_t* offsets_out, void* ws, size_t ws_bytes,
                                      void* stream);
 
+/* Expert-parallel balance statistics (page "Step3.5 Flash 大模型技术深度解析",
+ * section 3.2.3: the 288 routed experts split into G equal groups, one group
+ * per GPU, with the balance loss L_EP = G * sum_g f_g p_g, f_g the activation
+ * frequency of group g's experts and p_g their routing probability). The
+ * router as moe_route_dynamic (k_per_token may be NULL), plus
+ *   n_groups   G in [1, 16], dividing E; group g = experts g*E/G .. (g+1)*E/G - 1
+ *   stats      [2G] fp64 out: stats[g] = sum over tokens of the softmax mass of
+ *              group g's experts (p_g = stats[g] / T); stats[G + g] = number
+ *              of chosen (token, slot) pairs in group g (f_g = stats[G + g] /
+ *              sum of stats[G..2G-1]). Sums over tokens run in a fixed order:
+ *              the result does not depend on scheduling.
+ *   ws         >= moe_route_group_stats_workspace_bytes(cfg, T, G) bytes  */
+size_t moe_route_group_stats_workspace_bytes(const moe_config* cfg, int64_t T, int32_t n_groups);
+moe_status moe_route_group_stats(const moe_config* cfg, int64_t T, const void* x,
+                                 const void* w_router, const float* bias,
+                                 const int32_t* k_per_token, int32_t n_groups, int32_t* topk_idx,
+                                 float* topk_prob, double* stats, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* Receive plan of one GPU's share under expert parallelism (section 3.2.3:
+ * each GPU holds one group of experts). The dispatch exchange delivers one
+ * chunk per (source rank r, local expert e), r-major, each chunk holding that
+ * source's rows for e in its own (token) order: exactly the source's
+ * moe_permute rows of the group's experts, so a source's send buffer is one
+ * contiguous slice of its permuted rows per destination.
+ *   counts   [n_src * n_local] int32 (device): rows of chunk (r, e) at
+ *            r * n_local + e; negative counts count as 0; the total must be
+ *            below 2^31. n_src >= 1, n_local >= 1, n_src * n_local <= 1024.
+ *   offsets  [n_local + 1] int32 out: expert e's rows in expert-major order
+ *            are offsets[e] .. offsets[e+1]-1 (experts in turn, sources in
+ *            turn inside an expert, a chunk's rows in turn)
+ *   gather   [max_rows] int32 out: expert-major row q is receive row gather[q]
+ *   scatter  [max_rows] int32 out: receive row i is expert-major row scatter[i]
+ * Rows at or past max_rows are not written. With `gather` as the row map of
+ * moe_expert_gate_up (x = the receive buffer) the local experts run on the
+ * received rows in place; moe_gather_rows with `scatter` puts their outputs
+ * back in receive order, the layout the return exchange sends. */
+moe_status moe_ep_receive_plan(int32_t n_src, int32_t n_local, const int32_t* counts,
+                               int64_t max_rows, int32_t* offsets, int32_t* gather,
+                               int32_t* scatter, void* stream);
+
+/* Row gather: dst[i] = src[index[i]] for i < n_rows, rows of row_bytes bytes
+ * (index clamped to [0, n_src_rows)). row_bytes in [1, 2^30]. */
+moe_status moe_gather_rows(const void* src, int64_t n_src_rows, int64_t row_bytes,
+                           const int32_t* index, int64_t n_rows, void* dst, void* stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status s);
 

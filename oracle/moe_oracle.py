@@ -38,7 +38,15 @@ notes):
      the first k_t of its choices in the same order (k_t clamped to [0, K]),
      with the same unrenormalised probabilities; its remaining slots hold
      expert -1 with probability 0 and contribute nothing; the shared expert
-     is unchanged.
+     is unchanged;
+  R13 expert-parallel balance (page "Step3.5 Flash 大模型技术深度解析",
+     section 3.2.3: the 288 experts in G groups, one per GPU; L_EP = G sum_g
+     f_g p_g): groups are E/G contiguous expert ids; f_g is the fraction of
+     the chosen (token, slot) pairs that fall in group g and p_g the mean over
+     tokens of the softmax mass of group g's experts, so both sum to 1 and a
+     perfectly balanced routing gives L_EP = 1. One GPU's share receives, per
+     source rank r and local expert e, that source's rows for e in token
+     order, chunks r-major; its experts run on them in expert-major order.
 """
 from __future__ import annotations
 
@@ -286,3 +294,48 @@ def group_counts(counts: np.ndarray, groups: int) -> np.ndarray:
     """Activation counts of `groups` contiguous equal expert groups (e // (E/groups))."""
     c = np.asarray(counts)
     return c.reshape(groups, -1).sum(axis=1)
+
+
+# --------------------------------------------------- expert parallelism ---
+
+def group_stats(p64, idx, n_groups: int) -> dict:
+    """Balance statistics of G contiguous expert groups (R13).
+
+    mass[g]  = sum over tokens of sum_{e in g} p[t,e]     (p: the softmax, fp64)
+    pairs[g] = number of chosen (t, slot) pairs with an expert in g
+    f = pairs / sum(pairs), p = mass / T, l_ep = G * sum_g f_g p_g.
+    """
+    p64 = as_f64(p64)
+    T, E = p64.shape
+    gs = E // n_groups
+    mass = np.array([p64[:, g * gs:(g + 1) * gs].sum() for g in range(n_groups)])
+    flat = np.asarray(idx).reshape(-1).astype(np.int64)
+    flat = flat[(flat >= 0) & (flat < E)]
+    pairs = np.bincount(flat // gs, minlength=n_groups).astype(np.int64)
+    f = pairs / pairs.sum() if pairs.sum() else np.zeros(n_groups)
+    p = mass / T if T else np.zeros(n_groups)
+    return dict(mass=mass, pairs=pairs, f=f, p=p, l_ep=float(n_groups * np.sum(f * p)))
+
+
+def ep_receive_plan(counts) -> dict:
+    """Expert-major order of one GPU's receive buffer (R13).
+
+    counts[r, e]: rows of source r for local expert e; the buffer holds the
+    chunks (r, e) r-major, each chunk's rows in order. Expert-major order
+    takes experts in turn, sources in turn inside an expert, a chunk's rows
+    in turn. gather[q] = receive row of expert-major row q; scatter is its
+    inverse; offsets[e] = first expert-major row of e.
+    """
+    c = np.maximum(np.asarray(counts, dtype=np.int64), 0)
+    R, El = c.shape
+    start = np.concatenate([[0], np.cumsum(c.reshape(-1))])[:-1].reshape(R, El)   # r-major chunk starts
+    gather = []
+    offsets = [0]
+    for e in range(El):
+        for r in range(R):
+            gather.extend(range(int(start[r, e]), int(start[r, e] + c[r, e])))
+        offsets.append(len(gather))
+    gather = np.array(gather, dtype=np.int64)
+    scatter = np.empty_like(gather)
+    scatter[gather] = np.arange(len(gather))
+    return dict(offsets=np.array(offsets, dtype=np.int64), gather=gather, scatter=scatter)

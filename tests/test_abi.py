@@ -38,7 +38,7 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails its checks
 def test_exports_every_declared_function():
     L = moe.lib()
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(L, n), f"libmoe.so does not export {n}"
     assert set(names) == set(M._SIGS), "binding signatures out of sync with the header"
@@ -222,3 +222,41 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(M, "LIB_PATH", os.path.join(ROOT, "does_not_exist", "libmoe.so"))
     with pytest.raises(RuntimeError, match="missing"):
         M.lib()
+
+
+def test_dynamic_and_expert_parallel_entry_checks():
+    """Argument checks of the dynamic-top-k, group-statistics, receive-plan and row-gather entry points."""
+    L = moe.lib()
+    c = cfg()
+    ws = L.moe_route_workspace_bytes(ctypes.byref(c), 8)
+    # dynamic router: a misaligned per-token count array is refused, T = 0 is a no-op
+    assert L.moe_route_dynamic(ctypes.byref(c), 8, FAKE, FAKE, None, FAKE + 4, FAKE, FAKE, None, FAKE, ws,
+                               None) == MISALIGNED
+    assert L.moe_route_dynamic(ctypes.byref(c), 0, FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE, ws, None) == OK
+    lw = L.moe_layer_workspace_bytes(ctypes.byref(c), 8)
+    wts = M.MoeWeights()
+    assert L.moe_layer_forward_dynamic(ctypes.byref(c), 8, FAKE, ctypes.byref(wts), None, FAKE, None, None, None,
+                                       FAKE, lw, None) == NULL
+    # group statistics: G must divide E and lie in [1, 16]
+    assert L.moe_route_group_stats_workspace_bytes(ctypes.byref(c), 8, 3) == M.SIZE_MAX   # 16 % 3
+    assert L.moe_route_group_stats_workspace_bytes(ctypes.byref(c), 8, 0) == M.SIZE_MAX
+    gw = L.moe_route_group_stats_workspace_bytes(ctypes.byref(c), 8, 4)
+    assert gw >= ws + 8 * 4 * 4
+    gcall = lambda G=4, st=FAKE, wsb=gw: L.moe_route_group_stats(ctypes.byref(c), 8, FAKE, FAKE, None, None, G, FAKE,
+                                                                   FAKE, st, FAKE, wsb, None)
+    assert gcall(G=32) == SHAPE
+    assert gcall(st=None) == NULL
+    assert gcall(wsb=gw - 1) == WS
+    # receive plan: at most 1024 chunks, a bounded row capacity, every output present
+    plan = lambda ns=8, nl=36, cnt=FAKE, mx=100, off=FAKE, ga=FAKE, sc=FAKE: \
+        L.moe_ep_receive_plan(ns, nl, cnt, mx, off, ga, sc, None)
+    assert plan(ns=32, nl=33) == SHAPE
+    assert plan(ns=0) == SHAPE
+    assert plan(mx=-1) == SHAPE and plan(mx=1 << 31) == SHAPE
+    assert plan(ga=None) == NULL and plan(cnt=None) == NULL
+    assert plan(sc=FAKE + 4) == MISALIGNED
+    # row gather
+    gat = lambda src=FAKE, ns=10, rb=64, idx=FAKE, n=5, dst=FAKE: L.moe_gather_rows(src, ns, rb, idx, n, dst, None)
+    assert gat(rb=0) == SHAPE and gat(n=-1) == SHAPE and gat(ns=0) == SHAPE
+    assert gat(n=0, src=None) == OK
+    assert gat(idx=None) == NULL and gat(dst=FAKE + 2) == MISALIGNED

@@ -351,6 +351,79 @@ def pin_dynamic_topk_layer():
     assert np.allclose(rr["out_rows"], rf["out"][[1, 6, 13]], rtol=1e-12, atol=1e-13)
 
 
+def pin_ep_receive_plan():
+    """Hand-worked receive plan, then invariants on random counts."""
+    # chunks r-major: (0,0) rows 0,1; (0,1) none; (0,2) row 2; (1,0) row 3; (1,1) rows 4,5,6; (1,2) none
+    p = O.ep_receive_plan([[2, 0, 1], [1, 3, 0]])
+    assert p["gather"].tolist() == [0, 1, 3, 4, 5, 6, 2]
+    assert p["offsets"].tolist() == [0, 3, 6, 7]
+    assert p["scatter"].tolist() == [0, 1, 6, 2, 3, 4, 5]
+    rng = np.random.default_rng(8)
+    for R, El in [(8, 36), (3, 5), (1, 4), (6, 1)]:
+        c = rng.integers(0, 7, size=(R, El)) * (rng.random((R, El)) > 0.2)
+        p = O.ep_receive_plan(c)
+        n = int(c.sum())
+        assert np.array_equal(np.sort(p["gather"]), np.arange(n))             # a permutation of the rows
+        assert np.array_equal(p["scatter"][p["gather"]], np.arange(n))
+        assert np.array_equal(np.diff(p["offsets"]), c.sum(axis=0))           # segment = the expert's rows
+        # inside an expert, sources in turn: receive rows increase
+        for e in range(El):
+            seg = p["gather"][p["offsets"][e]:p["offsets"][e + 1]]
+            assert np.all(np.diff(seg) > 0)
+
+
+def pin_group_stats():
+    """Balance statistics: closed forms (uniform router, balanced routing) and brute force."""
+    G, E, T = 4, 12, 6
+    # all logits equal: every group holds mass 1/G; top-2 takes experts 0 and 1 (group 0)
+    r = O.route(np.ones((T, 3)), np.zeros((E, 3)), 2)
+    st = O.group_stats(r["p64"], r["idx"], G)
+    assert np.allclose(st["p"], 1.0 / G, rtol=0, atol=1e-15)
+    assert st["pairs"].tolist() == [2 * T, 0, 0, 0] and st["f"].tolist() == [1.0, 0, 0, 0]
+    assert math.isclose(st["l_ep"], G * 1.0 * (1.0 / G), rel_tol=1e-14)
+    # perfectly balanced: uniform p and one pair per group per token -> L_EP = 1
+    idx = np.array([[g * (E // G) for g in range(G)]] * T)
+    st = O.group_stats(np.full((T, E), 1.0 / E), idx, G)
+    assert math.isclose(st["l_ep"], 1.0, rel_tol=1e-14)
+    # brute force on random probabilities and choices (with empty slots)
+    rng = np.random.default_rng(12)
+    p = rng.random((T, E))
+    p /= p.sum(axis=1, keepdims=True)
+    idx = np.stack([rng.permutation(E)[:3] for _ in range(T)])
+    idx[1, 2] = -1
+    st = O.group_stats(p, idx, G)
+    for g in range(G):
+        m = math.fsum(p[t][e] for t in range(T) for e in range(E) if e // (E // G) == g)
+        n = sum(1 for t in range(T) for j in range(3) if idx[t][j] >= 0 and idx[t][j] // (E // G) == g)
+        assert math.isclose(st["mass"][g], m, rel_tol=1e-14) and st["pairs"][g] == n
+    assert math.isclose(st["f"].sum(), 1.0, rel_tol=1e-14) and math.isclose(st["p"].sum(), 1.0, rel_tol=1e-14)
+
+
+def pin_ep_share_composition():
+    """Per-source permutes, the receive plan and a grouped FFN give each received row its expert's FFN."""
+    rng = np.random.default_rng(31)
+    R, Tl, D, E, K, F, G = 3, 5, 4, 8, 2, 3, 2
+    El = E // G
+    L = rand_layer(rng, R * Tl, D, E, K, F, 0)
+    W = O.LayerWeights.from_dict(L)
+    for g in range(G):
+        chunks, counts, want = [], np.zeros((R, El), dtype=np.int64), []
+        for r in range(R):
+            xs = L["x"][r * Tl:(r + 1) * Tl]
+            rt = O.route(xs, L["w_router"], K)
+            pm = O.permute(rt["idx"], E)
+            for e in range(El):
+                a, b = pm["offsets"][g * El + e], pm["offsets"][g * El + e + 1]
+                counts[r, e] = b - a
+                chunks.append(xs[pm["sorted_token"][a:b]])
+                want.extend(O.swiglu_ffn(xs[t:t + 1], *W.expert(g * El + e))[0] for t in pm["sorted_token"][a:b])
+        recv = np.concatenate(chunks) if chunks else np.zeros((0, D))
+        plan = O.ep_receive_plan(counts)
+        y_em = O.grouped_ffn(recv[plan["gather"]], plan["offsets"], lambda e: W.expert(g * El + e))
+        y_recv = y_em[plan["scatter"]]
+        assert np.allclose(y_recv, np.array(want).reshape(-1, D), rtol=1e-12, atol=1e-14)
+
+
 def pin_page_constants():
     """The page's structural numbers, and the width reading they force."""
     g = json.load(open(os.path.join(GOLDEN, "step35_layer_constants.json")))["values"]
@@ -376,7 +449,7 @@ def pin_page_constants():
 PINS = [pin_route_bruteforce, pin_route_ties, pin_route_properties, pin_route_bias, pin_permute,
         pin_ffn_closed_form, pin_ffn_bruteforce, pin_layer_worked_example,
         pin_layer_special_cases, pin_dynamic_topk_route, pin_dynamic_topk_permute, pin_dynamic_topk_layer,
-        pin_page_constants]
+        pin_ep_receive_plan, pin_group_stats, pin_ep_share_composition, pin_page_constants]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -492,7 +565,27 @@ def _no_expert_as_expert0(idx, n_experts):
     return _orig["permute"](np.where(np.asarray(idx) < 0, 0, idx), n_experts)
 
 
-_orig = {n: getattr(O, n) for n in ("select_topk", "swiglu_ffn", "permute", "combine",
+def _plan_source_major(counts):
+    c = np.maximum(np.asarray(counts, dtype=np.int64), 0)
+    p = _orig["ep_receive_plan"](c)
+    g = np.arange(int(c.sum()))                                  # rows left in receive order
+    s = np.empty_like(g)
+    s[g] = np.arange(len(g))
+    return dict(p, gather=g, scatter=s)
+
+
+def _stats_from_chosen_only(p64, idx, n_groups):
+    p64 = np.asarray(p64, dtype=np.float64)
+    kept = np.zeros_like(p64)
+    ii = np.asarray(idx)
+    for t in range(ii.shape[0]):
+        for e in ii[t]:
+            if e >= 0:
+                kept[t, e] = p64[t, e]
+    return _orig["group_stats"](kept, idx, n_groups)
+
+
+_orig = {n: getattr(O, n) for n in ("ep_receive_plan", "group_stats", "select_topk", "swiglu_ffn", "permute", "combine",
                                     "router_logits", "softmax", "silu", "route")}
 
 MUTANTS = {
@@ -511,6 +604,8 @@ MUTANTS = {
     "dynamic_k_ignored": ("select_topk", _dynamic_k_ignored),
     "dropped_slot_keeps_expert": ("select_topk", _dropped_slot_kept),
     "no_expert_routed_to_expert_0": ("permute", _no_expert_as_expert0),
+    "receive_plan_left_source_major": ("ep_receive_plan", _plan_source_major),
+    "group_mass_of_chosen_experts_only": ("group_stats", _stats_from_chosen_only),
 }
 
 

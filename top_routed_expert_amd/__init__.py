@@ -1,12 +1,15 @@
 """MI355X-native sparse Mixture-of-Experts FFN layer (Step 3.5 Flash style).
 
 The compute path is libmoe.so: hand-written HIP kernels for gfx950 behind
-the C ABI of include/moe.h (moe_route, moe_permute, moe_expert_gate_up,
-moe_expert_down, moe_grouped_ffn, moe_combine, moe_layer_forward, moe_pack_weights). This package is its Python binding.
+the C ABI of include/moe.h (moe_route[_dynamic], moe_permute, moe_expert_gate_up,
+moe_expert_down, moe_grouped_ffn, moe_combine, moe_layer_forward[_dynamic],
+moe_pack_weights, moe_route_group_stats, moe_ep_receive_plan, moe_gather_rows).
+This package is its Python binding.
 """
 from .moe import (BF16, F32, LAYOUT_PACKED, LAYOUT_ROWS, Config, MoeError, Workspace, combine,  # noqa: F401
-                  expert_down, expert_gate_up, grouped_ffn, layer_forward, lib, pack_layer, pack_weights,
-                  packed_weights_bytes, permute, route, status_string, weights_struct)
+                  ep_receive_plan, expert_down, expert_gate_up, gather_rows, grouped_ffn, layer_forward, lib,
+                  pack_layer, pack_weights, packed_weights_bytes, permute, route, route_group_stats, status_string,
+                  weights_struct)
 
 
 def config_for(spec, packed: bool = False) -> Config:

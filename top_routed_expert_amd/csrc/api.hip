@@ -192,7 +192,8 @@ LayerWs carve_layer(Arena& a, const moe_config* c, int64_t T) {
 // ---- launch sequences ----
 
 moe_status run_route(const moe_config* c, int64_t T, const void* x, const void* w_router, const float* bias,
-                     const int32_t* k_tok, int32_t* idx, float* prob, float* gap, const RouteWs& ws, hipStream_t s) {
+                     const int32_t* k_tok, int32_t* idx, float* prob, float* gap, const RouteWs& ws, hipStream_t s,
+                     float* gmass = nullptr, int G = 0) {
   const bool fast = fast_path(c->dtype, c->d_model, 64);
   GemmArgs g{};
   g.a = x;
@@ -214,7 +215,7 @@ moe_status run_route(const moe_config* c, int64_t T, const void* x, const void* 
   g.ksplit = route_ksplit(c, T);
   g.slice_stride = T * c->n_experts;
   MOE_TRY_HIP(launch_grouped_gemm(c->dtype, fast, EPI_F32, BM, g, s), "router linear layer");
-  MOE_TRY_HIP(launch_topk(ws.logits, g.ksplit, T, c->n_experts, c->top_k, k_tok, idx, prob, gap, s),
+  MOE_TRY_HIP(launch_topk(ws.logits, g.ksplit, T, c->n_experts, c->top_k, k_tok, idx, prob, gap, gmass, G, s),
               "router top-k");
   return MOE_OK;
 }
@@ -579,6 +580,77 @@ moe_status moe_layer_forward_dynamic(const moe_config* cfg, int64_t T, const voi
   }
   // 4. weighted combine: shared + sum_k prob * routed, one rounding to out_dtype
   MOE_TRY_HIP(launch_combine(cfg->out_dtype, T, D, K, L.y, P, L.dest, prob, L.y_shared, out, s), "combine");
+  return ok();
+}
+
+size_t moe_route_group_stats_workspace_bytes(const moe_config* cfg, int64_t T, int32_t n_groups) {
+  if (check_cfg(cfg) != MOE_OK || check_tokens(cfg, T) != MOE_OK || n_groups < 1 || n_groups > 16 ||
+      cfg->n_experts % n_groups)
+    return SIZE_MAX;
+  Arena a(nullptr);
+  carve_route(a, cfg, T);
+  a.take<float>(T * n_groups);
+  return a.off;
+}
+
+moe_status moe_route_group_stats(const moe_config* cfg, int64_t T, const void* x, const void* w_router,
+                                 const float* bias, const int32_t* k_per_token, int32_t n_groups,
+                                 int32_t* topk_idx, float* topk_prob, double* stats, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_tokens(cfg, T));
+  if (n_groups < 1 || n_groups > 16 || cfg->n_experts % n_groups)
+    return fail(MOE_ERR_SHAPE, "n_groups must be in [1, 16] and divide n_experts (%d)", cfg->n_experts);
+  if (!x || !w_router || !topk_idx || !topk_prob || !stats || !ws)
+    return fail(MOE_ERR_NULL, "x, w_router, topk_idx, topk_prob, stats and ws are required");
+  if (misaligned(x) || misaligned(w_router) || misaligned(bias) || misaligned(k_per_token) || misaligned(topk_idx) ||
+      misaligned(topk_prob) || misaligned(stats) || misaligned(ws))
+    return fail(MOE_ERR_MISALIGNED, "moe_route_group_stats: a pointer is not 16-byte aligned");
+  if (cfg->dtype == MOE_BF16 && cfg->d_model % 8)
+    return fail(MOE_ERR_UNSUPPORTED, "bf16 rows need d_model % 8 == 0");
+  const size_t need = moe_route_group_stats_workspace_bytes(cfg, T, n_groups);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_route_group_stats needs %zu workspace bytes, got %zu", need, ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) {  // no tokens: the statistics kernel writes zeros (it reads nothing)
+    MOE_TRY_HIP(launch_group_stats(nullptr, nullptr, 0, cfg->top_k, cfg->n_experts, n_groups, stats, s),
+                "group statistics");
+    return ok();
+  }
+  Arena a(ws);
+  const RouteWs w = carve_route(a, cfg, T);
+  float* gmass = a.take<float>(T * n_groups);
+  MOE_TRY(run_route(cfg, T, x, w_router, bias, k_per_token, topk_idx, topk_prob, nullptr, w, s, gmass, n_groups));
+  MOE_TRY_HIP(launch_group_stats(gmass, topk_idx, T, cfg->top_k, cfg->n_experts, n_groups, stats, s),
+              "group statistics");
+  return ok();
+}
+
+moe_status moe_ep_receive_plan(int32_t n_src, int32_t n_local, const int32_t* counts, int64_t max_rows,
+                               int32_t* offsets, int32_t* gather, int32_t* scatter, void* stream) {
+  if (n_src < 1 || n_local < 1 || (int64_t)n_src * n_local > 1024)
+    return fail(MOE_ERR_SHAPE, "n_src and n_local must be >= 1 with n_src * n_local <= 1024");
+  if (max_rows < 0 || max_rows >= kMaxRows) return fail(MOE_ERR_SHAPE, "max_rows must be in [0, 2^31)");
+  if (!counts || !offsets || (max_rows > 0 && (!gather || !scatter)))
+    return fail(MOE_ERR_NULL, "counts, offsets, gather and scatter are required");
+  if (misaligned(counts) || misaligned(offsets) || misaligned(gather) || misaligned(scatter))
+    return fail(MOE_ERR_MISALIGNED, "moe_ep_receive_plan: a pointer is not 16-byte aligned");
+  MOE_TRY_HIP(launch_ep_plan(counts, n_src, n_local, max_rows, offsets, gather, scatter, (hipStream_t)stream),
+              "receive plan");
+  return ok();
+}
+
+moe_status moe_gather_rows(const void* src, int64_t n_src_rows, int64_t row_bytes, const int32_t* index,
+                           int64_t n_rows, void* dst, void* stream) {
+  if (n_rows < 0 || n_rows >= kMaxRows || row_bytes <= 0 || row_bytes > (1 << 30) || n_src_rows < 0)
+    return fail(MOE_ERR_SHAPE, "n_rows in [0, 2^31), row_bytes in [1, 2^30] and n_src_rows >= 0 are required");
+  if (n_rows == 0) return ok();
+  if (n_src_rows == 0) return fail(MOE_ERR_SHAPE, "n_rows > 0 needs n_src_rows > 0");
+  if (!src || !index || !dst) return fail(MOE_ERR_NULL, "src, index and dst are required");
+  if (misaligned(src) || misaligned(index) || misaligned(dst))
+    return fail(MOE_ERR_MISALIGNED, "moe_gather_rows: a pointer is not 16-byte aligned");
+  MOE_TRY_HIP(launch_gather_rows(src, n_src_rows, (int)row_bytes, 1, index, n_rows, dst, (hipStream_t)stream),
+              "row gather");
   return ok();
 }
 

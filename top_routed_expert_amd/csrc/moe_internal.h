@@ -114,8 +114,14 @@ hipError_t launch_grouped_gemm_big(int epi, const GemmArgs& g, hipStream_t s);
 // Logits are the sum of nsplit partial arrays [nsplit][T][E], added in slice order.
 // k_tok (optional): token t keeps its first k_tok[t] (clamped to [0, K])
 // choices; later slots get idx -1 and prob 0.
+// gmass (optional): [T][G] routing probability mass of each of G equal
+// contiguous expert groups (E % G == 0, G <= 16).
 hipError_t launch_topk(const float* logits, int nsplit, int64_t T, int E, int K, const int32_t* k_tok, int32_t* idx,
-                       float* prob, float* gap, hipStream_t s);
+                       float* prob, float* gap, float* gmass, int G, hipStream_t s);
+// out [2G] fp64: per-group probability mass summed over tokens, then the
+// number of chosen pairs per group.
+hipError_t launch_group_stats(const float* gmass, const int32_t* idx, int64_t T, int K, int E, int G, double* out,
+                              hipStream_t s);
 
 // permute.hip. Pairs with idx outside [0, E) get dest -1 and no row.
 // offsets_ext [E+3] (optional), the row groups of the fused expert launch:
@@ -134,6 +140,9 @@ hipError_t launch_permute_small(const int32_t* idx, int64_t T, int K, int E, int
                                 int32_t* n_tiles, int32_t max_tiles, int block_rows, hipStream_t s);
 hipError_t launch_gather_rows(const void* x, int64_t T, int D, int elem_bytes, const int32_t* sorted_token,
                               int64_t rows, void* x_perm, hipStream_t s);
+// Expert-parallel receive plan (see moe_ep_receive_plan in include/moe.h).
+hipError_t launch_ep_plan(const int32_t* counts, int n_src, int n_local, int64_t max_rows, int32_t* offsets,
+                          int32_t* gather, int32_t* scatter, hipStream_t s);
 
 // pack.hip: n_mats row-major [rows, cols] bf16 matrices -> packed fragment
 // layout (rows rounded up to a multiple of 16, zero-filled), matrix after

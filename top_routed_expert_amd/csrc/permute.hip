@@ -244,7 +244,64 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
   if (tid == 1023) *n_tiles = n_all < max_tiles ? n_all : max_tiles;
 }
 
+// Receive plan of one GPU's share under expert parallelism (page "Step3.5
+// Flash 大模型技术深度解析", section 3.2.3: the experts in G groups, one group
+// per GPU). The receive buffer of the dispatch exchange holds one chunk per
+// (source rank r, local expert e), r-major, counts[r * n_local + e] rows each,
+// rows in the source's token order. Expert-major order takes the experts in
+// turn, inside an expert the sources in turn, inside a chunk its rows in turn:
+// expert-major row q reads receive row gather[q], receive row i holds
+// expert-major row scatter[i], and offsets [n_local+1] bound the experts'
+// segments. Every block rebuilds both chunk scans in LDS (at most 1024
+// chunks), then maps receive rows grid-stride, finding each row's chunk by
+// binary search. Rows at or past max_rows are not written.
+__global__ void __launch_bounds__(1024) ep_plan_kernel(const int32_t* __restrict__ counts, int n_src, int n_local,
+                                                       int64_t max_rows, int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ gather, int32_t* __restrict__ scatter) {
+  __shared__ int s_rcv[1025];  // receive-order start of chunk c = r * n_local + e; s_rcv[n] = total
+  __shared__ int s_em[1024];   // expert-major start of chunk c
+  __shared__ int s_tot[16];
+  const int tid = threadIdx.x, n = n_src * n_local;
+  const int cnt = tid < n ? max(counts[tid], 0) : 0;
+  int total;
+  const int rcv = block1024_excl_scan(cnt, s_tot, &total);
+  if (tid < n) s_rcv[tid] = rcv;
+  if (tid == 0) s_rcv[n] = total;
+  __syncthreads();  // s_tot is reused
+  // expert-major position p = e * n_src + r holds chunk r * n_local + e
+  const int pe = tid / n_src, pr = tid - pe * n_src;
+  const int cnt_em = tid < n ? max(counts[pr * n_local + pe], 0) : 0;
+  int total_em;
+  const int em = block1024_excl_scan(cnt_em, s_tot, &total_em);
+  if (tid < n) s_em[pr * n_local + pe] = em;
+  if (blockIdx.x == 0) {
+    if (tid < n && pr == 0) offsets[pe] = em;
+    if (tid == 0) offsets[n_local] = total_em;
+  }
+  __syncthreads();
+  const int64_t rows = total < max_rows ? total : max_rows;
+  for (int64_t i = (int64_t)blockIdx.x * 1024 + tid; i < rows; i += (int64_t)gridDim.x * 1024) {
+    int lo = 0, hi = n - 1;  // the last chunk starting at or before i (it holds row i)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_rcv[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    const int64_t q = (int64_t)s_em[lo] + (i - s_rcv[lo]);
+    scatter[i] = (int32_t)q;
+    if (q < max_rows) gather[q] = (int32_t)i;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_ep_plan(const int32_t* counts, int n_src, int n_local, int64_t max_rows, int32_t* offsets,
+                          int32_t* gather, int32_t* scatter, hipStream_t s) {
+  int64_t blocks = (max_rows + 1023) / 1024;
+  blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
+  ep_plan_kernel<<<(unsigned)blocks, 1024, 0, s>>>(counts, n_src, n_local, max_rows, offsets, gather, scatter);
+  return hipGetLastError();
+}
 
 bool permute_small_fits(int64_t T, int K, int E) { return T * K <= 1024 && E <= 1022; }
 

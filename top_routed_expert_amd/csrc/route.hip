@@ -108,7 +108,7 @@ template <int VPL>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int nsplit, int64_t T, int E,
                                                    int K, const int32_t* __restrict__ k_tok,
                                                    int32_t* __restrict__ idx, float* __restrict__ prob,
-                                                   float* __restrict__ gap) {
+                                                   float* __restrict__ gap, float* __restrict__ gmass, int G) {
   __shared__ float s_logit[1024];
   __shared__ float s_part[4096];
   const int lane = threadIdx.x & 63;
@@ -143,6 +143,22 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     s += v[j];
   }
   s = wave_sum(s);
+
+  // optional: the token's routing probability mass per expert group (G
+  // equal contiguous groups), for the expert-parallel balance statistics
+  if (gmass) {
+    const int gs = E / G;
+    for (int g = 0; g < G; ++g) {
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const int e = lane + 64 * j;
+        if (e < E && e / gs == g) a += v[j] / s;
+      }
+      a = wave_sum(a);
+      if (lane == 0) gmass[t * G + g] = a;
+    }
+  }
 
   unsigned long long key[VPL];
 #pragma unroll
@@ -189,14 +205,56 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     }
 }
 
+// Expert-parallel balance statistics (page "Step3.5 Flash 大模型技术深度解析",
+// section 3.2.3: 288 experts in G groups, one group per GPU; the balance
+// loss L_EP = G * sum_g f_g p_g). Block g sums, over all tokens in a fixed
+// order (thread i takes tokens i, i+256, ..., then a fixed-shape tree), the
+// group's probability mass gmass[t][g] and its number of chosen pairs, in
+// fp64: out[g] = sum_t p_g(t), out[G + g] = #{(t, k): idx[t,k] in group g}.
+__global__ void __launch_bounds__(256) group_stats_kernel(const float* __restrict__ gmass,
+                                                          const int32_t* __restrict__ idx, int64_t T, int K, int E,
+                                                          int G, double* __restrict__ out) {
+  __shared__ double s_m[256], s_c[256];
+  const int g = blockIdx.x, tid = threadIdx.x, gs = E / G;
+  double m = 0.0, c = 0.0;
+  for (int64_t t = tid; t < T; t += 256) {
+    m += (double)gmass[t * G + g];
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[t * K + k];
+      c += (e >= 0 && e < E && e / gs == g) ? 1.0 : 0.0;
+    }
+  }
+  s_m[tid] = m;
+  s_c[tid] = c;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) {
+      s_m[tid] += s_m[tid + w];
+      s_c[tid] += s_c[tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    out[g] = s_m[0];
+    out[G + g] = s_c[0];
+  }
+}
+
 }  // namespace
 
+hipError_t launch_group_stats(const float* gmass, const int32_t* idx, int64_t T, int K, int E, int G, double* out,
+                              hipStream_t s) {
+  group_stats_kernel<<<G, 256, 0, s>>>(gmass, idx, T, K, E, G, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const float* logits, int nsplit, int64_t T, int E, int K, const int32_t* k_tok, int32_t* idx,
-                       float* prob, float* gap, hipStream_t s) {
+                       float* prob, float* gap, float* gmass, int G, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)(nsplit > 1 ? T : (T + 3) / 4);
   const int vpl = (E + 63) / 64;
-#define MOE_TOPK(V) topk_kernel<V><<<blocks, 256, 0, s>>>(logits, nsplit, T, E, K, k_tok, idx, prob, gap)
+#define MOE_TOPK(V) \
+  topk_kernel<V><<<blocks, 256, 0, s>>>(logits, nsplit, T, E, K, k_tok, idx, prob, gap, gmass, G)
   if (vpl <= 1) MOE_TOPK(1);
   else if (vpl <= 2) MOE_TOPK(2);
   else if (vpl <= 3) MOE_TOPK(3);

@@ -64,6 +64,10 @@ _SIGS = {
     "moe_layer_forward": ([_CFG, _I64, _P, ctypes.POINTER(MoeWeights), _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "moe_layer_forward_dynamic": ([_CFG, _I64, _P, ctypes.POINTER(MoeWeights), _P, _P, _P, _P, _P, _P, _SZ, _P],
                                   ctypes.c_int),
+    "moe_route_group_stats_workspace_bytes": ([_CFG, _I64, _I32], _SZ),
+    "moe_route_group_stats": ([_CFG, _I64, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "moe_ep_receive_plan": ([_I32, _I32, _P, _I64, _P, _P, _P, _P], ctypes.c_int),
+    "moe_gather_rows": ([_P, _I64, _I64, _P, _I64, _P, _P], ctypes.c_int),
     "moe_packed_weights_bytes": ([_I64, _I64, _I64], _SZ),
     "moe_pack_weights": ([_I64, _I64, _I64, _P, _P, _SZ, _P], ctypes.c_int),
 }
@@ -305,6 +309,52 @@ class Workspace:
         c = cfg.c()
         self.nbytes = lib().moe_layer_workspace_bytes(ctypes.byref(c), T)
         self.buf = _workspace(self.nbytes, device)
+
+
+def route_group_stats(cfg: Config, x: torch.Tensor, w_router: torch.Tensor, n_groups: int,
+                      bias: torch.Tensor | None = None, k_per_token: torch.Tensor | None = None):
+    """moe_route_group_stats: (topk_idx, topk_prob, stats [2G] fp64: group probability mass, pair counts)."""
+    T = x.shape[0]
+    dev = x.device
+    c = cfg.c()
+    idx = torch.empty((T, cfg.top_k), dtype=torch.int32, device=dev)
+    prob = torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev)
+    stats = torch.empty((2 * n_groups,), dtype=torch.float64, device=dev)
+    ws = _workspace(lib().moe_route_group_stats_workspace_bytes(ctypes.byref(c), T, n_groups), dev)
+    _check(lib().moe_route_group_stats(
+        ctypes.byref(c), T, _ptr(x, "x", cfg.dtype, (T, cfg.d_model)),
+        _ptr(w_router, "w_router", cfg.dtype, cfg.wshape(cfg.n_experts, cfg.d_model), dev),
+        _ptr(bias, "bias", torch.float32, (cfg.n_experts,), dev),
+        _ptr(k_per_token, "k_per_token", torch.int32, (T,), dev), n_groups, _ptr(idx, "idx"), _ptr(prob, "prob"),
+        _ptr(stats, "stats"), ws.data_ptr(), ws.numel(), _stream(dev)), "moe_route_group_stats")
+    return idx, prob, stats
+
+
+def ep_receive_plan(counts: torch.Tensor, max_rows: int):
+    """moe_ep_receive_plan: counts [n_src, n_local] int32 -> (offsets [n_local+1], gather, scatter [max_rows])."""
+    n_src, n_local = counts.shape
+    dev = counts.device
+    offsets = torch.empty((n_local + 1,), dtype=torch.int32, device=dev)
+    gather = torch.empty((max(max_rows, 1),), dtype=torch.int32, device=dev)
+    scatter = torch.empty((max(max_rows, 1),), dtype=torch.int32, device=dev)
+    _check(lib().moe_ep_receive_plan(n_src, n_local, _ptr(counts.contiguous(), "counts", torch.int32), max_rows,
+                                     _ptr(offsets, "offsets"), _ptr(gather, "gather"), _ptr(scatter, "scatter"),
+                                     _stream(dev)), "moe_ep_receive_plan")
+    return offsets, gather[:max_rows], scatter[:max_rows]
+
+
+def gather_rows(src: torch.Tensor, index: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """moe_gather_rows: out[i] = src[index[i]] (rows of src's trailing dimensions)."""
+    n = index.shape[0]
+    dev = src.device
+    if out is None:
+        out = torch.empty((n, *src.shape[1:]), dtype=src.dtype, device=dev)
+    row_bytes = src[0].numel() * src.element_size() if src.shape[0] else out[0].numel() * out.element_size()
+    _check(lib().moe_gather_rows(_ptr(src, "src", None, None, dev), src.shape[0], row_bytes,
+                                 _ptr(index, "index", torch.int32, (n,), dev), n,
+                                 _ptr(out, "out", src.dtype, (n, *src.shape[1:]), dev), _stream(dev)),
+           "moe_gather_rows")
+    return out
 
 
 def layer_forward(cfg: Config, x: torch.Tensor, w: dict, out: torch.Tensor | None = None,
