@@ -79,6 +79,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="fp8 (E4M3) vs bf16 expert weights at decode and prefill, one JSON line each")
     ap.add_argument("--ep-share", action="store_true",
                     help="one GPU's expert-parallel share (36 experts, 8 ranks x 8192 tokens), one JSON line")
     ap.add_argument("--dynamic-k", action="store_true",
@@ -262,6 +264,49 @@ def sweep(steps, warmup, flush_on):
                           "experts_touched": touched, "tile_rows": tile_kernel(T, spec)}), flush=True)
 
 
+def fp8_weights(steps, warmup, flush_on):
+    """FP8 (E4M3, per-row scales) expert weights against bf16 at the decode and prefill workloads: one
+    JSON line per (workload, weights), whole-layer figures; bytes count the weights as stored."""
+    import numpy as np
+    import torch
+
+    import synth
+    import top_routed_expert_amd as moe
+
+    for name in ("decode", "prefill"):
+        spec = synth.spec(name)
+        L = synth.make_layer(spec, "cuda")
+        dev = L["x"].device
+        T, D, E, F, Fs = spec.T, spec.D, spec.E, spec.F, spec.Fs
+        for mode in ("bf16", "fp8"):
+            cfg = moe.config_for(spec, packed=True, fp8=(mode == "fp8"))
+            W = moe.quantize_layer(L) if mode == "fp8" else moe.pack_layer(L)
+            ws = moe.Workspace(cfg, T, dev)
+            wt = moe.weights_struct(cfg, W)
+            out = torch.empty((T, D), dtype=cfg.odtype, device=dev)
+            ms, _ = timed(lambda: moe.layer_forward(cfg, L["x"], W, out=out, workspace=ws, weights=wt),
+                          steps, warmup, Flusher(flush_on))
+            ms_step = float(np.mean(ms))
+            idx, _ = moe.route(cfg, L["x"], W["w_router"], L["bias"])
+            offs, _, _ = moe.permute(cfg, idx)
+            counts = np.diff(offs.cpu().numpy())
+            flops, nbytes, touched = layer_flops_bytes(spec, counts)
+            if mode == "fp8":  # expert matrices at 1 byte per weight plus one fp32 scale per row
+                ex = touched * (2 * F + D) + (2 * Fs + D)
+                nbytes -= (touched * 3 * D * F + 3 * D * Fs) * 2
+                nbytes += (touched * 3 * D * F + 3 * D * Fs) + ex * 4
+            print(json.dumps({"workload": name, "T": T, "weights": mode, "ms_per_step": round(ms_step, 5),
+                              "tokens_per_s": round(T / (ms_step * 1e-3), 1), "experts_touched": touched,
+                              "bytes": int(nbytes), "gbs": round(nbytes / (ms_step * 1e-3) / 1e9, 1),
+                              "hbm_frac": round(nbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "mfma_frac": round(flops / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}),
+                  flush=True)
+            del W, ws, wt
+            torch.cuda.empty_cache()
+        del L
+        torch.cuda.empty_cache()
+
+
 def dynamic_topk(steps, warmup, flush_on):
     """Dynamic top-k (4 or 8 experts per token, seeded, about half each) against fixed top-8 at the
     decode and prefill workloads: one JSON line per (workload, mode), whole-layer figures."""
@@ -406,6 +451,11 @@ def main():
 
     import synth
 
+    if args.fp8:
+        print(f"[bench] fp8 vs bf16 expert weights, steps={args.steps} warmup={args.warmup}", file=sys.stderr,
+              flush=True)
+        fp8_weights(args.steps, args.warmup, not args.no_flush)
+        return
     if args.ep_share:
         print(f"[bench] expert-parallel share, steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
         print(json.dumps(ep_share(args.steps, args.warmup, not args.no_flush)), flush=True)

@@ -63,7 +63,7 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Storage layout of the weight matrices (see "Packed weights" below). */
-typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_PACKED = 1 } moe_weight_layout;
+typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_PACKED = 1, MOE_LAYOUT_FP8 = 2 } moe_weight_layout;
 
 /* Shape of one layer (section 3.2.1 / 3.2.2 of the page above). */
 typedef struct {
@@ -84,7 +84,11 @@ typedef struct {
  *   w_up        [E, F, D]   routed experts, up projection
  *   w_down      [E, D, F]   routed experts, down projection
  *   s_gate      [Fs, D], s_up [Fs, D], s_down [D, Fs]: the shared expert
- *               (ignored when d_shared == 0).                              */
+ *               (ignored when d_shared == 0).
+ *   *_scale     per-row fp32 scales of the expert matrices, used only with
+ *               MOE_LAYOUT_FP8 (below): w_gate_scale, w_up_scale [E, F],
+ *               w_down_scale [E, D], s_gate_scale, s_up_scale [Fs],
+ *               s_down_scale [D]; NULL otherwise.                           */
 typedef struct {
   const void* w_router;
   const float* router_bias;
@@ -94,6 +98,12 @@ typedef struct {
   const void* s_gate;
   const void* s_up;
   const void* s_down;
+  const float* w_gate_scale;
+  const float* w_up_scale;
+  const float* w_down_scale;
+  const float* s_gate_scale;
+  const float* s_up_scale;
+  const float* s_down_scale;
 } moe_weights;
 
 /* Packed weights
@@ -122,6 +132,38 @@ typedef struct {
 size_t moe_packed_weights_bytes(int64_t n_mats, int64_t rows, int64_t cols);
 moe_status moe_pack_weights(int64_t n_mats, int64_t rows, int64_t cols, const void* src, void* dst,
                             size_t dst_bytes, void* stream);
+
+/* FP8 expert weights
+ * ------------------
+ * With cfg->weight_layout == MOE_LAYOUT_FP8 the expert matrices (w_gate,
+ * w_up, w_down, s_gate, s_up, s_down) are OCP FP8 E4M3 codes written by
+ * moe_quantize_fp8, with one fp32 scale per matrix row (output channel) in
+ * the *_scale fields of moe_weights; the weight the layer uses is
+ * decode(code) * scale. Activations stay bf16 (dtype MOE_BF16), the router
+ * stays bf16 in the packed layout (moe_pack_weights), and the widths must be
+ * multiples of 64. Page "Step3.5 Flash 大模型技术深度解析", section 8.1,
+ * deploys the model with FP8/FP16 weights. The expert GEMMs read half the
+ * weight bytes and convert to bf16 in registers; they use row tiles of 32,
+ * 64 or 128 rows (the 256 x 256 kernel is bf16 only). Only
+ * moe_layer_forward and moe_layer_forward_dynamic take fp8 weights (the
+ * grouped expert entry points have no scale arguments: MOE_ERR_UNSUPPORTED).
+ *
+ * Layout of the codes of W [rows, cols] (cols % 64 == 0): fragments of 16
+ * rows x 64 columns (1 KB), ct-major then kb; lane l = c + 16q (c < 16,
+ * q < 4) of fragment (ct, kb) holds, at byte 16l, the codes of row 16ct + c
+ * at columns 64kb + 8q .. +7, then at 64kb + 32 + 8q .. +7. Rows past
+ * `rows` (when rows % 16 != 0) hold zero codes.
+ *
+ * moe_fp8_weights_bytes: n_mats * ceil(rows/16)*16 * cols; SIZE_MAX when a
+ *   size is negative or cols % 64 != 0.
+ * moe_quantize_fp8: src [n_mats, rows, cols] bf16 row-major -> dst codes
+ *   (>= moe_fp8_weights_bytes bytes) and scales [n_mats, rows] fp32. Per row:
+ *   scale = max|w| / 448 in fp32 (1 for an all-zero row); code = the E4M3
+ *   value nearest to fp32(w / scale), ties to the even code, magnitudes
+ *   above 448 saturating. */
+size_t moe_fp8_weights_bytes(int64_t n_mats, int64_t rows, int64_t cols);
+moe_status moe_quantize_fp8(int64_t n_mats, int64_t rows, int64_t cols, const void* src, void* dst,
+                            size_t dst_bytes, float* scales, void* stream);
 
 /* Workspace queries. They return the bytes the matching entry point needs
  * in its `ws` argument, or SIZE_MAX when the configuration is invalid. */

@@ -46,7 +46,15 @@ notes):
      tokens of the softmax mass of group g's experts, so both sum to 1 and a
      perfectly balanced routing gives L_EP = 1. One GPU's share receives, per
      source rank r and local expert e, that source's rows for e in token
-     order, chunks r-major; its experts run on them in expert-major order.
+     order, chunks r-major; its experts run on them in expert-major order;
+  R14 FP8 expert weights (page "Step3.5 Flash 大模型技术深度解析", section 8.1,
+     deploys the model with FP8/FP16 weights): each expert matrix row (one
+     output channel) is stored as OCP FP8 E4M3 codes q with one float32
+     scale s = float32(max|w| / 448) (1 for an all-zero row); q = the E4M3
+     value nearest to float32(w / s), ties to the even code, magnitudes
+     above 448 saturating to 448. The weight the layer uses is
+     decode(q) * s; activations stay bfloat16 and the router is not
+     quantised.
 """
 from __future__ import annotations
 
@@ -339,3 +347,60 @@ def ep_receive_plan(counts) -> dict:
     scatter = np.empty_like(gather)
     scatter[gather] = np.arange(len(gather))
     return dict(offsets=np.array(offsets, dtype=np.int64), gather=gather, scatter=scatter)
+
+
+# ------------------------------------------------------------ FP8 weights ---
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """OCP FP8 E4M3 code -> value (float64): 1 sign bit, 4 exponent bits with
+    bias 7, 3 mantissa bits; exponent 0 is subnormal (m * 2^-9); S.1111.111
+    is NaN; there are no infinities (R14)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e, m = (c >> 3) & 0xF, c & 7
+    v = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.where((e == 15) & (m == 7), np.nan, sign * v)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """float32 values -> E4M3 codes (uint8): the nearest finite E4M3 value,
+    ties to the even code, magnitudes above 448 saturating to 448 (R14).
+
+    Within the binade [2^e, 2^(e+1)) of |v| (e >= -6; below 2^-6 the
+    subnormal spacing) E4M3 values are the multiples of 2^(e-3); |v| is
+    rounded to the nearest multiple, ties to the even multiple, which is the
+    even code. Every step is an exact power-of-two scaling (float32 suffices).
+    """
+    v = np.asarray(v, dtype=np.float32)
+    a = np.minimum(np.abs(v), np.float32(E4M3_MAX))
+    _, ex = np.frexp(a)                             # a = f 2^ex, f in [0.5, 1): binade ex - 1
+    step = np.ldexp(np.float32(1.0), np.maximum(ex - 1, -6) - 3)
+    r = np.minimum(np.rint(a / step) * step, np.float32(E4M3_MAX))
+    _, ex2 = np.frexp(r)
+    normal = r >= np.float32(2.0 ** -6)
+    m = np.where(normal, np.rint(np.ldexp(r, 4 - ex2)) - 8, np.rint(np.ldexp(r, 9))).astype(np.int32)
+    code = np.where(normal, ((ex2 - 1 + 7) << 3) + m, m)     # 3-bit mantissa, or m 2^-9 below 2^-6
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_rows_fp8(w) -> tuple:
+    """Per-row FP8 quantisation of w [..., rows, cols] (R14): (codes uint8, scales float32 [..., rows])."""
+    if _torch is not None and isinstance(w, _torch.Tensor):
+        w32 = w.detach().cpu().float().numpy()    # bf16 / fp32 values are exact in float32
+    else:
+        w32 = np.asarray(w, dtype=np.float32)
+    amax = np.abs(w32).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q = e4m3_encode((w32 / scale[..., None]).astype(np.float32))
+    return q, scale
+
+
+_E4M3_ALL = e4m3_decode(np.arange(256))
+
+
+def dequantize_fp8(codes, scales) -> np.ndarray:
+    """decode(q) * s in float64 (exact; decode through the table of all 256 codes)."""
+    return _E4M3_ALL[np.asarray(codes, dtype=np.int64)] * np.asarray(scales, dtype=np.float64)[..., None]

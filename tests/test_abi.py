@@ -22,7 +22,7 @@ OK, NULL, SHAPE, UNSUP, WS, MISALIGNED, HIP = range(7)
 def header_functions() -> list[str]:
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def cfg(**kw) -> M.MoeConfig:
@@ -38,7 +38,7 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails its checks
 def test_exports_every_declared_function():
     L = moe.lib()
     names = header_functions()
-    assert len(names) == 22, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(L, n), f"libmoe.so does not export {n}"
     assert set(names) == set(M._SIGS), "binding signatures out of sync with the header"
@@ -96,7 +96,8 @@ def test_packed_weights_queries_and_checks():
     assert call(dst=FAKE + 8) == MISALIGNED
     assert call(nb=need - 1) == WS and str(need) in _last()
     # packed layout needs bf16 and widths multiple of 64
-    for bad in (cfg(weight_layout=2), cfg(weight_layout=moe.LAYOUT_PACKED, dtype=moe.F32),
+    for bad in (cfg(weight_layout=3), cfg(weight_layout=moe.LAYOUT_PACKED, dtype=moe.F32),
+                cfg(weight_layout=moe.LAYOUT_FP8, dtype=moe.F32), cfg(weight_layout=moe.LAYOUT_FP8, d_expert=96),
                 cfg(weight_layout=moe.LAYOUT_PACKED, d_model=320 - 32), cfg(weight_layout=moe.LAYOUT_PACKED, d_expert=96)):
         assert L.moe_layer_workspace_bytes(ctypes.byref(bad), 10) == M.SIZE_MAX
     good = cfg(weight_layout=moe.LAYOUT_PACKED)
@@ -260,3 +261,32 @@ def test_dynamic_and_expert_parallel_entry_checks():
     assert gat(rb=0) == SHAPE and gat(n=-1) == SHAPE and gat(ns=0) == SHAPE
     assert gat(n=0, src=None) == OK
     assert gat(idx=None) == NULL and gat(dst=FAKE + 2) == MISALIGNED
+
+
+def test_fp8_queries_and_checks():
+    L = moe.lib()
+    # n_mats * ceil(rows/16)*16 * cols bytes, cols a multiple of 64
+    assert L.moe_fp8_weights_bytes(288, 1280, 4096) == 288 * 1280 * 4096
+    assert L.moe_fp8_weights_bytes(2, 20, 64) == 2 * 32 * 64
+    assert L.moe_fp8_weights_bytes(1, 16, 96) == M.SIZE_MAX and L.moe_fp8_weights_bytes(-1, 16, 64) == M.SIZE_MAX
+    need = L.moe_fp8_weights_bytes(2, 20, 64)
+    call = lambda n=2, r=20, c=64, src=FAKE, dst=FAKE, nb=need, sc=FAKE: \
+        L.moe_quantize_fp8(n, r, c, src, dst, nb, sc, None)
+    assert call(c=96) == SHAPE and call(r=-1) == SHAPE
+    assert call(n=0) == OK
+    assert call(sc=None) == NULL and call(src=None) == NULL
+    assert call(dst=FAKE + 8) == MISALIGNED
+    assert call(nb=need - 1) == WS and str(need) in _last()
+    # fp8 weights reach the kernels only through the layer (which takes their scales)
+    f8 = cfg(weight_layout=moe.LAYOUT_FP8)
+    assert L.moe_layer_workspace_bytes(ctypes.byref(f8), 10) != M.SIZE_MAX
+    ws = L.moe_expert_workspace_bytes(ctypes.byref(f8), 4, 64, 128)
+    assert L.moe_expert_gate_up(ctypes.byref(f8), 4, 64, FAKE, FAKE, 64, None, 0, FAKE, FAKE, None, None, 128, FAKE,
+                                FAKE, ws, None) == UNSUP and "fp8" in _last()
+    lw = L.moe_layer_workspace_bytes(ctypes.byref(f8), 8)
+    w = M.MoeWeights(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)   # scales missing
+    assert L.moe_layer_forward(ctypes.byref(f8), 8, FAKE, ctypes.byref(w), FAKE, None, None, None, FAKE, lw,
+                               None) == NULL and "scale" in _last()
+    w = M.MoeWeights(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4)
+    assert L.moe_layer_forward(ctypes.byref(f8), 8, FAKE, ctypes.byref(w), FAKE, None, None, None, FAKE, lw,
+                               None) == MISALIGNED

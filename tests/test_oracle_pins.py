@@ -424,6 +424,52 @@ def pin_ep_share_composition():
         assert np.allclose(y_recv, np.array(want).reshape(-1, D), rtol=1e-12, atol=1e-14)
 
 
+def pin_fp8_codec():
+    """OCP E4M3 values the format fixes, rounding ties to even, saturation, subnormals, round trip."""
+    d = O.e4m3_decode
+    assert d(0x38) == 1.0 and d(0x3C) == 1.5 and d(0xB8) == -1.0 and d(0x40) == 2.0
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0 and np.isnan(d(0x7F)) and np.isnan(d(0xFF))
+    assert d(0x08) == 2.0 ** -6 and d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9 and d(0x00) == 0.0
+    assert d(0x30) == 0.5 and d(0x37) == 0.9375 and d(0x77) == 240.0
+    pos = d(np.arange(127))
+    assert np.all(np.diff(pos) > 0)                                       # codes 0..126 increase
+    enc = lambda *v: O.e4m3_encode(np.float32(v)).tolist()
+    assert enc(1.0625, 1.1875, 0.96875) == [0x38, 0x3A, 0x38]             # ties go to the even code
+    assert enc(1.06, 1.07) == [0x38, 0x39]                                # otherwise the nearest
+    assert enc(449.0, 464.0, 1e30, -3e5) == [0x7E, 0x7E, 0x7E, 0xFE]      # saturation, no NaN
+    assert enc(1.5 * 2 ** -9, 2.5 * 2 ** -9, 2 ** -11, 7.5 * 2 ** -9) == [0x02, 0x02, 0x00, 0x08]
+    assert enc(0.0, -0.0) == [0x00, 0x80]
+    c = np.arange(256)
+    fin = ~np.isnan(d(c))
+    assert np.array_equal(O.e4m3_encode(d(c)[fin].astype(np.float32)), c[fin].astype(np.uint8))
+    # against the decoded set by brute force: the nearest value, ties to the even code
+    rng = np.random.default_rng(17)
+    v = np.float32(rng.standard_normal(300) * np.exp(rng.uniform(-9, 6, 300)))
+    q = O.e4m3_encode(v)
+    for x, code in zip(v.tolist(), q.tolist()):
+        a = min(abs(x), 448.0)
+        best = min(range(127), key=lambda k: (abs(float(pos[k]) - a), k % 2))
+        assert code & 0x7F == best and (code >> 7) == (1 if math.copysign(1, x) < 0 else 0)
+
+
+def pin_fp8_quantisation():
+    """Per-row scales: the largest magnitude of each row lands on 448; zero rows keep scale 1."""
+    rng = np.random.default_rng(19)
+    w = rng.standard_normal((2, 6, 64)).astype(np.float32) * np.float32(rng.uniform(0.01, 3, (2, 6, 1)))
+    w[1, 2] = 0.0
+    q, s = O.quantize_rows_fp8(w)
+    assert q.dtype == np.uint8 and s.dtype == np.float32 and q.shape == w.shape and s.shape == (2, 6)
+    amax = np.abs(w).max(axis=-1)
+    assert s[1, 2] == 1.0 and np.all(q[1, 2] == 0)
+    nz = amax > 0
+    assert np.array_equal(s[nz], (amax[nz] / np.float32(448)).astype(np.float32))
+    assert np.all(np.abs(O.e4m3_decode(q)).max(axis=-1)[nz] == 448.0)
+    # the dequantised weights stay within half a step of E4M3 (relative 2^-4) plus the subnormal step
+    wd = O.dequantize_fp8(q, s)
+    step = np.maximum(np.abs(w.astype(np.float64)) * 2.0 ** -4, s[..., None] * 2.0 ** -10)
+    assert np.all(np.abs(wd - w) <= step + 1e-30)
+
+
 def pin_page_constants():
     """The page's structural numbers, and the width reading they force."""
     g = json.load(open(os.path.join(GOLDEN, "step35_layer_constants.json")))["values"]
@@ -449,7 +495,8 @@ def pin_page_constants():
 PINS = [pin_route_bruteforce, pin_route_ties, pin_route_properties, pin_route_bias, pin_permute,
         pin_ffn_closed_form, pin_ffn_bruteforce, pin_layer_worked_example,
         pin_layer_special_cases, pin_dynamic_topk_route, pin_dynamic_topk_permute, pin_dynamic_topk_layer,
-        pin_ep_receive_plan, pin_group_stats, pin_ep_share_composition, pin_page_constants]
+        pin_ep_receive_plan, pin_group_stats, pin_ep_share_composition, pin_fp8_codec, pin_fp8_quantisation,
+        pin_page_constants]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -585,7 +632,23 @@ def _stats_from_chosen_only(p64, idx, n_groups):
     return _orig["group_stats"](kept, idx, n_groups)
 
 
-_orig = {n: getattr(O, n) for n in ("ep_receive_plan", "group_stats", "select_topk", "swiglu_ffn", "permute", "combine",
+def _encode_truncating(v):
+    v = np.asarray(v, dtype=np.float32)
+    pos = O.e4m3_decode(np.arange(127))
+    a = np.minimum(np.abs(v.astype(np.float64)), 448.0)
+    code = np.clip(np.searchsorted(pos, a, side="right") - 1, 0, 126)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def _scale_by_max(w):
+    q, s = _orig["quantize_rows_fp8"](w)
+    w32 = O.as_f64(w).astype(np.float32)
+    amax = np.abs(w32).max(axis=-1)
+    s2 = np.where(amax > 0, amax, np.float32(1)).astype(np.float32)
+    return O.e4m3_encode((w32 / s2[..., None]).astype(np.float32)), s2
+
+
+_orig = {n: getattr(O, n) for n in ("quantize_rows_fp8", "ep_receive_plan", "group_stats", "select_topk", "swiglu_ffn", "permute", "combine",
                                     "router_logits", "softmax", "silu", "route")}
 
 MUTANTS = {
@@ -606,6 +669,8 @@ MUTANTS = {
     "no_expert_routed_to_expert_0": ("permute", _no_expert_as_expert0),
     "receive_plan_left_source_major": ("ep_receive_plan", _plan_source_major),
     "group_mass_of_chosen_experts_only": ("group_stats", _stats_from_chosen_only),
+    "fp8_encode_truncates": ("e4m3_encode", _encode_truncating),
+    "fp8_scale_without_448": ("quantize_rows_fp8", _scale_by_max),
 }
 
 

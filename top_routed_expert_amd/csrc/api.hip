@@ -78,15 +78,20 @@ moe_status check_cfg(const moe_config* c) {
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "dtype %d", c->dtype);
   if (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "out_dtype %d", c->out_dtype);
-  if (c->weight_layout != MOE_LAYOUT_ROWS && c->weight_layout != MOE_LAYOUT_PACKED)
+  if (c->weight_layout != MOE_LAYOUT_ROWS && c->weight_layout != MOE_LAYOUT_PACKED &&
+      c->weight_layout != MOE_LAYOUT_FP8)
     return fail(MOE_ERR_UNSUPPORTED, "weight_layout %d", c->weight_layout);
-  if (c->weight_layout == MOE_LAYOUT_PACKED &&
+  if (c->weight_layout != MOE_LAYOUT_ROWS &&
       (c->dtype != MOE_BF16 || c->d_model % 64 || c->d_expert % 64 || c->d_shared % 64))
-    return fail(MOE_ERR_UNSUPPORTED, "packed weights need bf16 and d_model, d_expert, d_shared multiples of 64");
+    return fail(MOE_ERR_UNSUPPORTED,
+                "packed and fp8 weights need bf16 and d_model, d_expert, d_shared multiples of 64");
   return MOE_OK;
 }
 
-bool packed(const moe_config* c) { return c->weight_layout == MOE_LAYOUT_PACKED; }
+// bf16 weights in the packed layout: every weight with MOE_LAYOUT_PACKED, the
+// router with MOE_LAYOUT_FP8 (only expert matrices are fp8)
+bool packed(const moe_config* c) { return c->weight_layout != MOE_LAYOUT_ROWS; }
+bool fp8(const moe_config* c) { return c->weight_layout == MOE_LAYOUT_FP8; }
 
 moe_status check_tokens(const moe_config* c, int64_t T) {
   if (T < 0) return fail(MOE_ERR_SHAPE, "T = %lld < 0", (long long)T);
@@ -136,7 +141,8 @@ SchedWs carve_sched(Arena& a, const moe_config* c, int n_groups, int64_t n_rows,
   // 256-row tiles need contractions of at least 128 and A offsets that fit
   // 32 bits in 16-byte units (A has at most n_rows rows of either width)
   const int64_t kmax = c->d_model > d_ff ? c->d_model : d_ff;
-  const bool big_ok = c->d_model >= 128 && d_ff >= 128 && (uint64_t)n_rows * (uint64_t)kmax / 8u <= 0xffffffffull;
+  const bool big_ok = c->d_model >= 128 && d_ff >= 128 && !fp8(c) &&
+                      (uint64_t)n_rows * (uint64_t)kmax / 8u <= 0xffffffffull;
   w.block_rows = gemm_block_rows(w.fast, n_rows, n_groups, big_ok);
   w.max_tiles = (int32_t)gemm_max_tiles(n_rows, n_groups, w.block_rows);
   w.tiles = a.take<Tile>(w.max_tiles);
@@ -241,9 +247,17 @@ moe_status fill_tiles(GemmArgs& g, const SchedWs& ws, const int32_t* offsets, in
 moe_status run_gate_up(const moe_config* c, const SchedWs& ws, bool build, int n_groups, int n_main, int64_t n_rows,
                        const int32_t* offsets, const void* x, int64_t n_x_rows, const int32_t* gather,
                        int64_t n_gather, const void* w_gate, const void* w_up, const void* s_gate, const void* s_up,
-                       int d_ff, void* h, hipStream_t s, int skip_group = -1) {
+                       int d_ff, void* h, hipStream_t s, int skip_group = -1, const float* const* scales = nullptr) {
   GemmArgs g{};
   MOE_TRY(fill_tiles(g, ws, offsets, n_groups, n_rows, build, skip_group, s));
+  if (fp8(c)) {  // scales: gate, up, shared gate, shared up
+    g.b_fp8 = 1;
+    g.s0 = scales[0];
+    g.s1 = scales[1];
+    g.s0_extra = scales[2];
+    g.s1_extra = scales[3];
+    g.s_stride = d_ff;
+  }
   g.a = x;
   g.n_a_rows = n_x_rows;
   g.gather = gather;
@@ -265,9 +279,15 @@ moe_status run_gate_up(const moe_config* c, const SchedWs& ws, bool build, int n
 
 moe_status run_down(const moe_config* c, const SchedWs& ws, bool build, int n_groups, int n_main, int64_t n_rows,
                     const int32_t* offsets, const void* h, const void* w_down, const void* s_down, int d_ff, float* y,
-                    hipStream_t s) {
+                    hipStream_t s, const float* const* scales = nullptr) {
   GemmArgs g{};
   MOE_TRY(fill_tiles(g, ws, offsets, n_groups, n_rows, build, -1, s));
+  if (fp8(c)) {  // scales: down, shared down
+    g.b_fp8 = 1;
+    g.s0 = scales[0];
+    g.s0_extra = scales[1];
+    g.s_stride = c->d_model;
+  }
   g.a = h;
   g.n_a_rows = n_rows;
   g.b0 = w_down;
@@ -288,10 +308,17 @@ moe_status run_ffn(const moe_config* c, int n_groups, int n_main, int64_t n_rows
                    const void* x, int64_t n_x_rows, const int32_t* gather, int64_t n_gather, const void* w_gate,
                    const void* w_up, const void* w_down, const void* s_gate, const void* s_up, const void* s_down,
                    int d_ff, float* y, const FfnWs& ws, hipStream_t s, bool tiles_ready = false,
-                   int skip_group = -1) {
+                   int skip_group = -1, const float* const* scales = nullptr) {
+  // scales (fp8 weights): gate, up, down of the main group, then of the extra group
+  const float* gu[4] = {nullptr, nullptr, nullptr, nullptr};
+  const float* dn[2] = {nullptr, nullptr};
+  if (scales) {
+    gu[0] = scales[0], gu[1] = scales[1], gu[2] = scales[3], gu[3] = scales[4];
+    dn[0] = scales[2], dn[1] = scales[5];
+  }
   MOE_TRY(run_gate_up(c, ws.sched, !tiles_ready, n_groups, n_main, n_rows, offsets, x, n_x_rows, gather, n_gather,
-                      w_gate, w_up, s_gate, s_up, d_ff, ws.h, s, skip_group));
-  MOE_TRY(run_down(c, ws.sched, false, n_groups, n_main, n_rows, offsets, ws.h, w_down, s_down, d_ff, y, s));
+                      w_gate, w_up, s_gate, s_up, d_ff, ws.h, s, skip_group, gu));
+  MOE_TRY(run_down(c, ws.sched, false, n_groups, n_main, n_rows, offsets, ws.h, w_down, s_down, d_ff, y, s, dn));
   return MOE_OK;
 }
 
@@ -304,6 +331,8 @@ moe_status check_grouped(const moe_config* cfg, int32_t n_groups, int64_t n_rows
   if (cfg->dtype == MOE_BF16 && (cfg->d_model % 8 || d_ff % 8))
     return fail(MOE_ERR_UNSUPPORTED, "bf16 rows need d_model and d_ff multiples of 8");
   if (packed(cfg) && d_ff % 64) return fail(MOE_ERR_UNSUPPORTED, "packed weights need d_ff %% 64 == 0");
+  if (fp8(cfg))
+    return fail(MOE_ERR_UNSUPPORTED, "fp8 weights need their scales: only moe_layer_forward[_dynamic] takes them");
   return MOE_OK;
 }
 
@@ -529,6 +558,12 @@ moe_status moe_layer_forward_dynamic(const moe_config* cfg, int64_t T, const voi
   const bool shared = cfg->d_shared > 0;
   if (shared && (!w->s_gate || !w->s_up || !w->s_down))
     return fail(MOE_ERR_NULL, "d_shared > 0 needs s_gate, s_up and s_down");
+  if (fp8(cfg) && (!w->w_gate_scale || !w->w_up_scale || !w->w_down_scale ||
+                   (shared && (!w->s_gate_scale || !w->s_up_scale || !w->s_down_scale))))
+    return fail(MOE_ERR_NULL, "fp8 weights need the scales of every expert matrix");
+  if (fp8(cfg) && (misaligned(w->w_gate_scale) || misaligned(w->w_up_scale) || misaligned(w->w_down_scale) ||
+                   misaligned(w->s_gate_scale) || misaligned(w->s_up_scale) || misaligned(w->s_down_scale)))
+    return fail(MOE_ERR_MISALIGNED, "moe_layer_forward: a scale pointer is not 16-byte aligned");
   if (misaligned(x) || misaligned(out) || misaligned(w->w_router) || misaligned(w->router_bias) ||
       misaligned(w->w_gate) || misaligned(w->w_up) || misaligned(w->w_down) ||
       (shared && (misaligned(w->s_gate) || misaligned(w->s_up) || misaligned(w->s_down))) ||
@@ -571,12 +606,15 @@ moe_status moe_layer_forward_dynamic(const moe_config* cfg, int64_t T, const voi
   //    when widths match, the shared expert as one more group over x itself
   //    (group E+1; group E, the unused rows, gets no tiles)
   const int n_groups = E + (L.fused_shared ? 2 : 0);
+  const float* sc[6] = {w->w_gate_scale, w->w_up_scale, w->w_down_scale, w->s_gate_scale, w->s_up_scale,
+                        w->s_down_scale};
   MOE_TRY(run_ffn(cfg, n_groups, E, P + extra, L.offsets_ext, x, T, L.sorted_token, P, w->w_gate, w->w_up,
                   w->w_down, w->s_gate, w->s_up, w->s_down, cfg->d_expert, L.y, L.ffn, s, small,
-                  L.fused_shared ? E : -1));
+                  L.fused_shared ? E : -1, sc));
   if (shared && !L.fused_shared) {
+    const float* sc_shared[6] = {w->s_gate_scale, w->s_up_scale, w->s_down_scale, nullptr, nullptr, nullptr};
     MOE_TRY(run_ffn(cfg, 1, 1, T, nullptr, x, T, nullptr, 0, w->s_gate, w->s_up, w->s_down, nullptr, nullptr,
-                    nullptr, cfg->d_shared, L.y_shared, L.ffn_shared, s));
+                    nullptr, cfg->d_shared, L.y_shared, L.ffn_shared, s, false, -1, sc_shared));
   }
   // 4. weighted combine: shared + sum_k prob * routed, one rounding to out_dtype
   MOE_TRY_HIP(launch_combine(cfg->out_dtype, T, D, K, L.y, P, L.dest, prob, L.y_shared, out, s), "combine");
@@ -623,6 +661,27 @@ moe_status moe_route_group_stats(const moe_config* cfg, int64_t T, const void* x
   MOE_TRY(run_route(cfg, T, x, w_router, bias, k_per_token, topk_idx, topk_prob, nullptr, w, s, gmass, n_groups));
   MOE_TRY_HIP(launch_group_stats(gmass, topk_idx, T, cfg->top_k, cfg->n_experts, n_groups, stats, s),
               "group statistics");
+  return ok();
+}
+
+size_t moe_fp8_weights_bytes(int64_t n_mats, int64_t rows, int64_t cols) {
+  if (n_mats < 0 || rows < 0 || cols <= 0 || cols % 64) return SIZE_MAX;
+  return (size_t)n_mats * (size_t)((rows + 15) / 16 * 16) * (size_t)cols;
+}
+
+moe_status moe_quantize_fp8(int64_t n_mats, int64_t rows, int64_t cols, const void* src, void* dst,
+                            size_t dst_bytes, float* scales, void* stream) {
+  if (n_mats < 0 || rows < 0 || cols <= 0 || cols % 64 || cols > (1 << 20))
+    return fail(MOE_ERR_SHAPE, "n_mats, rows >= 0 and cols in (0, 2^20], a multiple of 64, are required");
+  if (n_mats == 0 || rows == 0) return ok();
+  if (n_mats * ((rows + 15) / 16 * 16) >= kMaxRows) return fail(MOE_ERR_SHAPE, "too many rows");
+  if (!src || !dst || !scales) return fail(MOE_ERR_NULL, "src, dst and scales are required");
+  if (misaligned(src) || misaligned(dst) || misaligned(scales))
+    return fail(MOE_ERR_MISALIGNED, "moe_quantize_fp8: a pointer is not 16-byte aligned");
+  const size_t need = moe_fp8_weights_bytes(n_mats, rows, cols);
+  if (dst_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_quantize_fp8 needs %zu dst bytes, got %zu", need, dst_bytes);
+  MOE_TRY_HIP(launch_quant_fp8((const bf16_t*)src, n_mats, rows, cols, (uint8_t*)dst, scales, (hipStream_t)stream),
+              "fp8 quantisation");
   return ok();
 }
 

@@ -97,6 +97,25 @@ __device__ __forceinline__ uint4 load_b(const bf16_t* p) {
   }
 }
 
+// FP8 E4M3 -> bf16, exactly (an E4M3 value has at most 4 significant bits):
+// the hardware conversion gives fp32 (OCP E4M3 on gfx950), whose upper 16
+// bits are the bf16 value. HI selects bytes 2-3 of w instead of 0-1.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16x2(uint32_t w) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xFFFF0000u);
+}
+// 8 codes (lo: the first 4, hi: the next 4) -> one bf16x8 MFMA operand
+__device__ __forceinline__ uint4 fp8x8_bf16x8(uint32_t lo, uint32_t hi) {
+  return make_uint4(fp8x2_bf16x2<false>(lo), fp8x2_bf16x2<true>(lo), fp8x2_bf16x2<false>(hi),
+                    fp8x2_bf16x2<true>(hi));
+}
+
+__device__ __forceinline__ const float* group_scale(const GemmArgs& p, const float* main, const float* extra, int g) {
+  return g < p.n_main ? main + (int64_t)g * p.s_stride : extra;
+}
+
 // LDS offset (in bf16 elements) of 16-byte chunk `c` of staged row `r` (row
 // length KS): chunks are XOR-swizzled by (r & 7) so the 16-byte operand reads
 // of 8 consecutive rows hit distinct banks.
@@ -107,12 +126,16 @@ __device__ __forceinline__ int lds_off(int r, int c) { return r * KS + ((c ^ (r 
 // per wave and operand; KSTEPS: 32-element MFMA steps per pipeline stage;
 // NS: pipeline depth; PK: weights in the packed fragment layout (below);
 // NT: weights loaded non-temporally (load_stream; not for the router, whose
-// weights every row tile reads again). Loads of stage k+NS-1 are issued before stage k is
+// weights every row tile reads again); F8: weights are FP8 E4M3 codes in the
+// packed fp8 layout (one 16-byte load per lane covers a stage's two MFMA
+// steps), converted to bf16 in registers, with per-column scales applied in
+// the epilogue. Loads of stage k+NS-1 are issued before stage k is
 // multiplied, so NS-1 stages of weights (and A rows) are in flight per wave
 // while the matrix cores work; the ring lives in VGPRs and the loop is
 // unrolled by NS so every ring slot is a fixed register range.
-template <int EPI, int MT, int NW, int KSTEPS, int NS, bool PK, bool NT>
+template <int EPI, int MT, int NW, int KSTEPS, int NS, bool PK, bool NT, bool F8 = false>
 __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
+  static_assert(!F8 || (PK && KSTEPS == 2), "fp8 weights: packed, one fragment (64 columns) per stage");
   constexpr int KS = 32 * KSTEPS;                       // contraction elements per stage
   constexpr int CPR = KS / 8;                           // 16-byte chunks per staged row
   constexpr int RPP = 256 / CPR;                        // rows staged per pass of the block
@@ -164,8 +187,11 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
   // 32-element MFMA step. Columns past N are clamped to a valid row; their
   // results are never stored.
   const int wcol0 = nb * BN + wave * NW * 16;
-  const bf16_t* bg = group_b<bf16_t>(p, p.b0, p.b0_extra, t.group);
-  const bf16_t* bu = EPI == EPI_SWIGLU ? group_b<bf16_t>(p, p.b1, p.b1_extra, t.group) : bg;
+  const bf16_t* bg = F8 ? (const bf16_t*)group_b<uint8_t>(p, p.b0, p.b0_extra, t.group)
+                        : group_b<bf16_t>(p, p.b0, p.b0_extra, t.group);
+  const bf16_t* bu = EPI == EPI_SWIGLU ? (F8 ? (const bf16_t*)group_b<uint8_t>(p, p.b1, p.b1_extra, t.group)
+                                             : group_b<bf16_t>(p, p.b1, p.b1_extra, t.group))
+                                       : bg;
   // Packed weights: the operand of a whole wave for one 16-column tile and
   // one MFMA step is one contiguous 1 KB fragment, lane l at l*16 bytes
   // (packed_offset); the tiles past the last one are clamped to it.
@@ -173,7 +199,12 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
 #pragma unroll
   for (int j = 0; j < NBT; ++j) {
     const bf16_t* base = j < NW ? bg : bu;
-    if constexpr (PK) {
+    if constexpr (F8) {  // byte offsets into the fp8 codes
+      int ct = (wcol0 + (j % NW) * 16) >> 4;
+      const int ct_last = (p.N + 15) / 16 - 1;
+      ct = ct < ct_last ? ct : ct_last;
+      bptr[j] = (const bf16_t*)((const uint8_t*)base + fp8_offset(ct, kbase, lane, Kdim));
+    } else if constexpr (PK) {
       int ct = (wcol0 + (j % NW) * 16) >> 4;
       const int ct_last = (p.N + 15) / 16 - 1;
       ct = ct < ct_last ? ct : ct_last;
@@ -195,10 +226,15 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
 
   auto load_stage = [&](uint4(&a)[NA], uint4(&b)[NBT][KSTEPS], int ks) {
 #pragma unroll
-    for (int j = 0; j < NBT; ++j)
+    for (int j = 0; j < NBT; ++j) {
+      if constexpr (F8) {  // one fragment (both MFMA steps) per stage
+        b[j][0] = load_b<NT>((const bf16_t*)((const uint8_t*)bptr[j] + (int64_t)ks * FP8_FRAG));
+      } else {
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
-        b[j][s] = load_b<NT>(bptr[j] + (PK ? (ks * KSTEPS + s) * PACKED_FRAG : ks * KS + s * 32));
+        for (int s = 0; s < KSTEPS; ++s)
+          b[j][s] = load_b<NT>(bptr[j] + (PK ? (ks * KSTEPS + s) * PACKED_FRAG : ks * KS + s * 32));
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NA; ++i) a[i] = *(const uint4*)(arow[i] + ks * KS);
   };
@@ -209,13 +245,19 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
   auto compute = [&](int buf, const uint4(&b)[NBT][KSTEPS]) {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
+      uint4 bop[NBT];
+#pragma unroll
+      for (int j = 0; j < NBT; ++j) {
+        if constexpr (F8) bop[j] = s == 0 ? fp8x8_bf16x8(b[j][0].x, b[j][0].y) : fp8x8_bf16x8(b[j][0].z, b[j][0].w);
+        else bop[j] = b[j][s];
+      }
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const bf16x8 a =
             as_bf16x8(*(const uint4*)&sA[buf][lds_off<KS>(m * 16 + (lane & 15), s * 4 + (lane >> 4))]);
 #pragma unroll
         for (int j = 0; j < NBT; ++j)
-          acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(b[j][s]), acc[m][j], 0, 0, 0);
+          acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(bop[j]), acc[m][j], 0, 0, 0);
       }
     }
   };
@@ -258,21 +300,29 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
   // Accumulator layout of a 16x16 MFMA tile: lane holds column (lane & 15),
   // rows 4*(lane >> 4) + v for v = 0..3.
   const int64_t rbase = (int64_t)t.row0 + (lane >> 4) * 4;
+  const float* sc0 = F8 ? group_scale(p, p.s0, p.s0_extra, t.group) : nullptr;
+  const float* sc1 = F8 && EPI == EPI_SWIGLU ? group_scale(p, p.s1, p.s1_extra, t.group) : nullptr;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
       const int col = wcol0 + j * 16 + (lane & 15);
       if (col >= p.N) continue;
+      // fp8 weights: the column's scale (one per weight row)
+      const float f0 = F8 ? sc0[col] : 1.f;
+      const float f1 = F8 && EPI == EPI_SWIGLU ? sc1[col] : 1.f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t r = rbase + m * 16 + v;
         if (r >= t.row1) continue;
         if constexpr (EPI == EPI_SWIGLU) {
-          ((bf16_t*)p.out)[r * p.ldo + col] = f32_to_bf16(silu(acc[m][j][v]) * acc[m][j + NW][v]);
+          const float gv = F8 ? acc[m][j][v] * f0 : acc[m][j][v];
+          const float uv = F8 ? acc[m][j + NW][v] * f1 : acc[m][j + NW][v];
+          ((bf16_t*)p.out)[r * p.ldo + col] = f32_to_bf16(silu(gv) * uv);
         } else {
           const float b = (p.bias && blockIdx.y == 0) ? p.bias[col] : 0.f;
-          ((float*)p.out + (int64_t)blockIdx.y * p.slice_stride)[r * p.ldo + col] = acc[m][j][v] + b;
+          const float a = F8 ? acc[m][j][v] * f0 : acc[m][j][v];
+          ((float*)p.out + (int64_t)blockIdx.y * p.slice_stride)[r * p.ldo + col] = a + b;
         }
       }
     }
@@ -429,7 +479,10 @@ static hipError_t launch_fast(const GemmArgs& g, hipStream_t s) {
   const int n_nb = (g.N + 4 * NW * 16 - 1) / (4 * NW * 16);
   const int64_t blocks = ((int64_t)g.max_tiles * n_nb + 7) / 8 * 8;
   const dim3 grid((unsigned)blocks, (unsigned)g.ksplit);
-  if (g.b_reuse) {
+  if (g.b_fp8) {  // expert weights only (streamed, packed)
+    if (g.b_reuse || KSTEPS != 2) return hipErrorInvalidValue;
+    gemm_bf16_mfma<EPI, MT, NW, KSTEPS, NS, true, true, true><<<grid, 256, 0, s>>>(g);
+  } else if (g.b_reuse) {
     if (g.b_packed) gemm_bf16_mfma<EPI, MT, NW, KSTEPS, NS, true, false><<<grid, 256, 0, s>>>(g);
     else gemm_bf16_mfma<EPI, MT, NW, KSTEPS, NS, false, false><<<grid, 256, 0, s>>>(g);
   } else {
@@ -441,6 +494,7 @@ static hipError_t launch_fast(const GemmArgs& g, hipStream_t s) {
 
 hipError_t launch_grouped_gemm(int dtype, bool fast, int epi, int block_rows, const GemmArgs& g, hipStream_t s) {
   if (g.max_tiles <= 0 || g.N <= 0) return hipSuccess;
+  if (g.b_fp8 && (!fast || block_rows == 256)) return hipErrorInvalidValue;  // fp8: 32/64/128-row tiles only
   if (!fast) {
     if (g.b_packed) return hipErrorInvalidValue;  // packed weights exist only on the bf16 MFMA path
     const int n_nb = (g.N + 63) / 64;

@@ -49,6 +49,16 @@ struct Tile {
   int32_t count, pad0, pad1, pad2;
 };
 
+// Packed FP8 layout of W [N, K] (K % 64 == 0), E4M3 codes: fragments of 16
+// rows x 64 columns (1 KB), ct-major then kb; lane l = c + 16q of fragment
+// (ct, kb) holds, at byte 16l, the codes of row 16ct + c at columns
+// 64kb + 8q .. +8 and then 64kb + 32 + 8q .. +8: the two 32-column halves
+// are the lane's operands of two consecutive MFMA steps.
+constexpr int FP8_FRAG = 1024;  // bytes per fp8 fragment
+__host__ __device__ __forceinline__ int64_t fp8_offset(int64_t ct, int64_t kb, int lane, int64_t K) {
+  return (ct * (K / 64) + kb) * FP8_FRAG + lane * 16;
+}
+
 // Packed fragment layout of a bf16 weight matrix W [N, K] (K % 32 == 0):
 // W is cut into 16-row x 32-column fragments, fragment (ct, kb) covering rows
 // 16ct.. and columns 32kb.. . Each fragment is 1 KB stored in MFMA operand
@@ -88,6 +98,12 @@ struct GemmArgs {
   void* out;              // [rows, ldo]
   int64_t ldo;
   int32_t b_packed;       // B operands in the packed fragment layout (bf16 MFMA kernels only)
+  int32_t b_fp8;          // B operands are FP8 E4M3 codes in the packed fp8 layout (b_stride in bytes),
+  const float* s0;        //   with per-column scales: group g < n_main: s0 + g*s_stride, else s0_extra
+  const float* s1;        //   (second B operand: s1 / s1_extra)
+  const float* s0_extra;
+  const float* s1_extra;
+  int64_t s_stride;
   int32_t b_reuse;        // B is read again by many row tiles (router): keep it cacheable
   const float* bias;      // EPI_F32: per-column bias or NULL
   int32_t ksplit;         // EPI_F32 only: the contraction is cut into ksplit slices;
@@ -148,6 +164,11 @@ hipError_t launch_ep_plan(const int32_t* counts, int n_src, int n_local, int64_t
 // layout (rows rounded up to a multiple of 16, zero-filled), matrix after
 // matrix.
 hipError_t launch_pack(const bf16_t* src, int64_t n_mats, int64_t rows, int64_t cols, bf16_t* dst, hipStream_t s);
+// pack.hip: per-row FP8 quantisation of n_mats row-major [rows, cols] bf16
+// matrices (cols % 64 == 0) into the packed fp8 layout (rows rounded up to
+// 16, zero codes) and scales [n_mats, rows].
+hipError_t launch_quant_fp8(const bf16_t* src, int64_t n_mats, int64_t rows, int64_t cols, uint8_t* dst,
+                            float* scales, hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(int out_dtype, int64_t T, int D, int K, const float* y_perm, int64_t n_perm_rows,

@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 F32, BF16 = 0, 1
-LAYOUT_ROWS, LAYOUT_PACKED = 0, 1
+LAYOUT_ROWS, LAYOUT_PACKED, LAYOUT_FP8 = 0, 1, 2
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 _TORCH = {F32: torch.float32, BF16: torch.bfloat16}
 SIZE_MAX = ctypes.c_size_t(-1).value
@@ -39,7 +39,8 @@ class MoeConfig(ctypes.Structure):
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w_router", "router_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")]
+                ("w_router", "router_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+                 "w_gate_scale", "w_up_scale", "w_down_scale", "s_gate_scale", "s_up_scale", "s_down_scale")]
 
 
 _lib = None
@@ -69,6 +70,8 @@ _SIGS = {
     "moe_ep_receive_plan": ([_I32, _I32, _P, _I64, _P, _P, _P, _P], ctypes.c_int),
     "moe_gather_rows": ([_P, _I64, _I64, _P, _I64, _P, _P], ctypes.c_int),
     "moe_packed_weights_bytes": ([_I64, _I64, _I64], _SZ),
+    "moe_fp8_weights_bytes": ([_I64, _I64, _I64], _SZ),
+    "moe_quantize_fp8": ([_I64, _I64, _I64, _P, _P, _SZ, _P, _P], ctypes.c_int),
     "moe_pack_weights": ([_I64, _I64, _I64, _P, _P, _SZ, _P], ctypes.c_int),
 }
 
@@ -107,15 +110,17 @@ class Config:
     dtype: torch.dtype = torch.bfloat16
     out_dtype: torch.dtype | None = None
     packed: bool = False  # weight matrices in the packed fragment layout (pack_weights)
+    fp8: bool = False     # expert matrices FP8 E4M3 (quantize_fp8) with per-row scales; router packed bf16
 
     def c(self) -> MoeConfig:
         out = self.out_dtype if self.out_dtype is not None else self.dtype
+        layout = LAYOUT_FP8 if self.fp8 else (LAYOUT_PACKED if self.packed else LAYOUT_ROWS)
         return MoeConfig(self.d_model, self.n_experts, self.top_k, self.d_expert, self.d_shared,
-                         _DT[self.dtype], _DT[out], LAYOUT_PACKED if self.packed else LAYOUT_ROWS)
+                         _DT[self.dtype], _DT[out], layout)
 
     def wshape(self, *shape: int) -> tuple:
         """Shape of a weight tensor whose row-major shape is `shape` (rows rounded up to 16 when packed)."""
-        if not self.packed:
+        if not (self.packed or self.fp8):
             return tuple(shape)
         return (*shape[:-2], (shape[-2] + 15) // 16 * 16, shape[-1])
 
@@ -292,13 +297,23 @@ def weights_struct(cfg: Config, w: dict) -> MoeWeights:
     s = MoeWeights()
     s.w_router = _ptr(w["w_router"], "w_router", cfg.dtype, cfg.wshape(E, D), dev)
     s.router_bias = _ptr(w.get("bias"), "bias", torch.float32, (E,), dev)
-    s.w_gate = _ptr(w["w_gate"], "w_gate", cfg.dtype, (E, F, D), dev)
-    s.w_up = _ptr(w["w_up"], "w_up", cfg.dtype, (E, F, D), dev)
-    s.w_down = _ptr(w["w_down"], "w_down", cfg.dtype, (E, D, F), dev)
+    ed = torch.uint8 if cfg.fp8 else cfg.dtype   # fp8: E4M3 codes, rows rounded up to 16
+    r16 = (lambda n: (n + 15) // 16 * 16) if cfg.fp8 else (lambda n: n)
+    s.w_gate = _ptr(w["w_gate"], "w_gate", ed, (E, r16(F), D), dev)
+    s.w_up = _ptr(w["w_up"], "w_up", ed, (E, r16(F), D), dev)
+    s.w_down = _ptr(w["w_down"], "w_down", ed, (E, r16(D), F), dev)
+    if cfg.fp8:
+        s.w_gate_scale = _ptr(w["w_gate_scale"], "w_gate_scale", torch.float32, (E, F), dev)
+        s.w_up_scale = _ptr(w["w_up_scale"], "w_up_scale", torch.float32, (E, F), dev)
+        s.w_down_scale = _ptr(w["w_down_scale"], "w_down_scale", torch.float32, (E, D), dev)
     if Fs:
-        s.s_gate = _ptr(w["s_gate"], "s_gate", cfg.dtype, (Fs, D), dev)
-        s.s_up = _ptr(w["s_up"], "s_up", cfg.dtype, (Fs, D), dev)
-        s.s_down = _ptr(w["s_down"], "s_down", cfg.dtype, (D, Fs), dev)
+        s.s_gate = _ptr(w["s_gate"], "s_gate", ed, (r16(Fs), D), dev)
+        s.s_up = _ptr(w["s_up"], "s_up", ed, (r16(Fs), D), dev)
+        s.s_down = _ptr(w["s_down"], "s_down", ed, (r16(D), Fs), dev)
+        if cfg.fp8:
+            s.s_gate_scale = _ptr(w["s_gate_scale"], "s_gate_scale", torch.float32, (Fs,), dev)
+            s.s_up_scale = _ptr(w["s_up_scale"], "s_up_scale", torch.float32, (Fs,), dev)
+            s.s_down_scale = _ptr(w["s_down_scale"], "s_down_scale", torch.float32, (D,), dev)
     return s
 
 
@@ -407,6 +422,38 @@ def pack_weights(w: torch.Tensor) -> torch.Tensor:
     out = torch.empty((*w.shape[:-2], (rows + 15) // 16 * 16, cols), dtype=torch.bfloat16, device=w.device)
     _check(lib().moe_pack_weights(n, rows, cols, _ptr(w, "w", torch.bfloat16), _ptr(out, "out"),
                                   out.numel() * 2, _stream(w.device)), "moe_pack_weights")
+    return out
+
+
+def fp8_weights_bytes(n_mats: int, rows: int, cols: int) -> int:
+    return lib().moe_fp8_weights_bytes(n_mats, rows, cols)
+
+
+def quantize_fp8(w: torch.Tensor):
+    """moe_quantize_fp8: bf16 [rows, cols] or [n, rows, cols] -> (E4M3 codes uint8 [..., ceil(rows/16)*16, cols]
+    in the packed fp8 layout, per-row fp32 scales [..., rows])."""
+    if w.dim() not in (2, 3):
+        raise ValueError("quantize_fp8 takes a [rows, cols] or [n, rows, cols] tensor")
+    n = w.shape[0] if w.dim() == 3 else 1
+    rows, cols = w.shape[-2], w.shape[-1]
+    nbytes = fp8_weights_bytes(n, rows, cols)
+    if nbytes == SIZE_MAX:
+        raise ValueError(f"cannot quantise [{rows}, {cols}]: cols must be a multiple of 64")
+    codes = torch.empty((*w.shape[:-2], (rows + 15) // 16 * 16, cols), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((*w.shape[:-2], rows), dtype=torch.float32, device=w.device)
+    _check(lib().moe_quantize_fp8(n, rows, cols, _ptr(w, "w", torch.bfloat16), _ptr(codes, "codes"), codes.numel(),
+                                  _ptr(scales, "scales"), _stream(w.device)), "moe_quantize_fp8")
+    return codes, scales
+
+
+def quantize_layer(w: dict) -> dict:
+    """A copy of a layer's weight dict for a Config with fp8=True: expert matrices as E4M3 codes with
+    *_scale entries, the router packed (bf16)."""
+    out = dict(w)
+    out["w_router"] = pack_weights(w["w_router"])
+    for k in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down"):
+        if w.get(k) is not None:
+            out[k], out[k + "_scale"] = quantize_fp8(w[k])
     return out
 
 
