@@ -46,6 +46,11 @@
 // which the operand reads take at 16 bytes per lane, conflict-free.
 #include "moe_internal.h"
 
+// The operand-read lambdas capture their asm operands explicitly (clang's
+// device pass does not capture names used only as asm operands); the host
+// pass, which does not see the asm's use, would warn about those captures.
+#pragma clang diagnostic ignored "-Wunused-lambda-capture"
+
 namespace moe {
 
 namespace {
