@@ -143,8 +143,8 @@ moe_status moe_pack_weights(int64_t n_mats, int64_t rows, int64_t cols, const vo
  * stays bf16 in the packed layout (moe_pack_weights), and the widths must be
  * multiples of 64. Page "Step3.5 Flash 大模型技术深度解析", section 8.1,
  * deploys the model with FP8/FP16 weights. The expert GEMMs read half the
- * weight bytes and convert to bf16 in registers; they use row tiles of 32,
- * 64 or 128 rows (the 256 x 256 kernel is bf16 only). Only
+ * weight bytes and convert to bf16 in registers, with the same row tiles
+ * as bf16 weights. Only
  * moe_layer_forward and moe_layer_forward_dynamic take fp8 weights (the
  * grouped expert entry points have no scale arguments: MOE_ERR_UNSUPPORTED).
  *

@@ -5,7 +5,7 @@
 // outputs and tables) and runs every lane of every block of both
 // projections, packed and row-major, under AddressSanitizer.
 //
-// usage: driver T E K D F Fs seed [skew]
+// usage: driver T E K D F Fs seed [skew] [fp8]
 #include <algorithm>
 #include <random>
 #include <thread>
@@ -79,6 +79,7 @@ int main(int argc, char** argv) {
   const int T = atoi(argv[1]), E = atoi(argv[2]), K = atoi(argv[3]), D = atoi(argv[4]), F = atoi(argv[5]),
             Fs = atoi(argv[6]), seed = atoi(argv[7]);
   const bool skew = argc > 8 && atoi(argv[8]);
+  const bool fp8 = argc > 9 && atoi(argv[9]);  // fp8 weights (codes + per-row scales) instead of bf16
   if (Fs && Fs != F) { fprintf(stderr, "a fused shared expert needs Fs == F\n"); return 2; }
   std::mt19937 rng(seed);
   std::vector<std::vector<int>> by_e(E);
@@ -111,7 +112,7 @@ int main(int argc, char** argv) {
   printf("T=%d E=%d K=%d D=%d F=%d Fs=%d skew=%d: %zu tiles\n", T, E, K, D, F, Fs, (int)skew, tv.size());
   auto pad16 = [](int n) { return (n + 15) / 16 * 16; };
   for (int epi : {EPI_SWIGLU, EPI_F32})
-    for (int pk = 1; pk >= 0; --pk) {
+    for (int pk = 1; pk >= (fp8 ? 1 : 0); --pk) {
       GemmArgs g{};
       g.tiles = tiles;
       g.n_tiles = n_tiles;
@@ -119,17 +120,27 @@ int main(int argc, char** argv) {
       g.max_tiles = max_tiles;
       g.n_main = E;
       g.b_packed = pk;
+      g.b_fp8 = fp8;
       bf16_t *a, *b0, *b1 = nullptr, *b0x = nullptr, *b1x = nullptr;
+      float *s0 = nullptr, *s1 = nullptr, *s0x = nullptr, *s1x = nullptr;
       void* out;
+      // weight buffers in bf16 elements: fp8 codes take half as many bytes
+      auto wbuf = [&](size_t elems) { return fp8 ? (bf16_t*)buffer<uint8_t>(elems) : buffer<bf16_t>(elems); };
       if (epi == EPI_SWIGLU) {  // A: the token rows, gathered
         a = buffer<bf16_t>((size_t)T * D);
         g.n_a_rows = T;
         g.gather = gather;
         g.n_gather = P;
         const size_t wn = (size_t)(pk ? pad16(F) : F) * D;
-        b0 = buffer<bf16_t>(wn * E);
-        b1 = buffer<bf16_t>(wn * E);
-        if (Fs) { b0x = buffer<bf16_t>(wn); b1x = buffer<bf16_t>(wn); }
+        b0 = wbuf(wn * E);
+        b1 = wbuf(wn * E);
+        if (Fs) { b0x = wbuf(wn); b1x = wbuf(wn); }
+        if (fp8) {
+          s0 = buffer<float>((size_t)E * F);
+          s1 = buffer<float>((size_t)E * F);
+          if (Fs) { s0x = buffer<float>(F); s1x = buffer<float>(F); }
+          g.s_stride = F;
+        }
         g.b_stride = (int64_t)F * D;
         g.N = F;
         g.Kdim = D;
@@ -139,8 +150,13 @@ int main(int argc, char** argv) {
         a = buffer<bf16_t>((size_t)n_rows * F);
         g.n_a_rows = n_rows;
         const size_t wn = (size_t)(pk ? pad16(D) : D) * F;
-        b0 = buffer<bf16_t>(wn * E);
-        if (Fs) b0x = buffer<bf16_t>(wn);
+        b0 = wbuf(wn * E);
+        if (Fs) b0x = wbuf(wn);
+        if (fp8) {
+          s0 = buffer<float>((size_t)E * D);
+          if (Fs) s0x = buffer<float>(D);
+          g.s_stride = D;
+        }
         g.b_stride = (int64_t)D * F;
         g.N = D;
         g.Kdim = F;
@@ -153,13 +169,18 @@ int main(int argc, char** argv) {
       g.b0_extra = b0x;
       g.b1_extra = b1x;
       g.out = out;
+      g.s0 = s0;
+      g.s1 = s1;
+      g.s0_extra = s0x;
+      g.s1_extra = s1x;
       emul_loads = 0;
       const int rc = launch_grouped_gemm_big(epi, g, nullptr);
-      printf("  %s %s: rc=%d direct loads %lld ok\n", epi == EPI_SWIGLU ? "gate/up" : "down", pk ? "packed" : "rows",
-             rc, emul_loads);
+      printf("  %s %s: rc=%d direct loads %lld ok\n", epi == EPI_SWIGLU ? "gate/up" : "down",
+             fp8 ? "fp8" : (pk ? "packed" : "rows"), rc, emul_loads);
       fflush(stdout);
       if (rc != 0) return 3;
       free(a); free(b0); free(b1); free(b0x); free(b1x); free(out);
+      free(s0); free(s1); free(s0x); free(s1x);
     }
   return 0;
 }

@@ -19,6 +19,7 @@
 #define __restrict__
 struct uint4 { uint32_t x, y, z, w; };
 struct float4 { float x, y, z, w; };
+inline uint4 make_uint4(uint32_t x, uint32_t y, uint32_t z, uint32_t w) { return uint4{x, y, z, w}; }
 struct emul_dim3 { unsigned x = 0, y = 0, z = 0; };
 extern thread_local emul_dim3 threadIdx, blockIdx;
 extern emul_dim3 gridDim, blockDim;
@@ -54,3 +55,9 @@ template <class V> inline V emul_ds_read(uint32_t vaddr) {
 #define __builtin_amdgcn_readfirstlane(x) (x)
 #define __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, x, y, z) (c)
 #define __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, x, y, z) (c)
+typedef float emul_f32x2 __attribute__((ext_vector_type(2)));
+inline emul_f32x2 emul_cvt_pk_f32_fp8(int w, bool hi) {  // values are not needed, only the call's shape
+  (void)w, (void)hi;
+  return emul_f32x2{0.f, 0.f};
+}
+#define __builtin_amdgcn_cvt_pk_f32_fp8(w, hi) emul_cvt_pk_f32_fp8((w), (hi))

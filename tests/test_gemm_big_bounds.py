@@ -45,10 +45,11 @@ def host_source(kernel_src: str) -> str:
                                f"({m.group(2)} + ({m.group(3)}));"), s)
     s, _ = re.subn(r'asm volatile\("s_waitcnt lgkmcnt\(%1\)" : "\+v"\([^)]*\) : "n"\([^)]*\)\);', ";", s)
     s, _ = re.subn(r'asm volatile\("[^"]*" ::: "memory"\);', ";", s)
+    s, _ = re.subn(r'asm volatile\("s_waitcnt lgkmcnt\(%1\)" : "\+v"\([^)]*\) : "n"\([^)]*\)\);', ";", s)
     s, k4 = re.subn(r"(gemm_bf16_big<[^>]*>)<<<\(unsigned\)blocks, 256, 0, s>>>\(g\);",
                     lambda m: f"emul_launch({m.group(1)}, (unsigned)blocks, g);", s)
     left = re.findall(r"asm volatile.*|<<<.*>>>", s)
-    assert k0 >= 1 and k1 >= 2 and k4 == 4 and not left, (k0, k1, k4, left)
+    assert k0 >= 1 and k1 >= 3 and k4 == 6 and not left, (k0, k1, k4, left)
     return s
 
 
@@ -82,6 +83,10 @@ SHAPES = {
     "skewed": (4096, 64, 8, 512, 256, 256, 4, 1),
     # the decode/prefill widths with fewer tokens
     "wide": (512, 16, 8, 4096, 1280, 1280, 5, 0),
+    # fp8 weights (64-element weight stages, per-column scales): short and odd contractions, several items
+    "fp8_multi_item_short_k": (32768, 8, 2, 128, 192, 192, 2, 0, 1),
+    "fp8_odd_stages_skewed": (4096, 64, 8, 512, 320, 320, 4, 1, 1),
+    "fp8_wide": (512, 16, 8, 4096, 1280, 1280, 5, 0, 1),
 }
 
 
@@ -90,7 +95,7 @@ def test_big_gemm_accesses_stay_in_bounds(driver, name):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0")
     r = subprocess.run([driver, *map(str, SHAPES[name])], capture_output=True, text=True, timeout=600, env=env)
     assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-4000:])
-    assert r.stdout.count(" ok") == 4, r.stdout
+    assert r.stdout.count(" ok") == (2 if name.startswith("fp8") else 4), r.stdout
 
 
 def test_planted_offset_is_caught(driver, tmp_path):

@@ -122,3 +122,14 @@ def test_fp8_full_size(name):
     L = device_layer(spec)
     r, c32, c16 = run_fp8(spec, L, rows=sample_rows(spec.T, 6, 3))  # the oracle quantises each expert it uses
     print(f"{name}: out_rel(before cast)={c32['rel']:.3e} out_rel={c16['rel']:.3e}")
+
+
+@pytest.mark.parametrize("name", ["d256_f512", "d128_f192"])
+def test_fp8_many_items_per_block(name):
+    """fp8 weights through the 256x256 kernel with several items per block (the stream of 64-element
+    stages runs on across items), the shortest and an odd number of stages per item; sampled rows."""
+    from test_gpu_parity import MANY_ITEMS
+    spec = MANY_ITEMS[name]
+    L = device_layer(spec)
+    r, c32, c16 = run_fp8(spec, L, rows=sample_rows(spec.T, 24, 11))
+    print(f"{name}: out_rel(before cast)={c32['rel']:.3e} out_rel={c16['rel']:.3e}")

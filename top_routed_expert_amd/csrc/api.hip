@@ -141,8 +141,7 @@ SchedWs carve_sched(Arena& a, const moe_config* c, int n_groups, int64_t n_rows,
   // 256-row tiles need contractions of at least 128 and A offsets that fit
   // 32 bits in 16-byte units (A has at most n_rows rows of either width)
   const int64_t kmax = c->d_model > d_ff ? c->d_model : d_ff;
-  const bool big_ok = c->d_model >= 128 && d_ff >= 128 && !fp8(c) &&
-                      (uint64_t)n_rows * (uint64_t)kmax / 8u <= 0xffffffffull;
+  const bool big_ok = c->d_model >= 128 && d_ff >= 128 && (uint64_t)n_rows * (uint64_t)kmax / 8u <= 0xffffffffull;
   w.block_rows = gemm_block_rows(w.fast, n_rows, n_groups, big_ok);
   w.max_tiles = (int32_t)gemm_max_tiles(n_rows, n_groups, w.block_rows);
   w.tiles = a.take<Tile>(w.max_tiles);

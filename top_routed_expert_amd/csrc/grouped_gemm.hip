@@ -97,25 +97,6 @@ __device__ __forceinline__ uint4 load_b(const bf16_t* p) {
   }
 }
 
-// FP8 E4M3 -> bf16, exactly (an E4M3 value has at most 4 significant bits):
-// the hardware conversion gives fp32 (OCP E4M3 on gfx950), whose upper 16
-// bits are the bf16 value. HI selects bytes 2-3 of w instead of 0-1.
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_bf16x2(uint32_t w) {
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  const f32x2_t f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-  return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xFFFF0000u);
-}
-// 8 codes (lo: the first 4, hi: the next 4) -> one bf16x8 MFMA operand
-__device__ __forceinline__ uint4 fp8x8_bf16x8(uint32_t lo, uint32_t hi) {
-  return make_uint4(fp8x2_bf16x2<false>(lo), fp8x2_bf16x2<true>(lo), fp8x2_bf16x2<false>(hi),
-                    fp8x2_bf16x2<true>(hi));
-}
-
-__device__ __forceinline__ const float* group_scale(const GemmArgs& p, const float* main, const float* extra, int g) {
-  return g < p.n_main ? main + (int64_t)g * p.s_stride : extra;
-}
-
 // LDS offset (in bf16 elements) of 16-byte chunk `c` of staged row `r` (row
 // length KS): chunks are XOR-swizzled by (r & 7) so the 16-byte operand reads
 // of 8 consecutive rows hit distinct banks.
@@ -494,7 +475,7 @@ static hipError_t launch_fast(const GemmArgs& g, hipStream_t s) {
 
 hipError_t launch_grouped_gemm(int dtype, bool fast, int epi, int block_rows, const GemmArgs& g, hipStream_t s) {
   if (g.max_tiles <= 0 || g.N <= 0) return hipSuccess;
-  if (g.b_fp8 && (!fast || block_rows == 256)) return hipErrorInvalidValue;  // fp8: 32/64/128-row tiles only
+  if (g.b_fp8 && !fast) return hipErrorInvalidValue;  // fp8 weights: bf16 MFMA kernels only
   if (!fast) {
     if (g.b_packed) return hipErrorInvalidValue;  // packed weights exist only on the bf16 MFMA path
     const int n_nb = (g.N + 63) / 64;

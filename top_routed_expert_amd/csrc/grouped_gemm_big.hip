@@ -38,6 +38,14 @@
 // compiler may not move memory accesses across it and does not add a drain
 // of its own.
 //
+// FP8 weights (F8): the codes of a weight stage cover 64 contraction
+// elements (a 1 KB fragment per 16 weight rows, the packed fp8 layout), so
+// both operands move in 64-element stages and a trip of two MFMA steps needs
+// one wait and one barrier. A wave reads its 8 weight fragments once per
+// trip, converts the first halves to bf16 operands for the first step and
+// the second halves for the second, and the epilogue applies the per-column
+// scales.
+//
 // A rows in LDS are 128 bytes (eight 16-byte chunks); chunk q of row r is
 // stored at position q ^ ((r >> 1) & 7), so the 16-byte MFMA operand reads
 // of 16 consecutive rows cover all banks once. B rows without packing are
@@ -85,8 +93,9 @@ constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }   // 64-byte B rows
 __device__ __forceinline__ int swzA(int row) { return (row >> 1) & 7; }  // 128-byte A rows
 
-template <int EPI, bool PK>
+template <int EPI, bool PK, bool F8 = false>
 __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
+  static_assert(!F8 || PK, "fp8 weights are packed");
   __shared__ __attribute__((aligned(16))) bf16_t ldsA[2][BIG_ROWS * A_KS];
   __shared__ __attribute__((aligned(16))) bf16_t ldsB[BIG_NS][BIG_ROWS * BIG_KS];
   __shared__ __attribute__((aligned(16))) float stg[4][16 * 128];  // epilogue staging, 8 KB per wave
@@ -175,12 +184,16 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
       aoff[i] = (uint32_t)rows[i] * (uint32_t)(Kdim >> 3) + (uint32_t)((lane & 7) ^ swzA(row));
     }
   };
+  // (fp8: byte pointers into the codes, kept in the same bf16_t* slots)
+  constexpr int64_t EB = F8 ? 1 : 2;  // bytes per weight element
   auto set_b_sources = [&](const Tile& t, int nb) {
-    const bf16_t* Bg = t.group < p.n_main ? (const bf16_t*)p.b0 + (int64_t)t.group * p.b_stride
-                                          : (const bf16_t*)p.b0_extra;
-    const bf16_t* Bu = EPI == EPI_SWIGLU ? (t.group < p.n_main ? (const bf16_t*)p.b1 + (int64_t)t.group * p.b_stride
-                                                               : (const bf16_t*)p.b1_extra)
-                                         : Bg;
+    const bf16_t* Bg = (const bf16_t*)(t.group < p.n_main ? (const char*)p.b0 + (int64_t)t.group * p.b_stride * EB
+                                                          : (const char*)p.b0_extra);
+    const bf16_t* Bu =
+        EPI == EPI_SWIGLU
+            ? (const bf16_t*)(t.group < p.n_main ? (const char*)p.b1 + (int64_t)t.group * p.b_stride * EB
+                                                 : (const char*)p.b1_extra)
+            : Bg;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wave * 64 + i * 16 + (lane >> 2);
@@ -196,7 +209,12 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
         col = nb * BN + row;
         base = Bg;
       }
-      if constexpr (PK) {
+      if constexpr (F8) {
+        int ct = (col - (row & 15)) >> 4;
+        const int ct_last = (p.N + 15) / 16 - 1;
+        ct = ct < ct_last ? ct : ct_last;
+        bsrc[i] = (const bf16_t*)((const char*)base + fp8_offset(ct, 0, lane, Kdim));
+      } else if constexpr (PK) {
         // the 16 rows of this instruction are one fragment column tile
         int ct = (col - (row & 15)) >> 4;
         const int ct_last = (p.N + 15) / 16 - 1;
@@ -215,11 +233,13 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
       __builtin_amdgcn_global_load_lds((const void*)(A + (uint64_t)aoff[i] * 8u + ja * A_KS),
                                        (lds_void_t*)&ldsA[slot][(wave * 64 + i * 8) * A_KS], 16, 0, 0);
   };
-  auto issue_b = [&](int slot, int ks) {
+  auto issue_b = [&](int slot, int ks) {  // ks: a 32-element step (bf16) or a 64-element stage (fp8)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + (PK ? ks * PACKED_FRAG : ks * BIG_KS)),
-                                       (lds_void_t*)&ldsB[slot][(wave * 64 + i * 16) * BIG_KS], 16, 0, CPOL_NT);
+      __builtin_amdgcn_global_load_lds(
+          F8 ? (const void*)((const char*)bsrc[i] + (int64_t)ks * FP8_FRAG)
+             : (const void*)(bsrc[i] + (PK ? ks * PACKED_FRAG : ks * BIG_KS)),
+          (lds_void_t*)&ldsB[slot][(wave * 64 + i * 16) * BIG_KS], 16, 0, CPOL_NT);
   };
 
   // wave (wm, wn): rows wm*128 .., weight rows wn*128 ..
@@ -274,6 +294,36 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
     });
   };
 
+  // fp8: this wave's 8 weight fragments of a stage, 16 bytes per lane (both
+  // MFMA steps' codes); raw[n] lands at lgkmcnt(15 - n) when the 8 A reads
+  // follow them.
+  auto read_b8 = [&](int slot, u32x4(&raw)[8]) {
+    const uint32_t addr = ldsB_base + (uint32_t)slot * SLOT_B + (uint32_t)(wn * 8) * 1024u + (uint32_t)lane * 16u;
+    static_for<0, 8>([&raw, addr](auto N) {
+      constexpr int n = decltype(N)::value;
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(raw[n]) : "v"(addr), "n"(n * 1024));
+    });
+  };
+  // operands of MFMA step `hi` (0, 1) of a stage from the raw codes
+  auto convert_b = [&](const u32x4(&raw)[8], int hi, u32x4(&b)[8]) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const uint4 v = hi ? fp8x8_bf16x8(raw[n].z, raw[n].w) : fp8x8_bf16x8(raw[n].x, raw[n].y);
+      b[n] = u32x4{v.x, v.y, v.z, v.w};
+    }
+  };
+  // multiply with the A chunks as the only LDS reads in flight behind them
+  auto multiply_a_only = [&](u32x4(&a)[8], const u32x4(&b)[8]) {
+    static_for<0, 8>([&](auto M) {
+      constexpr int m = decltype(M)::value;
+      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a[m]) : "n"(7 - m));
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_big(a[m]), as_bf16x8_big(b[n]), acc[m][n], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
   // Epilogue of an item through this wave's staging area, one 16-row tile
   // at a time: the wave writes its results (accumulator layout: lane holds
   // column lane & 15 of each 16-column tile, rows 4*(lane >> 4) + v), then
@@ -286,13 +336,21 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
       constexpr int LDW = 72;
       bf16_t* wbuf = (bf16_t*)&stg[wave][0];
       const int col0 = nb * BN + wn * 64;
+      const float* sg = F8 ? group_scale(p, p.s0, p.s0_extra, t.group) : nullptr;
+      const float* su = F8 ? group_scale(p, p.s1, p.s1_extra, t.group) : nullptr;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
+        for (int n = 0; n < 4; ++n) {
+          // fp8: the scales of this lane's column (clamped: columns past N are never stored)
+          const int sc = col0 + n * 16 + (lane & 15) < p.N ? col0 + n * 16 + (lane & 15) : p.N - 1;
+          const float fg = F8 ? sg[sc] : 1.f, fu = F8 ? su[sc] : 1.f;
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            wbuf[(4 * (lane >> 4) + v) * LDW + n * 16 + (lane & 15)] = f32_to_bf16(silu(acc[m][n][v]) * acc[m][n + 4][v]);
+            wbuf[(4 * (lane >> 4) + v) * LDW + n * 16 + (lane & 15)] =
+                F8 ? f32_to_bf16(silu(acc[m][n][v] * fg) * (acc[m][n + 4][v] * fu))
+                   : f32_to_bf16(silu(acc[m][n][v]) * acc[m][n + 4][v]);
+        }
         // 8 lanes per row (16 bytes each), 8 rows per pass, 2 passes
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
@@ -310,15 +368,19 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
       // in different banks (no padding: the area is exactly 8 KB)
       float* wbuf = &stg[wave][0];
       const int col0 = nb * BN + wn * 128;
+      const float* sd = F8 ? group_scale(p, p.s0, p.s0_extra, t.group) : nullptr;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
 #pragma unroll
-        for (int n = 0; n < 8; ++n)
+        for (int n = 0; n < 8; ++n) {
+          const int sc = col0 + n * 16 + (lane & 15) < p.N ? col0 + n * 16 + (lane & 15) : p.N - 1;
+          const float fd = F8 ? sd[sc] : 1.f;
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int row = 4 * (lane >> 4) + v;
-            wbuf[row * 128 + ((n ^ ((row >> 2) & 3)) << 4) + (lane & 15)] = acc[m][n][v];
+            wbuf[row * 128 + ((n ^ ((row >> 2) & 3)) << 4) + (lane & 15)] = F8 ? acc[m][n][v] * fd : acc[m][n][v];
           }
+        }
         // 32 lanes per row (16 bytes each), 2 rows per pass, 8 passes
 #pragma unroll
         for (int pass = 0; pass < 8; ++pass) {
@@ -377,57 +439,113 @@ __global__ void __launch_bounds__(256) gemm_bf16_big(GemmArgs p) {
     map_item(L_next, t_next, nb_next);
     load_rows(t_next, rows);
   }
-  int baseA = 0, baseB = 0;  // slots of the current item's first A stage and first B step
-  const int lastA = nh - 1, lastB = nk - 1;
-  u32x4 a[8], b0[8], b1[8];
-  issue_a(0, 0);
-#pragma unroll
-  for (int s = 0; s < BIG_NS - 1; ++s) issue_b(s, s);  // nk >= 4: steps 0..2 exist
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));             // A stage 0, B step 0
-  asm volatile("s_barrier" ::: "memory");
-  read_b(0, b0);
-  auto step = [&](int k, auto ODD, const u32x4(&b_cur)[8], u32x4(&b_next)[8]) {
-    constexpr bool odd = decltype(ODD)::value;
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(odd ? 12 : 4));
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    const int h = k >> 1;
-    if constexpr (!odd) {
-      const int ha = h + 1;  // A stage to issue, counted from this item's start
-      if (ha == nh && has_next) set_a_sources(rows);  // from here on the next item's A stages
-      issue_a((baseA + ha) & 1, ha < nh ? ha : (has_next ? ha - nh : lastA));
+  if constexpr (!F8) {
+    int baseA = 0, baseB = 0;  // slots of the current item's first A stage and first B step
+    const int lastA = nh - 1, lastB = nk - 1;
+    u32x4 a[8], b0[8], b1[8];
+    issue_a(0, 0);
+  #pragma unroll
+    for (int s = 0; s < BIG_NS - 1; ++s) issue_b(s, s);  // nk >= 4: steps 0..2 exist
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));             // A stage 0, B step 0
+    asm volatile("s_barrier" ::: "memory");
+    read_b(0, b0);
+    auto step = [&](int k, auto ODD, const u32x4(&b_cur)[8], u32x4(&b_next)[8]) {
+      constexpr bool odd = decltype(ODD)::value;
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(odd ? 12 : 4));
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      const int h = k >> 1;
+      if constexpr (!odd) {
+        const int ha = h + 1;  // A stage to issue, counted from this item's start
+        if (ha == nh && has_next) set_a_sources(rows);  // from here on the next item's A stages
+        issue_a((baseA + ha) & 1, ha < nh ? ha : (has_next ? ha - nh : lastA));
+      }
+      const int ks = k + BIG_NS - 1;  // B step to issue, counted from this item's start
+      if (ks == nk && has_next) set_b_sources(t_next, nb_next);
+      issue_b((baseB + ks) % BIG_NS, ks < nk ? ks : (has_next ? ks - nk : lastB));
+      read_a((baseA + h) & 1, odd ? 1 : 0, a);
+      read_b((baseB + k + 1) % BIG_NS, b_next);
+      multiply(a, b_cur);
+    };
+    for (;;) {
+  #pragma unroll
+      for (int m = 0; m < 8; ++m)
+  #pragma unroll
+        for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // nk is even (the contraction is a multiple of 64): one A stage, two
+      // steps per trip, alternating the B register sets; every item starts
+      // with b0.
+  #pragma unroll 1
+      for (int k = 0; k < nk; k += 2) {
+        step(k, std::false_type{}, b0, b1);
+        step(k + 1, std::true_type{}, b1, b0);
+      }
+      epilogue(t_cur, nb_cur);
+      if (!has_next) break;
+      baseA = (baseA + nh) & 1;
+      baseB = (baseB + nk) % BIG_NS;
+      t_cur = t_next;
+      nb_cur = nb_next;
+      L_next += L_step;
+      has_next = L_next < L_end;
+      if (has_next) {
+        map_item(L_next, t_next, nb_next);
+        load_rows(t_next, rows);
+      }
     }
-    const int ks = k + BIG_NS - 1;  // B step to issue, counted from this item's start
-    if (ks == nk && has_next) set_b_sources(t_next, nb_next);
-    issue_b((baseB + ks) % BIG_NS, ks < nk ? ks : (has_next ? ks - nk : lastB));
-    read_a((baseA + h) & 1, odd ? 1 : 0, a);
-    read_b((baseB + k + 1) % BIG_NS, b_next);
-    multiply(a, b_cur);
-  };
-  for (;;) {
+  } else {
+    // fp8 weights: trips of one A stage and one weight stage (64 contraction
+    // elements, two MFMA steps), one wait and one barrier per trip. Per wave,
+    // trip h issues A(h+1) (8 loads) and then weight stage h+2 (4 loads); at
+    // the start of trip h, A(h) and weight stage h must have landed, so only
+    // weight stage h+1 (issued after A(h)) may still be in flight. A slot
+    // (h+1) % 2 was last read in trip h-1 and weight slot (h+2) % 4 in trip
+    // h-2, both before this trip's barrier. The weight codes of a stage are
+    // read once per trip, before the A chunks, and converted half by half.
+    int baseA = 0, baseB = 0;  // slots of the current item's first stages
+    const int last = nh - 1;
+    u32x4 a[8], b[8], raw[8];
+    issue_a(0, 0);
+    issue_b(0, 0);
+    issue_b(1, 1);  // nh >= 2: the contraction is at least 128
+    for (;;) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+      for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // nk is even (the contraction is a multiple of 64): one A stage, two
-    // steps per trip, alternating the B register sets; every item starts
-    // with b0.
+        for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-    for (int k = 0; k < nk; k += 2) {
-      step(k, std::false_type{}, b0, b1);
-      step(k + 1, std::true_type{}, b1, b0);
-    }
-    epilogue(t_cur, nb_cur);
-    if (!has_next) break;
-    baseA = (baseA + nh) & 1;
-    baseB = (baseB + nk) % BIG_NS;
-    t_cur = t_next;
-    nb_cur = nb_next;
-    L_next += L_step;
-    has_next = L_next < L_end;
-    if (has_next) {
-      map_item(L_next, t_next, nb_next);
-      load_rows(t_next, rows);
+      for (int h = 0; h < nh; ++h) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        const int ha = h + 1;  // A stage to issue, counted from this item's start
+        if (ha == nh && has_next) set_a_sources(rows);
+        issue_a((baseA + ha) & 1, ha < nh ? ha : (has_next ? ha - nh : last));
+        const int hb = h + 2;  // weight stage to issue
+        if (hb == nh && has_next) set_b_sources(t_next, nb_next);
+        issue_b((baseB + hb) % BIG_NS, hb < nh ? hb : (has_next ? hb - nh : last));
+        read_b8((baseB + h) % BIG_NS, raw);
+        read_a((baseA + h) & 1, 0, a);
+        asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");  // the 8 weight reads have landed
+        __builtin_amdgcn_sched_barrier(0);
+        convert_b(raw, 0, b);
+        multiply_a_only(a, b);
+        read_a((baseA + h) & 1, 1, a);
+        convert_b(raw, 1, b);
+        multiply_a_only(a, b);
+      }
+      epilogue(t_cur, nb_cur);
+      if (!has_next) break;
+      baseA = (baseA + nh) & 1;
+      baseB = (baseB + nh) % BIG_NS;
+      t_cur = t_next;
+      nb_cur = nb_next;
+      L_next += L_step;
+      has_next = L_next < L_end;
+      if (has_next) {
+        map_item(L_next, t_next, nb_next);
+        load_rows(t_next, rows);
+      }
     }
   }
   // drain the trailing reads and the loads of the clamped stages before the block ends
@@ -460,7 +578,10 @@ hipError_t launch_grouped_gemm_big(int epi, const GemmArgs& g, hipStream_t s) {
   int64_t blocks = ((int64_t)g.max_tiles * n_nb + 7) / 8 * 8;
   const int64_t cap = (int64_t)g_cus / 8 * 8;
   blocks = blocks < cap ? blocks : cap;
-  if (g.b_packed) {
+  if (g.b_fp8) {
+    if (epi == EPI_SWIGLU) gemm_bf16_big<EPI_SWIGLU, true, true><<<(unsigned)blocks, 256, 0, s>>>(g);
+    else gemm_bf16_big<EPI_F32, true, true><<<(unsigned)blocks, 256, 0, s>>>(g);
+  } else if (g.b_packed) {
     if (epi == EPI_SWIGLU) gemm_bf16_big<EPI_SWIGLU, true><<<(unsigned)blocks, 256, 0, s>>>(g);
     else gemm_bf16_big<EPI_F32, true><<<(unsigned)blocks, 256, 0, s>>>(g);
   } else {

@@ -70,6 +70,21 @@ __host__ __device__ __forceinline__ int64_t packed_offset(int64_t ct, int64_t kb
   return (ct * (K / 32) + kb) * PACKED_FRAG + lane * 8;
 }
 
+// FP8 E4M3 -> bf16, exactly (an E4M3 value has at most 4 significant bits):
+// the hardware conversion gives fp32 (OCP E4M3 on gfx950), whose upper 16
+// bits are the bf16 value. HI selects bytes 2-3 of w instead of 0-1.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16x2(uint32_t w) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xFFFF0000u);
+}
+// 8 codes (lo: the first 4, hi: the next 4) -> one bf16x8 MFMA operand
+__device__ __forceinline__ uint4 fp8x8_bf16x8(uint32_t lo, uint32_t hi) {
+  return make_uint4(fp8x2_bf16x2<false>(lo), fp8x2_bf16x2<true>(lo), fp8x2_bf16x2<false>(hi),
+                    fp8x2_bf16x2<true>(hi));
+}
+
 // Epilogues of the grouped GEMM.
 enum GemmEpilogue {
   EPI_SWIGLU = 0,  // two B operands (gate, up): out = dtype(silu(A Bg^T) * (A Bu^T))
@@ -109,6 +124,11 @@ struct GemmArgs {
   int32_t ksplit;         // EPI_F32 only: the contraction is cut into ksplit slices;
   int64_t slice_stride;   //   slice s writes its partial sums to out + s*slice_stride
 };
+
+// Per-column scales of group g (fp8 weights).
+__device__ __forceinline__ const float* group_scale(const GemmArgs& p, const float* main, const float* extra, int g) {
+  return g < p.n_main ? main + (int64_t)g * p.s_stride : extra;
+}
 
 // Launchers (grouped_gemm.hip). `dtype` is MOE_BF16 or MOE_F32 for A/B; the
 // SwiGLU output has the same dtype; EPI_F32 output is fp32.
