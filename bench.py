@@ -39,7 +39,7 @@ FLUSH_BYTES = 512 << 20
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "top_routed_expert_amd", "csrc", f)
-                  for f in ("grouped_gemm.hip", "grouped_gemm_big.hip", "moe_internal.h")]
+                  for f in ("grouped_gemm.hip", "grouped_gemm_big.hip", "grouped_gemm_big8.hip", "moe_internal.h")]
 
 
 def kernel_source_hash() -> str:
@@ -144,7 +144,7 @@ def gate_up_kernel(rows: int, groups: int) -> str:
     if rows <= 24 * groups:  # thresholds as gemm_block_rows
         return "gemm_bf16_mfma<EPI_SWIGLU>, 32-row tiles"
     if rows >= 96 * groups:
-        return "gemm_bf16_big<EPI_SWIGLU>, 256x256 tiles"
+        return "gemm_bf16_big8<EPI_SWIGLU>, 256x256 tiles, 8 waves"
     return "gemm_bf16_mfma<EPI_SWIGLU>, %d-row tiles" % (64 if rows <= 48 * groups else 128)
 
 

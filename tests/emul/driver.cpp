@@ -1,12 +1,15 @@
-// Bounds-checking driver for the 256x256 expert GEMM (grouped_gemm_big.hip
-// turned into host C++ by tests/test_gemm_big_bounds.py). It builds the
-// launch arguments of one workload the way the library does (random top-k
-// routing, the tile table, exact-size buffers for activations, weights,
-// outputs and tables) and runs every lane of every block of both
-// projections, packed and row-major, under AddressSanitizer.
+// Bounds-checking driver for the 256x256 expert GEMMs (grouped_gemm_big.hip
+// and grouped_gemm_big8.hip turned into host C++ by
+// tests/test_gemm_big_bounds.py). It builds the launch arguments of one
+// workload the way the library does (random top-k routing, the tile table,
+// exact-size buffers for activations, weights, outputs and tables) and runs
+// every lane of every block of both projections, packed and row-major, through
+// both kernels (fp8 weights: the four-wave kernel only), under
+// AddressSanitizer.
 //
 // usage: driver T E K D F Fs seed [skew] [fp8]
 #include <algorithm>
+#include <mutex>
 #include <random>
 #include <thread>
 #include <vector>
@@ -15,20 +18,29 @@ thread_local emul_dim3 threadIdx, blockIdx;
 emul_dim3 gridDim, blockDim;
 long long emul_loads = 0;
 
-static void* g_regions[8];
-static size_t g_sizes[8];
+// one region per LDS array of each kernel instantiation
+static void* g_regions[64];
+static size_t g_sizes[64];
 static int g_nreg = 0;
+static std::mutex g_reg_mu;
 uint32_t emul_lds_base(void* p, size_t bytes) {
+  std::lock_guard<std::mutex> lk(g_reg_mu);
   for (int i = 0; i < g_nreg; ++i)
     if (g_regions[i] == p) return (uint32_t)i << 20;
+  if (g_nreg == 64) { fprintf(stderr, "too many LDS regions\n"); abort(); }
   g_regions[g_nreg] = p;
   g_sizes[g_nreg] = bytes;
   return (uint32_t)(g_nreg++) << 20;
 }
 void* emul_lds_region_ptr(uint32_t vaddr, int bytes) {
+  int n;
+  {
+    std::lock_guard<std::mutex> lk(g_reg_mu);
+    n = g_nreg;
+  }
   const int r = (int)(vaddr >> 20);
   const uint32_t off = vaddr & 0xfffff;
-  if (r >= g_nreg || off + bytes > g_sizes[r]) {
+  if (r >= n || off + bytes > g_sizes[r]) {
     fprintf(stderr, "LDS read out of range: region %d offset %u (+%d); block %u thread %u\n", r, off, bytes,
             blockIdx.x, threadIdx.x);
     abort();
@@ -40,13 +52,13 @@ void emul_global_load_lds(const void* src, void* dst, int bytes) {
   memcpy((char*)dst + lane * bytes, src, bytes);
   __atomic_fetch_add(&emul_loads, 1, __ATOMIC_RELAXED);
 }
-template <class K, class A> void emul_launch(K kernel, unsigned blocks, const A& args) {
+template <class K, class A> void emul_launch(K kernel, unsigned blocks, unsigned threads, const A& args) {
   gridDim.x = blocks;
   std::vector<std::thread> th;
   for (int w = 0; w < 8; ++w)
     th.emplace_back([&, w] {
       for (unsigned b = w; b < blocks; b += 8)
-        for (unsigned t = 0; t < 256; ++t) {
+        for (unsigned t = 0; t < threads; ++t) {
           blockIdx.x = b;
           threadIdx.x = t;
           kernel(args);
@@ -111,8 +123,10 @@ int main(int argc, char** argv) {
   *n_tiles = (int32_t)tv.size();
   printf("T=%d E=%d K=%d D=%d F=%d Fs=%d skew=%d: %zu tiles\n", T, E, K, D, F, Fs, (int)skew, tv.size());
   auto pad16 = [](int n) { return (n + 15) / 16 * 16; };
+  for (int waves : {4, 8})
   for (int epi : {EPI_SWIGLU, EPI_F32})
     for (int pk = 1; pk >= (fp8 ? 1 : 0); --pk) {
+      if (fp8 && waves == 8) continue;  // fp8 weights take the four-wave kernel
       GemmArgs g{};
       g.tiles = tiles;
       g.n_tiles = n_tiles;
@@ -174,8 +188,8 @@ int main(int argc, char** argv) {
       g.s0_extra = s0x;
       g.s1_extra = s1x;
       emul_loads = 0;
-      const int rc = launch_grouped_gemm_big(epi, g, nullptr);
-      printf("  %s %s: rc=%d direct loads %lld ok\n", epi == EPI_SWIGLU ? "gate/up" : "down",
+      const int rc = waves == 8 ? launch_grouped_gemm_big8(epi, g, nullptr) : launch_grouped_gemm_big(epi, g, nullptr);
+      printf("  %d waves, %s %s: rc=%d direct loads %lld ok\n", waves, epi == EPI_SWIGLU ? "gate/up" : "down",
              fp8 ? "fp8" : (pk ? "packed" : "rows"), rc, emul_loads);
       fflush(stdout);
       if (rc != 0) return 3;

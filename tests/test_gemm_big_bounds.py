@@ -1,7 +1,7 @@
-"""Bounds check of the 256x256 expert GEMM without a GPU.
+"""Bounds check of the 256x256 expert GEMMs without a GPU.
 
-The kernel source (top_routed_expert_amd/csrc/grouped_gemm_big.hip) is turned
-into host C++: HIP keywords and builtins become plain functions (tests/emul/
+The kernel sources (top_routed_expert_amd/csrc/grouped_gemm_big.hip, four
+waves, and grouped_gemm_big8.hip, eight waves) are turned into host C++: HIP keywords and builtins become plain functions (tests/emul/
 shim.h), the inline-asm LDS reads become checked reads, the kernel launches
 become loops that run every lane of every block in turn. tests/emul/driver.cpp
 builds the launch arguments the way the library does, with exact-size buffers,
@@ -36,8 +36,8 @@ def _clang() -> str | None:
 def host_source(kernel_src: str) -> str:
     """The kernel source rewritten for the host build (see the module docstring)."""
     s = kernel_src.replace('#include "moe_internal.h"', '#include "emul_internal.h"')
-    s = s.replace("typedef __attribute__((address_space(3))) void lds_void_t;", "typedef void lds_void_t;")
-    s, k0 = re.subn(r"\(uint32_t\)\(uintptr_t\)\(lds_void_t\*\)&(\w+)\[0\]\[0\]",
+    s, _ = re.subn(r"typedef __attribute__\(\(address_space\(3\)\)\) void (lds8?_void_t);", r"typedef void \1;", s)
+    s, k0 = re.subn(r"\(uint32_t\)\(uintptr_t\)\(lds8?_void_t\*\)&(\w+)\[0\]\[0\]",
                     lambda m: f"emul_lds_base((void*)&{m.group(1)}, sizeof({m.group(1)}))", s)
     s, k1 = re.subn(r'asm volatile\("ds_read_b128 %0, %1 offset:%2" : "=v"\(([^)]*)\) : "v"\((\w+)\), '
                     r'"n"\(([^)]*)\)\);',
@@ -46,11 +46,20 @@ def host_source(kernel_src: str) -> str:
     s, _ = re.subn(r'asm volatile\("s_waitcnt lgkmcnt\(%1\)" : "\+v"\([^)]*\) : "n"\([^)]*\)\);', ";", s)
     s, _ = re.subn(r'asm volatile\("[^"]*" ::: "memory"\);', ";", s)
     s, _ = re.subn(r'asm volatile\("s_waitcnt lgkmcnt\(%1\)" : "\+v"\([^)]*\) : "n"\([^)]*\)\);', ";", s)
-    s, k4 = re.subn(r"(gemm_bf16_big<[^>]*>)<<<\(unsigned\)blocks, 256, 0, s>>>\(g\);",
-                    lambda m: f"emul_launch({m.group(1)}, (unsigned)blocks, g);", s)
+    s, k4 = re.subn(r"(gemm_bf16_big8?<[^>]*>)<<<\(unsigned\)blocks, (256|512), 0, s>>>\(g\);",
+                    lambda m: f"emul_launch({m.group(1)}, (unsigned)blocks, {m.group(2)}, g);", s)
     left = re.findall(r"asm volatile.*|<<<.*>>>", s)
-    assert k0 >= 1 and k1 >= 3 and k4 == 6 and not left, (k0, k1, k4, left)
+    assert k0 >= 1 and k1 >= 2 and k4 >= 4 and not left, (k0, k1, k4, left)
     return s
+
+
+def host_sources(four: str, eight: str) -> str:
+    """Both kernels in one host translation unit (their helpers have distinct names)."""
+    return host_source(four) + "\n" + host_source(eight).replace('#include "emul_internal.h"', "")
+
+
+def kernel_sources() -> tuple[str, str]:
+    return tuple(open(os.path.join(CSRC, f)).read() for f in ("grouped_gemm_big.hip", "grouped_gemm_big8.hip"))
 
 
 @pytest.fixture(scope="module")
@@ -62,7 +71,7 @@ def driver(tmp_path_factory):
     hdr = open(os.path.join(CSRC, "moe_internal.h")).read().replace("#include <hip/hip_runtime.h>",
                                                                     '#include "shim.h"')
     open(d / "emul_internal.h", "w").write(hdr)
-    open(d / "emul_big.cpp", "w").write(host_source(open(os.path.join(CSRC, "grouped_gemm_big.hip")).read()))
+    open(d / "emul_big.cpp", "w").write(host_sources(*kernel_sources()))
     exe = d / "driver"
     cmd = [cc, "-std=c++17", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer", "-pthread",
            "-I", str(d), "-I", EMUL, "-I", os.path.join(ROOT, "include"), os.path.join(EMUL, "driver.cpp"),
@@ -95,20 +104,23 @@ def test_big_gemm_accesses_stay_in_bounds(driver, name):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0")
     r = subprocess.run([driver, *map(str, SHAPES[name])], capture_output=True, text=True, timeout=600, env=env)
     assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-4000:])
-    assert r.stdout.count(" ok") == (2 if name.startswith("fp8") else 4), r.stdout
+    assert r.stdout.count(" ok") == (2 if name.startswith("fp8") else 8), r.stdout
 
 
-def test_planted_offset_is_caught(driver, tmp_path):
-    """The check itself: an A row offset one row too far must be reported."""
-    src = open(os.path.join(CSRC, "grouped_gemm_big.hip")).read()
+@pytest.mark.parametrize("which", [0, 1])
+def test_planted_offset_is_caught(driver, tmp_path, which):
+    """The check itself: an A row offset one row too far, in either kernel, must be reported."""
+    srcs = list(kernel_sources())
+    src = srcs[which]
     planted = src.replace("aoff[i] = (uint32_t)rows[i] * (uint32_t)(Kdim >> 3)",
                           "aoff[i] = (uint32_t)(rows[i] + 1) * (uint32_t)(Kdim >> 3)")
     assert planted != src
+    srcs[which] = planted
     d = os.path.dirname(driver)
     work = tmp_path / "planted"
     work.mkdir()
     shutil.copy(os.path.join(d, "emul_internal.h"), work / "emul_internal.h")
-    open(work / "emul_big.cpp", "w").write(host_source(planted))
+    open(work / "emul_big.cpp", "w").write(host_sources(*srcs))
     exe = work / "driver"
     r = subprocess.run([_clang(), "-std=c++17", "-O1", "-g", "-fsanitize=address", "-pthread", "-I", str(work),
                         "-I", EMUL, "-I", os.path.join(ROOT, "include"), os.path.join(EMUL, "driver.cpp"), "-o",
