@@ -39,7 +39,7 @@ FLUSH_BYTES = 512 << 20
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "top_routed_expert_amd", "csrc", f)
-                  for f in ("grouped_gemm.hip", "grouped_gemm_big.hip", "grouped_gemm_big8.hip", "moe_internal.h")]
+                  for f in ("grouped_gemm.hip", "grouped_gemm_big8.hip", "moe_internal.h")]
 
 
 def kernel_source_hash() -> str:

@@ -1,10 +1,10 @@
-// Bounds-checking driver for the 256x256 expert GEMMs (grouped_gemm_big.hip
-// and grouped_gemm_big8.hip turned into host C++ by
+// Bounds-checking driver for the 256x256 expert GEMM (grouped_gemm_big8.hip
+// turned into host C++ by
 // tests/test_gemm_big_bounds.py). It builds the launch arguments of one
 // workload the way the library does (random top-k routing, the tile table,
 // exact-size buffers for activations, weights, outputs and tables) and runs
-// every lane of every block of both projections, packed and row-major, through
-// both kernels (fp8 weights: the four-wave kernel only), under
+// every lane of every block of both projections, packed and row-major (fp8
+// weights: packed only), under
 // AddressSanitizer.
 //
 // usage: driver T E K D F Fs seed [skew] [fp8]
@@ -123,10 +123,8 @@ int main(int argc, char** argv) {
   *n_tiles = (int32_t)tv.size();
   printf("T=%d E=%d K=%d D=%d F=%d Fs=%d skew=%d: %zu tiles\n", T, E, K, D, F, Fs, (int)skew, tv.size());
   auto pad16 = [](int n) { return (n + 15) / 16 * 16; };
-  for (int waves : {4, 8})
   for (int epi : {EPI_SWIGLU, EPI_F32})
     for (int pk = 1; pk >= (fp8 ? 1 : 0); --pk) {
-      if (fp8 && waves == 8) continue;  // fp8 weights take the four-wave kernel
       GemmArgs g{};
       g.tiles = tiles;
       g.n_tiles = n_tiles;
@@ -188,8 +186,8 @@ int main(int argc, char** argv) {
       g.s0_extra = s0x;
       g.s1_extra = s1x;
       emul_loads = 0;
-      const int rc = waves == 8 ? launch_grouped_gemm_big8(epi, g, nullptr) : launch_grouped_gemm_big(epi, g, nullptr);
-      printf("  %d waves, %s %s: rc=%d direct loads %lld ok\n", waves, epi == EPI_SWIGLU ? "gate/up" : "down",
+      const int rc = launch_grouped_gemm_big8(epi, g, nullptr);
+      printf("  %s %s: rc=%d direct loads %lld ok\n", epi == EPI_SWIGLU ? "gate/up" : "down",
              fp8 ? "fp8" : (pk ? "packed" : "rows"), rc, emul_loads);
       fflush(stdout);
       if (rc != 0) return 3;

@@ -489,9 +489,7 @@ hipError_t launch_grouped_gemm(int dtype, bool fast, int epi, int block_rows, co
     }
     return hipGetLastError();
   }
-  // 256-row tiles: eight waves for bf16 weights, four for fp8 (whose in-register
-  // dequantisation needs the registers a second wave per SIMD would take)
-  if (block_rows == 256) return g.b_fp8 ? launch_grouped_gemm_big(epi, g, s) : launch_grouped_gemm_big8(epi, g, s);
+  if (block_rows == 256) return launch_grouped_gemm_big8(epi, g, s);
   const bool narrow = g.N <= 512;  // router-sized outputs: 64 columns per block
   if (block_rows == 64) {
     if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 4, 2, MOE_NS_SMALL>(g, s);

@@ -1,27 +1,63 @@
-// Expert GEMMs for many rows per expert, bf16 weights: 256 x 256 block
-// tiles with eight waves, two per SIMD.
+// Expert GEMMs for many rows per expert (prefill): 256 x 256 block tiles,
+// eight waves, bf16 or fp8 weights.
 //
 // Every expert is an independent FFN (page "Step3.5 Flash 大模型技术深度解析",
-// section 3.2.1). The work item, the persistent walk over items, the two
-// rings (gathered activation rows in 64-element stages, 128 bytes of a row;
-// weights in 32-element steps) and the explicit waits are those of the
-// four-wave kernel in grouped_gemm_big.hip. The difference is the wave
-// layout: eight waves in a 2 x 4 arrangement, each wave 128 rows x 64 weight
-// rows = 8 x 4 MFMA 16x16x32 tiles (128 fp32 accumulators), so two waves
+// section 3.2.1). With a few hundred rows per expert, the weights of one
+// column block should leave HBM once and be multiplied by all of the
+// expert's rows; a 256-row tile covers a whole expert in most cases.
+//
+// Work item: one (row tile, column block) pair, 256 rows x 256 weight rows.
+// Block: eight waves in a 2 x 4 layout, each wave 128 rows x 64 weight rows
+// = 8 x 4 MFMA 16x16x32 tiles (128 fp32 accumulators per lane), so two waves
 // share each SIMD: while one waits at a barrier, for LDS reads or for its
 // loads to be issued, the other keeps the matrix core busy, and two waves
-// interleaving their MFMAs reach a higher issue rate than one (about 86% of
-// peak against 72% back to back). The price is 50% more LDS operand reads
-// per step (96 KB for the block against 64 KB); gfx950's LDS serves about
-// 220 bytes per clock per CU, about twice what a step of multiplies needs.
+// interleaving their MFMAs issue faster than one back to back. For gate/up
+// the 256 weight rows of an item are 4 x [gate c0+32j .. c0+32j+31, up
+// c0+32j .. c0+32j+31] (j = 0..3), so wave (wm, j) holds the gate and up
+// sums of the same 32 output columns and applies the SwiGLU in registers.
 //
-// For gate/up the 256 weight rows of an item are 4 x [gate c0+32j ..
-// c0+32j+31, up c0+32j .. c0+32j+31] (j = 0..3), so wave (wm, j) holds the
-// gate and up sums of the same 32 output columns and applies the SwiGLU in
-// registers.
+// Persistent blocks: one block per CU walks its share of the items (split
+// evenly over the 8 XCDs, column blocks fastest; the row tiles of a group
+// with several run in chunks, row tile fastest, so blocks running together
+// read the same weight columns). The load stream runs on across items: the
+// last stages of an item issue the first stages of the next one, so items
+// meet with no pipeline drain and an item's epilogue (results through LDS
+// to HBM) runs while the next item's operands are already in flight.
 //
-// Loads per wave: an A stage is 4 direct loads (8 rows x 128 bytes each),
-// a weight step 2 (one 16-row fragment or 16 rows x 64 bytes each).
+// Both operands go HBM/L2 -> LDS through direct loads (global_load_lds, 16
+// bytes per lane, no VGPR staging). The weights stream from HBM through a
+// ring of 4 slots of 16 KB (bf16: one 32-element MFMA step per slot),
+// non-temporal since each weight byte is used by one block. The gathered
+// activation rows come mostly from L2 and move in stages of two MFMA steps,
+// 128 bytes of each row (32 KB per stage, two slots): a 64-byte piece of a
+// row uses half of a 128-byte cache line, and fetching whole lines raises
+// the per-CU fetch rate of the gathered rows by about 40%. With a 32 KB
+// epilogue staging area that fills the 160 KB of LDS. The weight operand of
+// a step is read from LDS into registers one step ahead (two register sets)
+// and the activation operand row tile by row tile in the step itself. Waits
+// are explicit: a wave waits for its own loads with s_waitcnt vmcnt (loads
+// complete in issue order), then one s_barrier per step makes every wave's
+// loads visible and ends every wave's reads of the slots about to be
+// refilled. The barrier is inline asm with a memory clobber, so the
+// compiler moves no memory access across it and adds no drain of its own.
+//
+// Activation rows in LDS are 128 bytes (eight 16-byte chunks); chunk q of
+// row r is stored at q ^ ((r >> 1) & 7), so the 16-byte operand reads of 16
+// consecutive rows cover all banks once. Weight rows without packing are 64
+// bytes with chunk q at q ^ ((r >> 1) & 3); with packed weights each 16-row
+// group is one 1 KB fragment copied as it is (lane order).
+//
+// Loads per wave: an activation stage is 4 direct loads (8 rows x 128 bytes
+// each), a weight step 2 (one 16-row fragment or 16 rows x 64 bytes each).
+//
+// FP8 weights (F8, packed): a weight stage holds 64 contraction elements of
+// E4M3 codes (one 1 KB fragment per 16 weight rows, the same 16 KB slot), so
+// both operands move in 64-element stages and a trip of two MFMA steps
+// needs one wait and one barrier. Each wave reads its 4 fragments once per
+// trip, converts the first halves of the codes to bf16 operands for the
+// first step and the second halves for the second (the conversion is exact),
+// and the epilogue multiplies by the per-column scales. The other wave of
+// the SIMD multiplies while one waits for its codes or converts them.
 #include "moe_internal.h"
 
 // The operand-read lambdas capture their asm operands explicitly (clang's
@@ -48,8 +84,9 @@ constexpr int waitcnt_vm8(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 <<
 __device__ __forceinline__ int swz8(int row) { return (row >> 1) & 3; }   // 64-byte weight rows
 __device__ __forceinline__ int swzA8(int row) { return (row >> 1) & 7; }  // 128-byte A rows
 
-template <int EPI, bool PK>
+template <int EPI, bool PK, bool F8 = false>
 __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
+  static_assert(!F8 || PK, "fp8 weights are packed");
   __shared__ __attribute__((aligned(16))) bf16_t ldsA[2][B8_ROWS * B8_AKS];
   __shared__ __attribute__((aligned(16))) bf16_t ldsB[B8_NS][B8_ROWS * B8_KS];
   __shared__ __attribute__((aligned(16))) float stg[8][1024];  // epilogue staging, 4 KB per wave
@@ -122,12 +159,16 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
   // weight load instruction i (0..1) of this wave fills weight rows
   // wave*32 + i*16 .. +15: the fragment of those rows (packed) or row
   // +l/4, chunk (l%4) ^ swz8(row) (row-major)
+  // (fp8: byte pointers into the codes, kept in the same bf16_t* slots)
+  constexpr int64_t EB = F8 ? 1 : 2;  // bytes per weight element
   auto set_b_sources = [&](const Tile& t, int nb) {
-    const bf16_t* Bg = t.group < p.n_main ? (const bf16_t*)p.b0 + (int64_t)t.group * p.b_stride
-                                          : (const bf16_t*)p.b0_extra;
-    const bf16_t* Bu = EPI == EPI_SWIGLU ? (t.group < p.n_main ? (const bf16_t*)p.b1 + (int64_t)t.group * p.b_stride
-                                                               : (const bf16_t*)p.b1_extra)
-                                         : Bg;
+    const bf16_t* Bg = (const bf16_t*)(t.group < p.n_main ? (const char*)p.b0 + (int64_t)t.group * p.b_stride * EB
+                                                          : (const char*)p.b0_extra);
+    const bf16_t* Bu =
+        EPI == EPI_SWIGLU
+            ? (const bf16_t*)(t.group < p.n_main ? (const char*)p.b1 + (int64_t)t.group * p.b_stride * EB
+                                                 : (const char*)p.b1_extra)
+            : Bg;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = wave * 32 + i * 16 + (lane >> 2);
@@ -141,7 +182,12 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
         col = nb * BN + row;
         base = Bg;
       }
-      if constexpr (PK) {
+      if constexpr (F8) {
+        int ct = (col - (row & 15)) >> 4;
+        const int ct_last = (p.N + 15) / 16 - 1;
+        ct = ct < ct_last ? ct : ct_last;
+        bsrc[i] = (const bf16_t*)((const char*)base + fp8_offset(ct, 0, lane, Kdim));
+      } else if constexpr (PK) {
         int ct = (col - (row & 15)) >> 4;
         const int ct_last = (p.N + 15) / 16 - 1;
         ct = ct < ct_last ? ct : ct_last;
@@ -158,11 +204,13 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
       __builtin_amdgcn_global_load_lds((const void*)(A + (uint64_t)aoff[i] * 8u + ja * B8_AKS),
                                        (lds8_void_t*)&ldsA[slot][(wave * 32 + i * 8) * B8_AKS], 16, 0, 0);
   };
-  auto issue_b = [&](int slot, int ks) {
+  auto issue_b = [&](int slot, int ks) {  // ks: a 32-element step (bf16) or a 64-element stage (fp8)
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + (PK ? ks * PACKED_FRAG : ks * B8_KS)),
-                                       (lds8_void_t*)&ldsB[slot][(wave * 32 + i * 16) * B8_KS], 16, 0, B8_CPOL_NT);
+      __builtin_amdgcn_global_load_lds(
+          F8 ? (const void*)((const char*)bsrc[i] + (int64_t)ks * FP8_FRAG)
+             : (const void*)(bsrc[i] + (PK ? ks * PACKED_FRAG : ks * B8_KS)),
+          (lds8_void_t*)&ldsB[slot][(wave * 32 + i * 16) * B8_KS], 16, 0, B8_CPOL_NT);
   };
 
   // wave (wm, wn): rows wm*128 .., weight rows wn*64 ..
@@ -206,6 +254,36 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
     });
   };
 
+  // fp8: this wave's 4 weight fragments of a stage, 16 bytes per lane (both
+  // MFMA steps' codes); raw[n] lands at lgkmcnt(11 - n) when the 8 A reads
+  // follow them.
+  auto read_b8 = [&](int slot, u32x4_8(&raw)[4]) {
+    const uint32_t addr = ldsB_base + (uint32_t)slot * SLOT_B + (uint32_t)(wn * 4) * 1024u + (uint32_t)lane * 16u;
+    static_for<0, 4>([&raw, addr](auto N) {
+      constexpr int n = decltype(N)::value;
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(raw[n]) : "v"(addr), "n"(n * 1024));
+    });
+  };
+  // operands of MFMA step `hi` (0, 1) of a stage from the raw codes
+  auto convert_b = [&](const u32x4_8(&raw)[4], int hi, u32x4_8(&b)[4]) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const uint4 v = hi ? fp8x8_bf16x8(raw[n].z, raw[n].w) : fp8x8_bf16x8(raw[n].x, raw[n].y);
+      b[n] = u32x4_8{v.x, v.y, v.z, v.w};
+    }
+  };
+  // multiply with the A chunks as the only LDS reads in flight behind them
+  auto multiply_a_only = [&](u32x4_8(&a)[8], const u32x4_8(&b)[4]) {
+    static_for<0, 8>([&](auto M) {
+      constexpr int m = decltype(M)::value;
+      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a[m]) : "n"(7 - m));
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_8(a[m]), as_bf16x8_8(b[n]), acc[m][n], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
   // Epilogue through this wave's 4 KB staging area, one 16-row tile at a
   // time (accumulator layout: lane holds column lane & 15 of each 16-column
   // tile, rows 4*(lane >> 4) + v); whole rows are stored 16 bytes per lane.
@@ -214,13 +292,27 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
       constexpr int LDW = 40;  // 16 rows x 32 bf16 columns, rows padded to 40
       bf16_t* wbuf = (bf16_t*)&stg[wave][0];
       const int col0 = nb * BN + wn * 32;
+      // fp8: the scales of this lane's columns (clamped: columns past N are never stored)
+      float fg[2] = {1.f, 1.f}, fu[2] = {1.f, 1.f};
+      if constexpr (F8) {
+        const float* sg = group_scale(p, p.s0, p.s0_extra, t.group);
+        const float* su = group_scale(p, p.s1, p.s1_extra, t.group);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const int sc = col0 + n * 16 + (lane & 15) < p.N ? col0 + n * 16 + (lane & 15) : p.N - 1;
+          fg[n] = sg[sc];
+          fu[n] = su[sc];
+        }
+      }
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            wbuf[(4 * (lane >> 4) + v) * LDW + n * 16 + (lane & 15)] = f32_to_bf16(silu(acc[m][n][v]) * acc[m][n + 2][v]);
+            wbuf[(4 * (lane >> 4) + v) * LDW + n * 16 + (lane & 15)] =
+                F8 ? f32_to_bf16(silu(acc[m][n][v] * fg[n]) * (acc[m][n + 2][v] * fu[n]))
+                   : f32_to_bf16(silu(acc[m][n][v]) * acc[m][n + 2][v]);
         // 4 lanes per row (8 bf16 each), 16 rows: one pass
         const int rr16 = lane >> 2, c8 = (lane & 3) * 8;
         const uint4 v = *(const uint4*)&wbuf[rr16 * LDW + c8];
@@ -233,6 +325,15 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
       // 16 rows x 64 fp32 columns; 16-column groups XOR-swizzled by (row >> 2) & 3
       float* wbuf = &stg[wave][0];
       const int col0 = nb * BN + wn * 64;
+      float fd[4] = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (F8) {
+        const float* sd = group_scale(p, p.s0, p.s0_extra, t.group);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int sc = col0 + n * 16 + (lane & 15) < p.N ? col0 + n * 16 + (lane & 15) : p.N - 1;
+          fd[n] = sd[sc];
+        }
+      }
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
 #pragma unroll
@@ -240,7 +341,7 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int row = 4 * (lane >> 4) + v;
-            wbuf[row * 64 + ((n ^ ((row >> 2) & 3)) << 4) + (lane & 15)] = acc[m][n][v];
+            wbuf[row * 64 + ((n ^ ((row >> 2) & 3)) << 4) + (lane & 15)] = F8 ? acc[m][n][v] * fd[n] : acc[m][n][v];
           }
         // 16 lanes per row (4 floats each), 4 rows per pass, 4 passes
 #pragma unroll
@@ -264,10 +365,25 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
     }
   };
 
-  // Rings and steps as in the four-wave kernel, with this wave's loads:
-  // even step k issues A(k/2+1) (4 loads) and weight step k+3 (2); odd step
-  // k weight step k+3 (2). At even k the loads younger than those waited for
-  // are weight step k+2 (2); at odd k, A(k/2+1) and weight step k+2 (6).
+  // Each ring holds stages in one sequence running across this block's
+  // items. Weights: global step s (item j, step k: s = j*nk + k) lives in
+  // slot s % 4; while step k is multiplied the ring holds steps k .. k+3
+  // (landed or in flight). Activations: global stage (item j, stage h:
+  // j*nk/2 + h, covering steps 2h and 2h+1) lives in slot stage % 2; while
+  // stage h is multiplied stage h+1 is in flight. After the last item,
+  // stages past its end re-load its last stage (never multiplied), so every
+  // trip issues the same loads and fixed wait counts hold.
+  //
+  // Step k: (1) wait until this wave's loads of weight step k+1 (and, for
+  // even k, of activation stage k/2) have landed; (2) lgkmcnt(0) + barrier:
+  // every wave's loads are visible and every wave has finished reading
+  // weight step k-1 (and, for even k, stage k/2-1), so (3) those slots are
+  // refilled: even k issues stage k/2+1 (4 loads per lane) and weight step
+  // k+3 (2), odd k weight step k+3 (2), of this item or else of the next
+  // one; (4) the activation chunks of step k and the weight chunks of step
+  // k+1 are read from LDS while (5) the matrix cores multiply step k. At
+  // even k the loads younger than those waited for are weight step k+2 (2);
+  // at odd k, stage k/2+1 and weight step k+2 (6).
   const int nh = nk >> 1;
   Tile t_cur, t_next;
   int nb_cur, nb_next;
@@ -282,54 +398,109 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
     map_item(L_next, t_next, nb_next);
     load_rows(t_next, rows);
   }
-  int baseA = 0, baseB = 0;
-  const int lastA = nh - 1, lastB = nk - 1;
-  u32x4_8 a[8], b0[4], b1[4];
-  issue_a(0, 0);
-#pragma unroll
-  for (int s = 0; s < B8_NS - 1; ++s) issue_b(s, s);  // nk >= 4
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm8(4));          // A stage 0, weight step 0
-  asm volatile("s_barrier" ::: "memory");
-  read_b(0, b0);
-  auto step = [&](int k, auto ODD, const u32x4_8(&b_cur)[4], u32x4_8(&b_next)[4]) {
-    constexpr bool odd = decltype(ODD)::value;
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm8(odd ? 6 : 2));
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    const int h = k >> 1;
-    if constexpr (!odd) {
-      const int ha = h + 1;
-      if (ha == nh && has_next) set_a_sources(rows);
-      issue_a((baseA + ha) & 1, ha < nh ? ha : (has_next ? ha - nh : lastA));
+  if constexpr (!F8) {
+    int baseA = 0, baseB = 0;
+    const int lastA = nh - 1, lastB = nk - 1;
+    u32x4_8 a[8], b0[4], b1[4];
+    issue_a(0, 0);
+  #pragma unroll
+    for (int s = 0; s < B8_NS - 1; ++s) issue_b(s, s);  // nk >= 4
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm8(4));          // A stage 0, weight step 0
+    asm volatile("s_barrier" ::: "memory");
+    read_b(0, b0);
+    auto step = [&](int k, auto ODD, const u32x4_8(&b_cur)[4], u32x4_8(&b_next)[4]) {
+      constexpr bool odd = decltype(ODD)::value;
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm8(odd ? 6 : 2));
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      const int h = k >> 1;
+      if constexpr (!odd) {
+        const int ha = h + 1;
+        if (ha == nh && has_next) set_a_sources(rows);
+        issue_a((baseA + ha) & 1, ha < nh ? ha : (has_next ? ha - nh : lastA));
+      }
+      const int ks = k + B8_NS - 1;
+      if (ks == nk && has_next) set_b_sources(t_next, nb_next);
+      issue_b((baseB + ks) % B8_NS, ks < nk ? ks : (has_next ? ks - nk : lastB));
+      read_a((baseA + h) & 1, odd ? 1 : 0, a);
+      read_b((baseB + k + 1) % B8_NS, b_next);
+      multiply(a, b_cur);
+    };
+    for (;;) {
+  #pragma unroll
+      for (int m = 0; m < 8; ++m)
+  #pragma unroll
+        for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll 1
+      for (int k = 0; k < nk; k += 2) {
+        step(k, std::false_type{}, b0, b1);
+        step(k + 1, std::true_type{}, b1, b0);
+      }
+      epilogue(t_cur, nb_cur);
+      if (!has_next) break;
+      baseA = (baseA + nh) & 1;
+      baseB = (baseB + nk) % B8_NS;
+      t_cur = t_next;
+      nb_cur = nb_next;
+      L_next += L_step;
+      has_next = L_next < L_end;
+      if (has_next) {
+        map_item(L_next, t_next, nb_next);
+        load_rows(t_next, rows);
+      }
     }
-    const int ks = k + B8_NS - 1;
-    if (ks == nk && has_next) set_b_sources(t_next, nb_next);
-    issue_b((baseB + ks) % B8_NS, ks < nk ? ks : (has_next ? ks - nk : lastB));
-    read_a((baseA + h) & 1, odd ? 1 : 0, a);
-    read_b((baseB + k + 1) % B8_NS, b_next);
-    multiply(a, b_cur);
-  };
-  for (;;) {
+  } else {
+    // fp8 weights: trips of one A stage and one weight stage (64 contraction
+    // elements, two MFMA steps), one wait and one barrier per trip. Per wave,
+    // trip h issues A(h+1) (4 loads) and then weight stage h+2 (2 loads); at
+    // the start of trip h, A(h) and weight stage h must have landed, so only
+    // weight stage h+1 (issued after A(h)) may still be in flight. A slot
+    // (h+1) % 2 was last read in trip h-1 and weight slot (h+2) % 4 in trip
+    // h-2, both before this trip's barrier.
+    int baseA = 0, baseB = 0;  // slots of the current item's first stages
+    const int last = nh - 1;
+    u32x4_8 a[8], b[4], raw[4];
+    issue_a(0, 0);
+    issue_b(0, 0);
+    issue_b(1, 1);  // nh >= 2: the contraction is at least 128
+    for (;;) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+      for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-    for (int k = 0; k < nk; k += 2) {
-      step(k, std::false_type{}, b0, b1);
-      step(k + 1, std::true_type{}, b1, b0);
-    }
-    epilogue(t_cur, nb_cur);
-    if (!has_next) break;
-    baseA = (baseA + nh) & 1;
-    baseB = (baseB + nk) % B8_NS;
-    t_cur = t_next;
-    nb_cur = nb_next;
-    L_next += L_step;
-    has_next = L_next < L_end;
-    if (has_next) {
-      map_item(L_next, t_next, nb_next);
-      load_rows(t_next, rows);
+      for (int h = 0; h < nh; ++h) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm8(2));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        const int ha = h + 1;  // A stage to issue, counted from this item's start
+        if (ha == nh && has_next) set_a_sources(rows);
+        issue_a((baseA + ha) & 1, ha < nh ? ha : (has_next ? ha - nh : last));
+        const int hb = h + 2;  // weight stage to issue
+        if (hb == nh && has_next) set_b_sources(t_next, nb_next);
+        issue_b((baseB + hb) % B8_NS, hb < nh ? hb : (has_next ? hb - nh : last));
+        read_b8((baseB + h) % B8_NS, raw);
+        read_a((baseA + h) & 1, 0, a);
+        asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");  // the 4 weight reads have landed
+        __builtin_amdgcn_sched_barrier(0);
+        convert_b(raw, 0, b);
+        multiply_a_only(a, b);
+        read_a((baseA + h) & 1, 1, a);
+        convert_b(raw, 1, b);
+        multiply_a_only(a, b);
+      }
+      epilogue(t_cur, nb_cur);
+      if (!has_next) break;
+      baseA = (baseA + nh) & 1;
+      baseB = (baseB + nh) % B8_NS;
+      t_cur = t_next;
+      nb_cur = nb_next;
+      L_next += L_step;
+      has_next = L_next < L_end;
+      if (has_next) {
+        map_item(L_next, t_next, nb_next);
+        load_rows(t_next, rows);
+      }
     }
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -342,7 +513,7 @@ int g_cus8 = 0;  // compute units of the device (queried once)
 
 hipError_t launch_grouped_gemm_big8(int epi, const GemmArgs& g, hipStream_t s) {
   if (g.max_tiles <= 0 || g.N <= 0) return hipSuccess;
-  if (g.b_fp8) return hipErrorInvalidValue;  // fp8 weights take the four-wave kernel
+  if (g.b_fp8 && !g.b_packed) return hipErrorInvalidValue;  // fp8 codes come in the packed layout only
   if (g.Kdim % B8_AKS || g.Kdim < 2 * B8_AKS) return hipErrorInvalidValue;
   if ((uint64_t)g.n_a_rows * (uint64_t)g.Kdim / 8u > 0xffffffffull) return hipErrorInvalidValue;
   if (g.N % 8 || g.ldo % 8) return hipErrorInvalidValue;
@@ -358,7 +529,10 @@ hipError_t launch_grouped_gemm_big8(int epi, const GemmArgs& g, hipStream_t s) {
   int64_t blocks = ((int64_t)g.max_tiles * n_nb + 7) / 8 * 8;
   const int64_t cap = (int64_t)g_cus8 / 8 * 8;
   blocks = blocks < cap ? blocks : cap;
-  if (g.b_packed) {
+  if (g.b_fp8) {
+    if (epi == EPI_SWIGLU) gemm_bf16_big8<EPI_SWIGLU, true, true><<<(unsigned)blocks, 512, 0, s>>>(g);
+    else gemm_bf16_big8<EPI_F32, true, true><<<(unsigned)blocks, 512, 0, s>>>(g);
+  } else if (g.b_packed) {
     if (epi == EPI_SWIGLU) gemm_bf16_big8<EPI_SWIGLU, true><<<(unsigned)blocks, 512, 0, s>>>(g);
     else gemm_bf16_big8<EPI_F32, true><<<(unsigned)blocks, 512, 0, s>>>(g);
   } else {

@@ -143,9 +143,8 @@ int64_t gemm_max_tiles(int64_t n_rows, int n_groups, int block_rows);
 hipError_t launch_build_tiles(const int32_t* offsets, int n_groups, int64_t n_rows, int block_rows,
                               Tile* tiles, int32_t* n_tiles, int32_t max_tiles, int skip_group, hipStream_t s);
 hipError_t launch_grouped_gemm(int dtype, bool fast, int epi, int block_rows, const GemmArgs& g, hipStream_t s);
-// 256 x 256 block tiles (block_rows == 256): grouped_gemm_big.hip (four waves,
-// bf16 or fp8 weights), grouped_gemm_big8.hip (eight waves, bf16 weights).
-hipError_t launch_grouped_gemm_big(int epi, const GemmArgs& g, hipStream_t s);
+// 256 x 256 block tiles (block_rows == 256): grouped_gemm_big8.hip (eight
+// waves, bf16 or fp8 weights).
 hipError_t launch_grouped_gemm_big8(int epi, const GemmArgs& g, hipStream_t s);
 
 // route.hip
