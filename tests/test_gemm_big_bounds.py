@@ -87,6 +87,9 @@ SHAPES = {
     "skewed": (4096, 64, 8, 512, 256, 256, 4, 1),
     # the decode/prefill widths with fewer tokens
     "wide": (512, 16, 8, 4096, 1280, 1280, 5, 0),
+    # 141 mean rows per group: the form that skips the empty half of an item
+    "sparse_items": (800, 16, 2, 256, 256, 256, 6, 0),
+    "fp8_sparse_items": (800, 16, 2, 256, 256, 256, 6, 0, 1),
     # fp8 weights (64-element weight stages, per-column scales): short and odd contractions, several items
     "fp8_multi_item_short_k": (32768, 8, 2, 128, 192, 192, 2, 0, 1),
     "fp8_odd_stages_skewed": (4096, 64, 8, 512, 320, 320, 4, 1, 1),

@@ -89,7 +89,7 @@ def run_fp8(spec, L, rows=None, k=None):
 
 
 FP8_SMALL = ["bf16_tiles32", "bf16_tiles32_fused", "bf16_tiles64", "bf16_tiles128", "bf16_tiles256",
-             "bf16_k_equals_e", "bf16_router_rows_padded"]
+             "bf16_tiles256_sparse", "bf16_k_equals_e", "bf16_router_rows_padded"]
 
 
 @pytest.mark.parametrize("name", FP8_SMALL)
@@ -115,7 +115,7 @@ def test_fp8_shared_expert_of_another_width():
     run_fp8(spec, L)
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "skew"])
 def test_fp8_full_size(name):
     spec = synth.spec(name)
     print(f"fp8 weights, full size: {name}", flush=True)

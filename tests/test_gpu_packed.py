@@ -91,7 +91,7 @@ def test_packed_entry_points_equal_rows():
     assert E == offs.shape[0] - 1
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "skew"])
 def test_packed_full_size_equals_rows(name):
     spec = synth.spec(name)
     print(f"packed vs row-major, full size: {name}", flush=True)

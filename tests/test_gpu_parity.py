@@ -34,6 +34,9 @@ SMALL = {
     "bf16_tiles32_fused": synth.spec("tiny", T=37, D=256, E=64, K=6, F=192, Fs=192, dtype="bf16", seed=9),
     "bf16_tiles64": synth.spec("tiny", T=150, D=256, E=16, K=4, F=192, Fs=192, dtype="bf16", seed=10),
     "bf16_tiles256": synth.spec("tiny", T=600, D=512, E=8, K=2, F=320, Fs=320, dtype="bf16", seed=8),
+    # 256-row tiles at 141 mean rows per group: most experts fill at most half a tile, so the
+    # 256x256 kernel takes its form that skips the empty half of an item
+    "bf16_tiles256_sparse": synth.spec("tiny", T=800, D=256, E=16, K=2, F=256, Fs=256, dtype="bf16", seed=9),
     "bf16_generic_widths": synth.spec("tiny", T=50, D=200, E=12, K=3, F=72, Fs=72, dtype="bf16", seed=3),
     "bf16_no_shared": synth.spec("tiny", T=129, D=384, E=24, K=8, F=128, Fs=0, dtype="bf16", seed=4),
     "bf16_k_equals_e": synth.spec("tiny", T=33, D=256, E=8, K=8, F=64, Fs=64, dtype="bf16", seed=5),
