@@ -224,7 +224,7 @@ def tile_kernel(T, spec):
     rows, groups = T * spec.K + (T if spec.Fs == spec.F else 0), spec.E + (1 if spec.Fs == spec.F else 0)
     if rows <= 24 * groups:  # thresholds as gemm_block_rows
         return 32
-    return 256 if rows >= 96 * groups else (64 if rows <= 48 * groups else 128)
+    return 256 if rows >= 48 * groups else (64 if rows <= 48 * groups else 128)
 
 
 def sweep(steps, warmup, flush_on):

@@ -36,7 +36,7 @@
 #define MOE_ROWS_64 48  // ... up to which 64-row tiles (then 128-row tiles)
 #endif
 #ifndef MOE_ROWS_256
-#define MOE_ROWS_256 96  // mean rows per group from which they use the 256 x 256 kernel
+#define MOE_ROWS_256 48  // mean rows per group from which they use the 256 x 256 kernel (its skipping form below 160)
 #endif
 #ifndef MOE_NS_LARGE
 #define MOE_NS_LARGE 4  // pipeline depth of the 128-row tiles
