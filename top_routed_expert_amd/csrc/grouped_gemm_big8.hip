@@ -370,7 +370,9 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
               v.z += p.bias[col + 2];
               v.w += p.bias[col + 3];
             }
-            *(float4*)&((float*)p.out)[r * p.ldo + col] = v;
+            // read once, by the combine: non-temporal, so it does not displace operands in L2
+            typedef float f32x4_st __attribute__((ext_vector_type(4)));
+            __builtin_nontemporal_store(f32x4_st{v.x, v.y, v.z, v.w}, (f32x4_st*)&((float*)p.out)[r * p.ldo + col]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
