@@ -254,6 +254,38 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
     });
   };
 
+  // Even steps: right after row tile m's multiplies, a[m] is refilled with
+  // row tile m's chunk of the following odd step (the second half of the
+  // same activation stage, visible since this step's barrier), so odd steps
+  // multiply at once. Chunk m of this step has landed once at most 11
+  // younger reads are pending: the later chunks, the 4 weight reads and the
+  // m refills issued so far add up to 11 for every m.
+  // (The refill is an inline-asm read like the others: a plain LDS load would
+  // make the compiler drain the direct loads in flight, which it cannot prove
+  // do not alias it.)
+  auto multiply_refill = [&](u32x4_8(&a)[8], const u32x4_8(&b)[4], int slot) {
+    const uint32_t next = ldsA_base + (uint32_t)slot * SLOT_A + aoffA1;
+    static_for<0, 8>([&a, &b, next, this_acc = &acc](auto M) {
+      constexpr int m = decltype(M)::value;
+      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a[m]) : "n"(11));
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        (*this_acc)[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_8(a[m]), as_bf16x8_8(b[n]), (*this_acc)[m][n], 0, 0, 0);
+      asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(a[m]) : "v"(next), "n"(m * 2048));
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // odd steps: the activation operand is in registers (refilled in the even step)
+  auto multiply_ready = [&](const u32x4_8(&a)[8], const u32x4_8(&b)[4]) {
+    static_for<0, 8>([&](auto M) {
+      constexpr int m = decltype(M)::value;
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_8(a[m]), as_bf16x8_8(b[n]), acc[m][n], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
   // fp8: this wave's 4 weight fragments of a stage, 16 bytes per lane (both
   // MFMA steps' codes); raw[n] lands at lgkmcnt(11 - n) when the 8 A reads
   // follow them.
@@ -437,9 +469,14 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
       const int ks = k + B8_NS - 1;
       if (ks == nk && has_next) set_b_sources(t_next, nb_next);
       issue_b((baseB + ks) % B8_NS, ks < nk ? ks : (has_next ? ks - nk : lastB));
-      if (!SKIP || busy) read_a((baseA + h) & 1, odd ? 1 : 0, a);
-      read_b((baseB + k + 1) % B8_NS, b_next);
-      if (!SKIP || busy) multiply(a, b_cur);
+      if constexpr (!odd) {
+        if (!SKIP || busy) read_a((baseA + h) & 1, 0, a);
+        read_b((baseB + k + 1) % B8_NS, b_next);
+        if (!SKIP || busy) multiply_refill(a, b_cur, (baseA + h) & 1);
+      } else {
+        read_b((baseB + k + 1) % B8_NS, b_next);
+        if (!SKIP || busy) multiply_ready(a, b_cur);
+      }
     };
     for (;;) {
   #pragma unroll
