@@ -126,7 +126,7 @@ def test_dynamic_route_gap():
     assert np.allclose(g[keep], ref["gap"][keep], atol=2e-7)
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "skew"])
 def test_dynamic_topk_full_size(name):
     """The pages' split (4 experts for simple inputs, 8 for complex ones) at the full workload sizes."""
     spec = synth.spec(name)

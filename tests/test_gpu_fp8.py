@@ -115,7 +115,7 @@ def test_fp8_shared_expert_of_another_width():
     run_fp8(spec, L)
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill", "skew"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "skew", "full"])
 def test_fp8_full_size(name):
     spec = synth.spec(name)
     print(f"fp8 weights, full size: {name}", flush=True)
