@@ -241,19 +241,6 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
       asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(a[m]) : "v"(addr), "n"(m * 2048));
     });
   };
-  // A chunk m lands at lgkmcnt(11 - m): the 8 A reads are followed by the 4
-  // weight reads of the next step
-  auto multiply = [&](u32x4_8(&a)[8], const u32x4_8(&b)[4]) {
-    static_for<0, 8>([&](auto M) {
-      constexpr int m = decltype(M)::value;
-      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a[m]) : "n"(11 - m));
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_8(a[m]), as_bf16x8_8(b[n]), acc[m][n], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
-
   // Even steps: right after row tile m's multiplies, a[m] is refilled with
   // row tile m's chunk of the following odd step (the second half of the
   // same activation stage, visible since this step's barrier), so odd steps
