@@ -16,8 +16,9 @@ Everything is float64 (inputs are converted exactly: bf16 and fp32 values and
 their pairwise products are exact in float64). Library primitives used as
 single steps: numpy matmul, exp, argsort (stable), bincount, cumsum.
 
-Readings where the pages leave a step open (each also listed with the design
-notes):
+Readings where the pages leave a step open (R8 to R11 are readings about the
+workload shapes, the initialisation and training-time terms, not about the
+steps below):
   R1 softmax runs over all E routed experts before selection (3.2.2 computes
      the probabilities, then selects the 8 most probable);
   R2 the selected probabilities weight the routed outputs as they are, with
@@ -31,7 +32,7 @@ notes):
   R6 no capacity limit: every (token, choice) pair is processed (dropless);
   R7 an optional per-expert router bias is added to the logits before the
      softmax;
-  R12 (numbered as in the design notes) dynamic top-k (page "Step3.5 Flash
+  R12 dynamic top-k (page "Step3.5 Flash
      大模型技术深度解析", section 8.2: 4 experts for simple inputs, 8 for
      complex ones; page "Step 3.5 Flash动态稀疏MoE架构解析与优化实践", section
      2.1: fewer experts for short texts, up to 8 for long ones): token t keeps
