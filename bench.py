@@ -451,7 +451,7 @@ def cpu_baseline(spec, L, n_tokens: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     import torch
