@@ -280,18 +280,13 @@ def layer_rows(x, W: LayerWeights, k: int, rows, k_per_token=None) -> dict:
 
 # -------------------------------------------------------------- helpers ---
 
-def round_out(out64: np.ndarray, dtype: str) -> np.ndarray:
-    """Round the float64 output once to the layer's output type (float32 values)."""
-    if dtype == "f32":
-        return out64.astype(np.float32)
-    if _torch is None:  # pragma: no cover
-        raise RuntimeError("bf16 rounding needs torch")
-    t = _torch.from_numpy(out64.astype(np.float32, copy=False))
-    return t.to(_torch.bfloat16).to(_torch.float32).numpy()
-
-
 def expert_load(counts: np.ndarray) -> dict:
-    """Expert Activation Skew = max / mean activation count over experts."""
+    """Expert Activation Skew (the untitled page at tqpw.cn, section 4.4, table
+    of serving metrics): the largest activation count of an expert divided by the mean
+    activation count, the mean taken over all E routed experts (experts that
+    no token chose count as 0). counts[e] is the number of (token, choice)
+    pairs routed to expert e. Also returns the max, the mean and the number
+    of experts with at least one pair. Skew is 0 when no pair was routed."""
     c = np.asarray(counts, dtype=np.float64)
     mean = c.mean() if c.size else 0.0
     return dict(max=float(c.max()) if c.size else 0.0, mean=float(mean),
@@ -300,8 +295,14 @@ def expert_load(counts: np.ndarray) -> dict:
 
 
 def group_counts(counts: np.ndarray, groups: int) -> np.ndarray:
-    """Activation counts of `groups` contiguous equal expert groups (e // (E/groups))."""
+    """Activation counts of the G expert groups of page "Step3.5 Flash
+    大模型技术深度解析", section 3.2.3 (the routed experts split evenly into G
+    groups, one per GPU; R13: group g holds the contiguous ids g*E/G ..
+    (g+1)*E/G - 1): entry g is the sum of counts[e] over the experts of
+    group g. E must be a multiple of G."""
     c = np.asarray(counts)
+    if groups <= 0 or c.size % groups:
+        raise ValueError(f"{c.size} experts do not split into {groups} equal groups")
     return c.reshape(groups, -1).sum(axis=1)
 
 

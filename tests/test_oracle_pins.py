@@ -470,6 +470,60 @@ def pin_fp8_quantisation():
     assert np.all(np.abs(wd - w) <= step + 1e-30)
 
 
+def pin_expert_load():
+    """Expert Activation Skew = max count / mean count over all experts: hand-worked values,
+    closed forms, invariances, and the counts of a routing whose choices are forced."""
+    r = O.expert_load(np.array([0, 0, 4, 2]))
+    # worked by hand: max 4, mean (0+0+4+2)/4 = 1.5, skew 4/1.5 = 8/3, two experts touched
+    assert r["max"] == 4.0 and r["mean"] == 1.5 and r["touched"] == 2
+    assert math.isclose(r["skew"], 8.0 / 3.0, rel_tol=1e-15)
+    # closed forms: uniform counts give 1; every pair on one of E experts gives E
+    assert O.expert_load(np.full(288, 57))["skew"] == 1.0
+    one = np.zeros(288, dtype=np.int64)
+    one[17] = 8192 * 8
+    assert math.isclose(O.expert_load(one)["skew"], 288.0, rel_tol=1e-15)
+    assert O.expert_load(one)["touched"] == 1
+    assert O.expert_load(np.zeros(5, dtype=np.int64))["skew"] == 0.0
+    # invariances: relabelling experts and scaling all counts leave the skew unchanged
+    rng = np.random.default_rng(41)
+    c = rng.integers(0, 50, 36)
+    c[3] = 0
+    s0 = O.expert_load(c)["skew"]
+    assert math.isclose(O.expert_load(rng.permutation(c))["skew"], s0, rel_tol=1e-14)
+    assert math.isclose(O.expert_load(7 * c)["skew"], s0, rel_tol=1e-14)
+    # brute force: pure-Python max and mean over all experts
+    assert math.isclose(s0, max(c.tolist()) / (math.fsum(c.tolist()) / len(c)), rel_tol=1e-14)
+    # a routing with forced choices: all logits equal, so every token takes experts 0..K-1
+    # (ties to the lower index): K experts hold T pairs each, the other E-K none, skew = E/K
+    T, E, K = 10, 12, 3
+    rt = O.route(np.ones((T, 2)), np.zeros((E, 2)), K)
+    ld = O.expert_load(O.permute(rt["idx"], E)["counts"])
+    assert ld["max"] == T and ld["touched"] == K and math.isclose(ld["skew"], E / K, rel_tol=1e-15)
+
+
+def pin_group_counts():
+    """Per-group counts of G contiguous equal expert groups: hand-worked, brute force, the page's 8 x 36."""
+    assert O.group_counts(np.arange(12), 3).tolist() == [0 + 1 + 2 + 3, 4 + 5 + 6 + 7, 8 + 9 + 10 + 11]
+    assert O.group_counts(np.arange(12), 1).tolist() == [66]
+    assert O.group_counts(np.arange(12), 12).tolist() == list(range(12))
+    g = json.load(open(os.path.join(GOLDEN, "step35_layer_constants.json")))["values"]
+    G, per = g["ep_groups"]["value"], g["experts_per_group"]["value"]
+    E = G * per
+    rng = np.random.default_rng(43)
+    c = rng.integers(0, 400, E)
+    got = O.group_counts(c, G)
+    want = [0] * G
+    for e in range(E):          # brute force: walk the experts, group e // (E / G)
+        want[e // per] += int(c[e])
+    assert got.tolist() == want and int(got.sum()) == int(c.sum())
+    # one hot expert lands in its own group only
+    hot = np.zeros(E, dtype=np.int64)
+    hot[per + 5] = 9
+    assert O.group_counts(hot, G).tolist() == [0, 9] + [0] * (G - 2)
+    with pytest.raises(ValueError):
+        O.group_counts(np.arange(10), 3)
+
+
 def pin_page_constants():
     """The page's structural numbers, and the width reading they force."""
     g = json.load(open(os.path.join(GOLDEN, "step35_layer_constants.json")))["values"]
@@ -496,7 +550,7 @@ PINS = [pin_route_bruteforce, pin_route_ties, pin_route_properties, pin_route_bi
         pin_ffn_closed_form, pin_ffn_bruteforce, pin_layer_worked_example,
         pin_layer_special_cases, pin_dynamic_topk_route, pin_dynamic_topk_permute, pin_dynamic_topk_layer,
         pin_ep_receive_plan, pin_group_stats, pin_ep_share_composition, pin_fp8_codec, pin_fp8_quantisation,
-        pin_page_constants]
+        pin_expert_load, pin_group_counts, pin_page_constants]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -648,6 +702,19 @@ def _scale_by_max(w):
     return O.e4m3_encode((w32 / s2[..., None]).astype(np.float32)), s2
 
 
+def _skew_mean_over_touched(counts):
+    c = np.asarray(counts, dtype=np.float64)
+    t = c[c > 0]
+    mean = t.mean() if t.size else 0.0
+    return dict(max=float(c.max()) if c.size else 0.0, mean=float(mean),
+                skew=float(c.max() / mean) if mean > 0 else 0.0, touched=int(t.size))
+
+
+def _strided_groups(counts, groups):
+    c = np.asarray(counts)
+    return np.array([int(c[g::groups].sum()) for g in range(groups)])
+
+
 _orig = {n: getattr(O, n) for n in ("quantize_rows_fp8", "ep_receive_plan", "group_stats", "select_topk", "swiglu_ffn", "permute", "combine",
                                     "router_logits", "softmax", "silu", "route")}
 
@@ -671,6 +738,8 @@ MUTANTS = {
     "group_mass_of_chosen_experts_only": ("group_stats", _stats_from_chosen_only),
     "fp8_encode_truncates": ("e4m3_encode", _encode_truncating),
     "fp8_scale_without_448": ("quantize_rows_fp8", _scale_by_max),
+    "skew_mean_over_touched_experts": ("expert_load", _skew_mean_over_touched),
+    "expert_groups_strided": ("group_counts", _strided_groups),
 }
 
 
