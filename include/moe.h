@@ -22,7 +22,9 @@
  * ---------------------------------------
  *  - Every tensor pointer is DEVICE memory owned by the caller, dense
  *    row-major (weights: or packed, below), 16-byte aligned. The library never allocates, frees or keeps
- *    a pointer past the call; it holds no mutable global state.
+ *    a pointer past the call. The one piece of device memory it owns is the
+ *    static scratch of moe_layer_forward_noalloc (below); every other entry
+ *    point works only in the caller's buffers and workspace.
  *  - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
  *    null stream) and returns; results are valid once the stream is
  *    synchronised. No call copies device data to the host or synchronises.
@@ -292,6 +294,28 @@ moe_status moe_layer_forward_dynamic(const moe_config* cfg, int64_t T, const voi
                                      int32_t* topk_idx_out, float* topk_prob_out,
                                      int32_t* offsets_out, void* ws, size_t ws_bytes,
                                      void* stream);
+
+/* The whole layer without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments and results as
+ * moe_layer_forward without ws/ws_bytes: the workspace is a static device
+ * array of moe_noalloc_scratch_bytes() bytes (64 MiB) inside the library,
+ * one copy per GPU, held from the first call on that GPU until the process
+ * ends. Nothing is allocated or freed by the call.
+ *   - Layers whose moe_layer_workspace_bytes(cfg, T) exceeds that size are
+ *     rejected with MOE_ERR_WORKSPACE before anything is enqueued (at
+ *     d_model 4096 and expert width 1280: up to about 370 tokens).
+ *   - The scratch of the current device is used (hipGetDevice); `stream`
+ *     must belong to that device.
+ *   - Every call on a GPU shares that GPU's scratch and leaves its contents
+ *     behind (nothing in it needs to start at zero). Calls that overlap on
+ *     one GPU (concurrent streams or threads) race on the scratch: the
+ *     caller must order them, e.g. by issuing them on one stream.
+ *   - MOE_ERR_HIP if the scratch's device address cannot be obtained. */
+size_t moe_noalloc_scratch_bytes(void);
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, int64_t T, const void* x,
+                                     const moe_weights* w, void* out, int32_t* topk_idx_out,
+                                     float* topk_prob_out, int32_t* offsets_out, void* stream);
 
 /* Expert-parallel balance statistics (page "Step3.5 Flash 大模型技术深度解析",
  * section 3.2.3: the 288 routed experts split into G equal groups, one group

@@ -38,7 +38,7 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails its checks
 def test_exports_every_declared_function():
     L = moe.lib()
     names = header_functions()
-    assert len(names) == 24, names
+    assert len(names) == 26, names
     for n in names:
         assert hasattr(L, n), f"libmoe.so does not export {n}"
     assert set(names) == set(M._SIGS), "binding signatures out of sync with the header"
@@ -209,6 +209,29 @@ def test_combine_and_layer_checks():
     c0 = cfg(d_shared=0)
     ws0 = L.moe_layer_workspace_bytes(ctypes.byref(c0), 8)
     assert call(cc=c0, ww=no_shared, wsb=ws0 - 1) == WS   # no shared expert: its weights may be NULL
+
+
+def test_noalloc_layer_checks():
+    """moe_layer_forward_noalloc: every check fails before the device is touched; a layer whose
+    workspace exceeds the static scratch is refused."""
+    L = moe.lib()
+    c = cfg()
+    assert L.moe_noalloc_scratch_bytes() == 64 << 20
+    w = M.MoeWeights(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    call = lambda T=8, cc=c, ww=w, x=FAKE, out=FAKE: L.moe_layer_forward_noalloc(
+        ctypes.byref(cc), T, x, ctypes.byref(ww), out, None, None, None, None)
+    assert call(T=0) == OK
+    assert L.moe_layer_forward_noalloc(None, 8, FAKE, ctypes.byref(w), FAKE, None, None, None, None) == NULL
+    assert call(T=-1) == SHAPE
+    assert call(x=None) == NULL and call(out=None) == NULL
+    assert call(ww=M.MoeWeights(FAKE, None, FAKE, FAKE, FAKE, None, None, None)) == NULL
+    assert call(x=FAKE + 8) == MISALIGNED
+    big = cfg(d_model=4096, n_experts=288, top_k=8, d_expert=1280, d_shared=1280)
+    T = 1024
+    assert L.moe_layer_workspace_bytes(ctypes.byref(big), T) > L.moe_noalloc_scratch_bytes()
+    assert call(T=T, cc=big) == WS and "static scratch" in _last()
+    if not torch.cuda.is_available():   # valid arguments: the device query is the first HIP call
+        assert call() == HIP and "static scratch" in _last()
 
 
 def test_binding_rejects_host_tensors():

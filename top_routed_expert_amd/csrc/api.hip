@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 using namespace moe;
@@ -335,6 +337,33 @@ moe_status check_grouped(const moe_config* cfg, int32_t n_groups, int64_t n_rows
   return MOE_OK;
 }
 
+// Pointer and shape checks of the whole-layer entry points (cfg and T checked before).
+moe_status check_layer_args(const moe_config* cfg, const void* x, const moe_weights* w, const int32_t* k_per_token,
+                            const void* out, const int32_t* topk_idx_out, const float* topk_prob_out,
+                            const int32_t* offsets_out) {
+  if (!x || !w || !out) return fail(MOE_ERR_NULL, "x, w and out are required");
+  if (!w->w_router || !w->w_gate || !w->w_up || !w->w_down)
+    return fail(MOE_ERR_NULL, "router and routed expert weights are required");
+  const bool shared = cfg->d_shared > 0;
+  if (shared && (!w->s_gate || !w->s_up || !w->s_down))
+    return fail(MOE_ERR_NULL, "d_shared > 0 needs s_gate, s_up and s_down");
+  if (fp8(cfg) && (!w->w_gate_scale || !w->w_up_scale || !w->w_down_scale ||
+                   (shared && (!w->s_gate_scale || !w->s_up_scale || !w->s_down_scale))))
+    return fail(MOE_ERR_NULL, "fp8 weights need the scales of every expert matrix");
+  if (fp8(cfg) && (misaligned(w->w_gate_scale) || misaligned(w->w_up_scale) || misaligned(w->w_down_scale) ||
+                   misaligned(w->s_gate_scale) || misaligned(w->s_up_scale) || misaligned(w->s_down_scale)))
+    return fail(MOE_ERR_MISALIGNED, "moe_layer_forward: a scale pointer is not 16-byte aligned");
+  if (misaligned(x) || misaligned(out) || misaligned(w->w_router) || misaligned(w->router_bias) ||
+      misaligned(w->w_gate) || misaligned(w->w_up) || misaligned(w->w_down) ||
+      (shared && (misaligned(w->s_gate) || misaligned(w->s_up) || misaligned(w->s_down))) ||
+      misaligned(topk_idx_out) || misaligned(topk_prob_out) || misaligned(offsets_out) ||
+      misaligned(k_per_token))
+    return fail(MOE_ERR_MISALIGNED, "moe_layer_forward: a pointer is not 16-byte aligned");
+  if (cfg->dtype == MOE_BF16 && (cfg->d_model % 8 || cfg->d_expert % 8 || (shared && cfg->d_shared % 8)))
+    return fail(MOE_ERR_UNSUPPORTED, "bf16 rows need d_model, d_expert, d_shared multiples of 8");
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -551,26 +580,9 @@ moe_status moe_layer_forward_dynamic(const moe_config* cfg, int64_t T, const voi
   MOE_TRY(check_cfg(cfg));
   MOE_TRY(check_tokens(cfg, T));
   if (T == 0) return ok();
-  if (!x || !w || !out || !ws) return fail(MOE_ERR_NULL, "x, w, out and ws are required");
-  if (!w->w_router || !w->w_gate || !w->w_up || !w->w_down)
-    return fail(MOE_ERR_NULL, "router and routed expert weights are required");
-  const bool shared = cfg->d_shared > 0;
-  if (shared && (!w->s_gate || !w->s_up || !w->s_down))
-    return fail(MOE_ERR_NULL, "d_shared > 0 needs s_gate, s_up and s_down");
-  if (fp8(cfg) && (!w->w_gate_scale || !w->w_up_scale || !w->w_down_scale ||
-                   (shared && (!w->s_gate_scale || !w->s_up_scale || !w->s_down_scale))))
-    return fail(MOE_ERR_NULL, "fp8 weights need the scales of every expert matrix");
-  if (fp8(cfg) && (misaligned(w->w_gate_scale) || misaligned(w->w_up_scale) || misaligned(w->w_down_scale) ||
-                   misaligned(w->s_gate_scale) || misaligned(w->s_up_scale) || misaligned(w->s_down_scale)))
-    return fail(MOE_ERR_MISALIGNED, "moe_layer_forward: a scale pointer is not 16-byte aligned");
-  if (misaligned(x) || misaligned(out) || misaligned(w->w_router) || misaligned(w->router_bias) ||
-      misaligned(w->w_gate) || misaligned(w->w_up) || misaligned(w->w_down) ||
-      (shared && (misaligned(w->s_gate) || misaligned(w->s_up) || misaligned(w->s_down))) ||
-      misaligned(topk_idx_out) || misaligned(topk_prob_out) || misaligned(offsets_out) || misaligned(ws) ||
-      misaligned(k_per_token))
-    return fail(MOE_ERR_MISALIGNED, "moe_layer_forward: a pointer is not 16-byte aligned");
-  if (cfg->dtype == MOE_BF16 && (cfg->d_model % 8 || cfg->d_expert % 8 || (shared && cfg->d_shared % 8)))
-    return fail(MOE_ERR_UNSUPPORTED, "bf16 rows need d_model, d_expert, d_shared multiples of 8");
+  if (!ws) return fail(MOE_ERR_NULL, "ws is required");
+  if (misaligned(ws)) return fail(MOE_ERR_MISALIGNED, "moe_layer_forward: ws is not 16-byte aligned");
+  MOE_TRY(check_layer_args(cfg, x, w, k_per_token, out, topk_idx_out, topk_prob_out, offsets_out));
   const size_t need = moe_layer_workspace_bytes(cfg, T);
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "moe_layer_forward needs %zu workspace bytes, got %zu", need, ws_bytes);
@@ -610,7 +622,7 @@ moe_status moe_layer_forward_dynamic(const moe_config* cfg, int64_t T, const voi
   MOE_TRY(run_ffn(cfg, n_groups, E, P + extra, L.offsets_ext, x, T, L.sorted_token, P, w->w_gate, w->w_up,
                   w->w_down, w->s_gate, w->s_up, w->s_down, cfg->d_expert, L.y, L.ffn, s, small,
                   L.fused_shared ? E : -1, sc));
-  if (shared && !L.fused_shared) {
+  if (cfg->d_shared > 0 && !L.fused_shared) {
     const float* sc_shared[6] = {w->s_gate_scale, w->s_up_scale, w->s_down_scale, nullptr, nullptr, nullptr};
     MOE_TRY(run_ffn(cfg, 1, 1, T, nullptr, x, T, nullptr, 0, w->s_gate, w->s_up, w->s_down, nullptr, nullptr,
                     nullptr, cfg->d_shared, L.y_shared, L.ffn_shared, s, false, -1, sc_shared));
@@ -722,6 +734,73 @@ moe_status moe_layer_forward(const moe_config* cfg, int64_t T, const void* x, co
 moe_status moe_route(const moe_config* cfg, int64_t T, const void* x, const void* w_router, const float* bias,
                      int32_t* topk_idx, float* topk_prob, float* gap, void* ws, size_t ws_bytes, void* stream) {
   return moe_route_dynamic(cfg, T, x, w_router, bias, nullptr, topk_idx, topk_prob, gap, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- the layer without a caller workspace ----
+//
+// moe_layer_forward_noalloc runs moe_layer_forward with its workspace in the
+// static device array below (one copy per GPU, held until the process ends).
+// In host code `scratch` names a host-side stand-in, not device memory: the
+// array's device address on each GPU comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is passed
+// to kernels.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the current device (nullptr on failure, with the HIP error in *err).
+void* scratch_on_current_device(hipError_t* err, int* dev_out) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  *dev_out = dev;
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w, void* out,
+                                     int32_t* topk_idx_out, float* topk_prob_out, int32_t* offsets_out,
+                                     void* stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_tokens(cfg, T));
+  if (T == 0) return ok();
+  MOE_TRY(check_layer_args(cfg, x, w, nullptr, out, topk_idx_out, topk_prob_out, offsets_out));
+  const size_t need = moe_layer_workspace_bytes(cfg, T);
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_layer_forward_noalloc: this layer needs %zu workspace bytes for %lld tokens; the static "
+                "scratch holds %zu (use moe_layer_forward with a caller workspace)",
+                need, (long long)T, kScratchBytes);
+  hipError_t e = hipSuccess;
+  int dev = 0;
+  void* ws = scratch_on_current_device(&e, &dev);
+  if (!ws) return fail(MOE_ERR_HIP, "moe_layer_forward_noalloc: address of the static scratch on device %d: %s", dev,
+                       hipGetErrorString(e));
+  return moe_layer_forward_dynamic(cfg, T, x, w, nullptr, out, topk_idx_out, topk_prob_out, offsets_out, ws,
+                                   kScratchBytes, stream);
 }
 
 }  // extern "C"

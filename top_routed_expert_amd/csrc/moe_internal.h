@@ -9,6 +9,9 @@
 
 #include "moe.h"
 
+// Size of the static device scratch of moe_layer_forward_noalloc (64 MiB).
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
 namespace moe {
 
 typedef uint16_t bf16_t;  // storage type of bfloat16 values

@@ -73,6 +73,8 @@ _SIGS = {
     "moe_fp8_weights_bytes": ([_I64, _I64, _I64], _SZ),
     "moe_quantize_fp8": ([_I64, _I64, _I64, _P, _P, _SZ, _P, _P], ctypes.c_int),
     "moe_pack_weights": ([_I64, _I64, _I64, _P, _P, _SZ, _P], ctypes.c_int),
+    "moe_noalloc_scratch_bytes": ([], _SZ),
+    "moe_layer_forward_noalloc": ([_CFG, _I64, _P, ctypes.POINTER(MoeWeights), _P, _P, _P, _P, _P], ctypes.c_int),
 }
 
 
@@ -402,6 +404,30 @@ def layer_forward(cfg: Config, x: torch.Tensor, w: dict, out: torch.Tensor | Non
             _ptr(out, "out", cfg.odtype, (T, cfg.d_model), dev), _ptr(idx, "idx"), _ptr(prob, "prob"),
             _ptr(offs, "offsets"), ws.data_ptr(), ws.numel(), _stream(dev)), "moe_layer_forward_dynamic")
     return (out, idx, prob, offs) if routing else out
+
+
+def noalloc_scratch_bytes() -> int:
+    """moe_noalloc_scratch_bytes: size of the library's static device scratch."""
+    return lib().moe_noalloc_scratch_bytes()
+
+
+def layer_forward_noalloc(cfg: Config, x: torch.Tensor, out: torch.Tensor, weights: MoeWeights,
+                          topk_idx: torch.Tensor | None = None, topk_prob: torch.Tensor | None = None,
+                          offsets: torch.Tensor | None = None) -> torch.Tensor:
+    """moe_layer_forward_noalloc: the layer with the library's static scratch as its workspace.
+
+    The caller passes every output (out [T, D]; optionally topk_idx [T,K], topk_prob [T,K],
+    offsets [E+1]) and a prepared weights_struct, so nothing is allocated on this path."""
+    T = x.shape[0]
+    dev = x.device
+    c = cfg.c()
+    _check(lib().moe_layer_forward_noalloc(
+        ctypes.byref(c), T, _ptr(x, "x", cfg.dtype, (T, cfg.d_model), dev), ctypes.byref(weights),
+        _ptr(out, "out", cfg.odtype, (T, cfg.d_model), dev),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, cfg.top_k), dev),
+        _ptr(topk_prob, "topk_prob", torch.float32, (T, cfg.top_k), dev),
+        _ptr(offsets, "offsets", torch.int32, (cfg.n_experts + 1,), dev), _stream(dev)), "moe_layer_forward_noalloc")
+    return out
 
 
 def packed_weights_bytes(n_mats: int, rows: int, cols: int) -> int:
