@@ -14,57 +14,9 @@
 #include <thread>
 #include <vector>
 #include "emul_internal.h"
-thread_local emul_dim3 threadIdx, blockIdx;
-emul_dim3 gridDim, blockDim;
-long long emul_loads = 0;
-
-// one region per LDS array of each kernel instantiation
-static void* g_regions[64];
-static size_t g_sizes[64];
-static int g_nreg = 0;
-static std::mutex g_reg_mu;
-uint32_t emul_lds_base(void* p, size_t bytes) {
-  std::lock_guard<std::mutex> lk(g_reg_mu);
-  for (int i = 0; i < g_nreg; ++i)
-    if (g_regions[i] == p) return (uint32_t)i << 20;
-  if (g_nreg == 64) { fprintf(stderr, "too many LDS regions\n"); abort(); }
-  g_regions[g_nreg] = p;
-  g_sizes[g_nreg] = bytes;
-  return (uint32_t)(g_nreg++) << 20;
-}
-void* emul_lds_region_ptr(uint32_t vaddr, int bytes) {
-  int n;
-  {
-    std::lock_guard<std::mutex> lk(g_reg_mu);
-    n = g_nreg;
-  }
-  const int r = (int)(vaddr >> 20);
-  const uint32_t off = vaddr & 0xfffff;
-  if (r >= n || off + bytes > g_sizes[r]) {
-    fprintf(stderr, "LDS read out of range: region %d offset %u (+%d); block %u thread %u\n", r, off, bytes,
-            blockIdx.x, threadIdx.x);
-    abort();
-  }
-  return (char*)g_regions[r] + off;
-}
-void emul_global_load_lds(const void* src, void* dst, int bytes) {
-  const int lane = threadIdx.x & 63;
-  memcpy((char*)dst + lane * bytes, src, bytes);
-  __atomic_fetch_add(&emul_loads, 1, __ATOMIC_RELAXED);
-}
+#include "runner.h"
 template <class K, class A> void emul_launch(K kernel, unsigned blocks, unsigned threads, const A& args) {
-  gridDim.x = blocks;
-  std::vector<std::thread> th;
-  for (int w = 0; w < 8; ++w)
-    th.emplace_back([&, w] {
-      for (unsigned b = w; b < blocks; b += 8)
-        for (unsigned t = 0; t < threads; ++t) {
-          blockIdx.x = b;
-          threadIdx.x = t;
-          kernel(args);
-        }
-    });
-  for (auto& t : th) t.join();
+  emul_run(false, kernel, dim3(blocks), threads, args);
 }
 #include "emul_big.cpp"
 

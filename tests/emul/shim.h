@@ -19,23 +19,90 @@
 #define __restrict__
 struct uint4 { uint32_t x, y, z, w; };
 struct float4 { float x, y, z, w; };
+struct int4 { int x, y, z, w; };
+struct uint2 { uint32_t x, y; };
+inline uint2 make_uint2(uint32_t x, uint32_t y) { return uint2{x, y}; }
+inline float4 make_float4(float x, float y, float z, float w) { return float4{x, y, z, w}; }
 inline uint4 make_uint4(uint32_t x, uint32_t y, uint32_t z, uint32_t w) { return uint4{x, y, z, w}; }
 struct emul_dim3 { unsigned x = 0, y = 0, z = 0; };
 extern thread_local emul_dim3 threadIdx, blockIdx;
 extern emul_dim3 gridDim, blockDim;
+#define __align__(n) __attribute__((aligned(n)))
+struct dim3 {
+  unsigned x, y, z;
+  constexpr dim3(unsigned a = 1, unsigned b = 1, unsigned c = 1) : x(a), y(b), z(c) {}
+};
 typedef int hipError_t;
 typedef void* hipStream_t;
-constexpr int hipSuccess = 0, hipErrorInvalidValue = 1;
+constexpr int hipSuccess = 0, hipErrorInvalidValue = 1, hipErrorInvalidDevice = 101;
 inline int hipGetLastError() { return 0; }
 inline int hipGetDevice(int* d) { *d = 0; return 0; }
+typedef int hipDevice_t;
+inline int hipStreamGetDevice(hipStream_t, hipDevice_t* d) { *d = 0; return 0; }
 constexpr int hipDeviceAttributeMultiprocessorCount = 0;
 inline int hipDeviceGetAttribute(int* v, int, int) { *v = 256; return 0; }
+inline const char* hipGetErrorString(int) { return "emulated HIP error"; }
+// a device variable's address is its host stand-in's address in the emulation
+#define HIP_SYMBOL(x) ((const void*)&(x))
+inline int hipGetSymbolAddress(void** p, const void* sym) { *p = (void*)sym; return 0; }
 inline float __uint_as_float(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
 inline uint32_t __float_as_uint(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
 inline float __expf(float x) { return expf(x); }
 template <class T> T min(T a, T b) { return a < b ? a : b; }
 template <class T> T max(T a, T b) { return a > b ? a : b; }
-inline void __syncthreads() {}
+// Block barrier: a real barrier when the block runs one OS thread per lane
+// (tests/emul/runner.h), nothing when lanes run one after another.
+void emul_syncthreads();
+inline void __syncthreads() { emul_syncthreads(); }
+// Lane exchange within a wave (needs the one-thread-per-lane mode).
+void emul_wave_sync();
+extern thread_local long long* emul_wave_slots;  // 1024 slots of the running block
+template <class T> T __shfl_up(T v, unsigned delta, int width) {
+  (void)width;  // always the whole wave (64) in this library
+  const unsigned lane = threadIdx.x & 63;
+  long long slot = 0;
+  memcpy(&slot, &v, sizeof(T));
+  emul_wave_slots[threadIdx.x] = slot;
+  emul_wave_sync();
+  T r = v;
+  if (lane >= delta) memcpy(&r, &emul_wave_slots[threadIdx.x - delta], sizeof(T));
+  emul_wave_sync();
+  return r;
+}
+inline int atomicAdd(int* p, int v) { return __atomic_fetch_add(p, v, __ATOMIC_SEQ_CST); }
+// DPP lane moves of one 32-bit value (the controls this library uses: quad
+// permutes, row half-mirror, row mirror, row_bcast:15, row_bcast:31): lane i
+// takes the value of its source lane when its row is enabled in row_mask and
+// the source exists, else keeps `old`. And readlane.
+inline int emul_dpp_source(int lane, int ctrl) {
+  if (ctrl <= 0xff) return (lane & ~3) + ((ctrl >> (2 * (lane & 3))) & 3);  // quad_perm
+  if (ctrl == 0x140) return (lane & ~15) + (15 - (lane & 15));              // row_mirror
+  if (ctrl == 0x141) return (lane & ~7) + (7 - (lane & 7));                 // row_half_mirror
+  if (ctrl == 0x142) return lane >= 16 ? (lane & ~15) - 1 : -1;             // row_bcast:15
+  if (ctrl == 0x143) return lane >= 32 ? 31 : -1;                           // row_bcast:31
+  fprintf(stderr, "DPP control 0x%x is not emulated\n", ctrl);
+  abort();
+}
+inline int emul_update_dpp(int old, int src, int ctrl, int row_mask, int bank_mask, bool bound_ctrl) {
+  (void)bank_mask, (void)bound_ctrl;  // all banks enabled in this library
+  const int lane = threadIdx.x & 63;
+  emul_wave_slots[threadIdx.x] = src;
+  emul_wave_sync();
+  const int from = emul_dpp_source(lane, ctrl);
+  int r = old;
+  if (((row_mask >> (lane >> 4)) & 1) && from >= 0) r = (int)emul_wave_slots[(threadIdx.x & ~63) + from];
+  emul_wave_sync();
+  return r;
+}
+inline int emul_readlane(int v, int l) {
+  emul_wave_slots[threadIdx.x] = v;
+  emul_wave_sync();
+  const int r = (int)emul_wave_slots[(threadIdx.x & ~63) + l];
+  emul_wave_sync();
+  return r;
+}
+#define __builtin_amdgcn_update_dpp(old, src, ctrl, rm, bm, bc) emul_update_dpp((old), (src), (ctrl), (rm), (bm), (bc))
+#define __builtin_amdgcn_readlane(v, l) emul_readlane((v), (l))
 
 // LDS addresses taken as 32-bit values become region * 2^20 + offset.
 void* emul_lds_region_ptr(uint32_t vaddr, int bytes);

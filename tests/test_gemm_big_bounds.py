@@ -15,46 +15,20 @@ and the shortest contraction the kernel accepts.
 from __future__ import annotations
 
 import os
-import re
 import shutil
 import subprocess
 
 import pytest
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-CSRC = os.path.join(ROOT, "top_routed_expert_amd", "csrc")
-EMUL = os.path.join(ROOT, "tests", "emul")
-
-
-def _clang() -> str | None:
-    for cand in ("/opt/rocm/llvm/bin/clang++", shutil.which("clang++")):
-        if cand and os.path.exists(cand):
-            return cand
-    return None
+from emul_source import big8_source, clang as _clang, compile_cmd, internal_header, read
 
 
 def host_source(kernel_src: str) -> str:
-    """The kernel source rewritten for the host build (see the module docstring)."""
-    s = kernel_src.replace('#include "moe_internal.h"', '#include "emul_internal.h"')
-    s, _ = re.subn(r"typedef __attribute__\(\(address_space\(3\)\)\) void (lds8?_void_t);", r"typedef void \1;", s)
-    s, k0 = re.subn(r"\(uint32_t\)\(uintptr_t\)\(lds8?_void_t\*\)&(\w+)\[0\]\[0\]",
-                    lambda m: f"emul_lds_base((void*)&{m.group(1)}, sizeof({m.group(1)}))", s)
-    s, k1 = re.subn(r'asm volatile\("ds_read_b128 %0, %1 offset:%2" : "=v"\(([^)]*)\) : "v"\((\w+)\), '
-                    r'"n"\(([^)]*)\)\);',
-                    lambda m: (f"{m.group(1)} = emul_ds_read<std::remove_reference_t<decltype({m.group(1)})>>"
-                               f"({m.group(2)} + ({m.group(3)}));"), s)
-    s, _ = re.subn(r'asm volatile\("s_waitcnt lgkmcnt\(%1\)" : "\+v"\([^)]*\) : "n"\([^)]*\)\);', ";", s)
-    s, _ = re.subn(r'asm volatile\("[^"]*" ::: "memory"\);', ";", s)
-    s, _ = re.subn(r'asm volatile\("s_waitcnt lgkmcnt\(%1\)" : "\+v"\([^)]*\) : "n"\([^)]*\)\);', ";", s)
-    s, k4 = re.subn(r"(gemm_bf16_big8?<[^>]*>)<<<\(unsigned\)blocks, (256|512), 0, s>>>\(g\);",
-                    lambda m: f"emul_launch({m.group(1)}, (unsigned)blocks, {m.group(2)}, g);", s)
-    left = re.findall(r"asm volatile.*|<<<.*>>>", s)
-    assert k0 >= 1 and k1 >= 2 and k4 >= 4 and not left, (k0, k1, k4, left)
-    return s
+    return big8_source(kernel_src)
 
 
 def kernel_source() -> str:
-    return open(os.path.join(CSRC, "grouped_gemm_big8.hip")).read()
+    return read("grouped_gemm_big8.hip")
 
 
 @pytest.fixture(scope="module")
@@ -63,15 +37,10 @@ def driver(tmp_path_factory):
     if cc is None:
         pytest.skip("clang++ with AddressSanitizer is needed")
     d = tmp_path_factory.mktemp("emul")
-    hdr = open(os.path.join(CSRC, "moe_internal.h")).read().replace("#include <hip/hip_runtime.h>",
-                                                                    '#include "shim.h"')
-    open(d / "emul_internal.h", "w").write(hdr)
+    open(d / "emul_internal.h", "w").write(internal_header())
     open(d / "emul_big.cpp", "w").write(host_source(kernel_source()))
     exe = d / "driver"
-    cmd = [cc, "-std=c++17", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer", "-pthread",
-           "-I", str(d), "-I", EMUL, "-I", os.path.join(ROOT, "include"), os.path.join(EMUL, "driver.cpp"),
-           "-o", str(exe)]
-    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    r = subprocess.run(compile_cmd(cc, d, "driver.cpp", exe), capture_output=True, text=True, timeout=300)
     if r.returncode != 0 and "asan" in r.stderr.lower() and "cannot find" in r.stderr.lower():
         pytest.skip("no AddressSanitizer runtime for the host compiler")
     assert r.returncode == 0, r.stderr[-3000:]
@@ -117,9 +86,7 @@ def test_planted_offset_is_caught(driver, tmp_path):
     shutil.copy(os.path.join(d, "emul_internal.h"), work / "emul_internal.h")
     open(work / "emul_big.cpp", "w").write(host_source(planted))
     exe = work / "driver"
-    r = subprocess.run([_clang(), "-std=c++17", "-O1", "-g", "-fsanitize=address", "-pthread", "-I", str(work),
-                        "-I", EMUL, "-I", os.path.join(ROOT, "include"), os.path.join(EMUL, "driver.cpp"), "-o",
-                        str(exe)], capture_output=True, text=True, timeout=300)
+    r = subprocess.run(compile_cmd(_clang(), work, "driver.cpp", exe), capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-3000:]
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0")
     r = subprocess.run([str(exe), "600", "8", "2", "512", "320", "320", "3"], capture_output=True, text=True,

@@ -550,7 +550,14 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm8(0));
 }
 
-int g_cus8 = 0;  // compute units of the device (queried once)
+// Compute units of the device `s` runs on (the runtime caches the attribute,
+// so asking on every launch is cheap and holds no state here).
+hipError_t stream_cus(hipStream_t s, int* cus) {
+  hipDevice_t dev = 0;
+  hipError_t e = hipStreamGetDevice(s, &dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, (int)dev);
+  return e;
+}
 
 }  // namespace
 
@@ -560,17 +567,14 @@ hipError_t launch_grouped_gemm_big8(int epi, const GemmArgs& g, hipStream_t s) {
   if (g.Kdim % B8_AKS || g.Kdim < 2 * B8_AKS) return hipErrorInvalidValue;
   if ((uint64_t)g.n_a_rows * (uint64_t)g.Kdim / 8u > 0xffffffffull) return hipErrorInvalidValue;
   if (g.N % 8 || g.ldo % 8) return hipErrorInvalidValue;
-  if (g_cus8 == 0) {
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    g_cus8 = cus > 8 ? cus : 8;
-  }
+  int cus = 0;
+  const hipError_t ce = stream_cus(s, &cus);
+  if (ce != hipSuccess) return ce;
+  cus = cus > 8 ? cus : 8;
   const int BN = epi == EPI_SWIGLU ? B8_ROWS / 2 : B8_ROWS;
   const int n_nb = (g.N + BN - 1) / BN;
   int64_t blocks = ((int64_t)g.max_tiles * n_nb + 7) / 8 * 8;
-  const int64_t cap = (int64_t)g_cus8 / 8 * 8;
+  const int64_t cap = (int64_t)cus / 8 * 8;
   blocks = blocks < cap ? blocks : cap;
   // mean rows per group below 160: many items of at most 128 rows (half of
   // the tiles at 4096 tokens over 289 groups), where the SKIP form gains
