@@ -251,30 +251,45 @@ def layer_forward(x, W: LayerWeights, k: int, k_per_token=None) -> dict:
     return dict(**r, **p, y_perm=y_perm, ys=ys, out=out)
 
 
-def layer_rows(x, W: LayerWeights, k: int, rows, k_per_token=None) -> dict:
-    """The layer's output for selected tokens only, with routing for all tokens.
+def rows_output(x, W: LayerWeights, rows, idx_rows, prob_rows) -> np.ndarray:
+    """The layer's output (3.2.2, step 3) for tokens `rows` given their routing.
 
-    Routing and the permutation are computed for every token (they are
-    cheap); the expert FFNs run only for the (token, choice) pairs of the
-    selected tokens, grouped by expert so each expert's weights are read once.
-    out_rows[i] is the output of token rows[i].
+    idx_rows [R, k]: each selected token's experts (-1: slot without an
+    expert, R12); prob_rows [R, k]: their weights. out_rows[i] = shared FFN of
+    token rows[i] (R3) + sum over j ascending of prob_rows[i, j] times expert
+    idx_rows[i, j]'s FFN of that token. The expert FFNs run grouped by expert,
+    so each expert's weights are read once.
     """
     xr = as_f64(x)
-    r = route(xr, W.router, k, W.bias) if k_per_token is None else route(xr, W.router, k, W.bias, k_per_token)
-    E = r["p32"].shape[1]
-    p = permute(r["idx"], E)
     rows = np.asarray(rows, dtype=np.int64)
-    idx = r["idx"][rows]                                  # [R, k]
+    idx = np.asarray(idx_rows, dtype=np.int64).reshape(len(rows), -1)
+    k = idx.shape[1]
     y_sel = np.zeros((len(rows), k, xr.shape[1]))
     for e in np.unique(idx[idx >= 0]):      # slots without an expert stay zero (R12)
         ri, kj = np.nonzero(idx == e)
         y_sel[ri, kj] = swiglu_ffn(xr[rows[ri]], *W.expert(int(e)))
     sh = W.shared()
     out = np.zeros((len(rows), xr.shape[1])) if sh is None else swiglu_ffn(xr[rows], *sh)
-    prob = as_f64(r["prob"][rows])
+    prob = as_f64(prob_rows).reshape(len(rows), k)
     for j in range(k):
         ok = idx[:, j] >= 0
         out[ok] += prob[ok, j:j + 1] * y_sel[ok, j]
+    return out
+
+
+def layer_rows(x, W: LayerWeights, k: int, rows, k_per_token=None) -> dict:
+    """The layer's output for selected tokens only, with routing for all tokens.
+
+    Routing and the permutation are computed for every token (they are
+    cheap); the expert FFNs run only for the (token, choice) pairs of the
+    selected tokens (rows_output). out_rows[i] is the output of token rows[i].
+    """
+    xr = as_f64(x)
+    r = route(xr, W.router, k, W.bias) if k_per_token is None else route(xr, W.router, k, W.bias, k_per_token)
+    E = r["p32"].shape[1]
+    p = permute(r["idx"], E)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = rows_output(xr, W, rows, r["idx"][rows], r["prob"][rows])
     return dict(**r, **p, rows=rows, out_rows=out)
 
 

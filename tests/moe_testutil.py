@@ -17,7 +17,14 @@ Comparison rules (the layer's tolerances):
     2e-2 * RMS + half a bf16 ulp of the oracle value, element by element.
     The half ulp is the final cast's own error: rounding the exact result to
     bf16 can by itself exceed 2e-2 * RMS once |out| >= 4 with RMS < 0.78;
-  - output of an fp32 layer: max |gpu - oracle| <= 1e-4 * RMS(oracle).
+  - output of an fp32 layer: max |gpu - oracle| <= 1e-4 * RMS(oracle);
+  - near-tie tokens (several top-K sets are right): the GPU's ids must be K
+    distinct experts whose oracle probabilities, widened by the same bound,
+    reach every unchosen expert's (min over chosen of p + b >= max over
+    unchosen of p - b), its probabilities within the bound of the oracle's at
+    those ids and non-increasing; and the token's output must match the
+    oracle's output recomputed with the GPU's ids (and the oracle's
+    probabilities of them), to the output rule above.
 """
 from __future__ import annotations
 
@@ -108,6 +115,50 @@ def compare_routing(idx_gpu, prob_gpu, ref, x, w_router) -> dict:
     return dict(near_ties=int((~keep).sum()), prob_err=float(dp.max()) if dp.size else 0.0,
                 prob_rel=float(rel.max()) if rel.size else 0.0,
                 bound_use=float(np.max(dp / np.where(bound > 0, bound, 1.0))) if dp.size else 0.0)
+
+
+def check_near_ties(idx_gpu, prob_gpu, ref, x, w_router, K: int) -> np.ndarray:
+    """Validity of the GPU's routing of the near-tie tokens (see the module notes); returns those tokens."""
+    tie = np.nonzero(ref["gap"] < NEAR_TIE)[0]
+    if tie.size == 0:
+        return tie
+    p = ref["p32"][tie].astype(np.float64)                      # [n, E]
+    xa = np.abs(O.as_f64(x)[tie])
+    wa = np.abs(O.as_f64(w_router))
+    b = 2.0 * p * math.sqrt(xa.shape[1]) * U32 * (xa @ wa.T) + 8.0 * U32 * p
+    ig = np.asarray(idx_gpu)[tie].astype(np.int64)
+    pg = np.asarray(prob_gpu, dtype=np.float64)[tie]
+    E = p.shape[1]
+    for i, t in enumerate(tie):
+        chosen = ig[i]
+        assert np.all((chosen >= 0) & (chosen < E)) and len(set(chosen.tolist())) == K, \
+            f"near-tie token {t}: ids {chosen} are not {K} distinct experts"
+        mask = np.zeros(E, dtype=bool)
+        mask[chosen] = True
+        low = float(np.min((p[i] + b[i])[mask]))
+        high = float(np.max((p[i] - b[i])[~mask])) if (~mask).any() else -np.inf
+        assert low >= high, f"near-tie token {t}: chosen {chosen} is not a top-{K} set within the bound " \
+                            f"({low:.9g} < {high:.9g})"
+        assert np.all(np.abs(pg[i] - p[i][chosen]) <= b[i][chosen]), f"near-tie token {t}: probabilities off"
+        assert np.all(np.diff(pg[i]) <= 0), f"near-tie token {t}: probabilities not in descending order"
+    return tie
+
+
+def near_tie_reference(x, W, tie, idx_gpu, ref) -> np.ndarray:
+    """The oracle's output rows of the near-tie tokens, recomputed with the GPU's ids and the oracle's p of them."""
+    ig = np.asarray(idx_gpu)[tie].astype(np.int64)
+    return O.rows_output(x, W, tie, ig, np.take_along_axis(ref["p32"][tie].astype(np.float64), ig, axis=1))
+
+
+def compare_rows(out_gpu_rows, out_ref_rows, rms: float, tol_rel: float, bf16: bool, what: str) -> float:
+    """Rows compared against a reference RMS taken elsewhere (the whole compared output)."""
+    g = np.asarray(out_gpu_rows, dtype=np.float64)
+    r = np.asarray(out_ref_rows, dtype=np.float64)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    err = np.abs(g - r)
+    bound = tol_rel * rms + (bf16_half_ulp(r) if bf16 else 0.0)
+    assert np.all(err <= bound), f"{what}: error {float(np.max(err - bound)):.3e} over the bound"
+    return float(err.max()) / rms if rms else 0.0
 
 
 def compare_permutation(offs, st, dest, ref) -> None:

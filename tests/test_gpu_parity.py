@@ -14,8 +14,8 @@ import torch
 
 import synth
 import top_routed_expert_amd as moe
-from moe_testutil import (compare_bf16_out, compare_out, compare_permutation, compare_routing, device_layer,
-                          oracle_weights, out_tol, to_host)
+from moe_testutil import (check_near_ties, compare_bf16_out, compare_out, compare_permutation, compare_routing,
+                          compare_rows, device_layer, near_tie_reference, oracle_weights, out_tol, to_host)
 from oracle import moe_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -53,16 +53,24 @@ def with_out(cfg, out_dtype):
     return moe.Config(cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_expert, cfg.d_shared, cfg.dtype, out_dtype)
 
 
-def check_outputs(spec, cfg, L, out, ref_out, rows=None):
-    """bf16 layers: strict bound on the fp32-output run, bf16 output within bound + half ulp."""
+def check_outputs(spec, cfg, L, out, ref_out, rows=None, tie=None, tie_ref=None):
+    """bf16 layers: strict bound on the fp32-output run, bf16 output within bound + half ulp.
+    tie / tie_ref: near-tie tokens and their oracle rows under the GPU's routing, held to the same
+    rule against the RMS of the compared rows."""
     sel = (lambda a: a) if rows is None else (lambda a: a[torch.from_numpy(rows).to(a.device)])
+    at = lambda a, r: a[torch.from_numpy(np.asarray(r)).to(a.device)]
     if spec.dtype == "bf16":
         out32 = moe.layer_forward(with_out(cfg, torch.float32), L["x"], L)
         c32 = compare_out(to_host(sel(out32)), ref_out, 2e-2, "out (fp32 before the final cast)")
         assert torch.equal(out, out32.to(torch.bfloat16)), "bf16 output is not the rounding of the fp32 output"
         c16 = compare_bf16_out(to_host(sel(out)), ref_out)
+        if tie is not None and len(tie):
+            compare_rows(to_host(at(out32, tie)), tie_ref, c32["rms"], 2e-2, False, "near-tie rows (fp32)")
+            compare_rows(to_host(at(out, tie)), tie_ref, c32["rms"], 2e-2, True, "near-tie rows (bf16)")
         return c32, c16
     c = compare_out(to_host(sel(out)), ref_out, out_tol(spec))
+    if tie is not None and len(tie):
+        compare_rows(to_host(at(out, tie)), tie_ref, c["rms"], out_tol(spec), False, "near-tie rows")
     return c, c
 
 
@@ -75,11 +83,13 @@ def run_full_compare(spec, L=None):
     ref = O.layer_forward(L["x"].cpu(), W, spec.K)
     r = compare_routing(to_host(idx), to_host(prob), ref, L["x"].cpu(), W.router)
     keep = ref["gap"] >= 1e-6
+    tie = check_near_ties(to_host(idx), to_host(prob), ref, L["x"].cpu(), W.router, spec.K)
+    tie_ref = near_tie_reference(L["x"].cpu(), W, tie, to_host(idx), ref) if tie.size else None
     # permutation of the GPU's own ids must equal the oracle's permutation of them
     p_ref = O.permute(to_host(idx), spec.E)
     assert np.array_equal(to_host(offs).astype(np.int64), p_ref["offsets"])
     rows = np.nonzero(keep)[0]
-    c32, c16 = check_outputs(spec, cfg, L, out, ref["out"][rows], rows)
+    c32, c16 = check_outputs(spec, cfg, L, out, ref["out"][rows], rows, tie, tie_ref)
     return r, c32, c16
 
 
@@ -219,11 +229,14 @@ def test_layer_full_size(name, n_rows):
     rows = sample_rows(spec.T, n_rows, 1234, must=[first_hot])
     rows = rows[ref["gap"][rows] >= 1e-6]
     rr = O.layer_rows(x_host, W, spec.K, rows)
-    c32, c16 = check_outputs(spec, cfg, L, out, rr["out_rows"], rows)
+    # near ties: a valid top-K set, and the output of the experts the GPU chose
+    tie = check_near_ties(gidx, to_host(prob), ref, x_host, W.router, spec.K)
+    tie_ref = near_tie_reference(x_host, W, tie, gidx, ref) if tie.size else None
+    c32, c16 = check_outputs(spec, cfg, L, out, rr["out_rows"], rows, tie, tie_ref)
     msg = (f"{name}: near_ties={r['near_ties']} prob_err={r['prob_err']:.2e} prob_rel={r['prob_rel']:.2e} "
            f"bound_use={r['bound_use']:.3f} touched={load['touched']} "
            f"skew={load['skew']:.2f} out_rel(before cast)={c32['rel']:.3e} out_rel(output)={c16['rel']:.3e} "
-           f"rows={len(rows)}")
+           f"rows={len(rows)} near_tie_rows_checked={len(tie)}")
     if spec.groups:
         msg += f" group_counts={O.group_counts(counts, spec.groups).tolist()}"
     print(msg)
@@ -278,3 +291,70 @@ def test_stage_permutation_full_prefill():
     torch.cuda.synchronize()
     p_ref = O.permute(to_host(idx), spec.E)
     compare_permutation(to_host(offs), to_host(st), to_host(dest), p_ref)
+
+
+def whole_segments(spec, L, W_dev, cfg):
+    """Every row of whole expert segments through the layer's own expert launch (the E routed
+    groups plus the shared expert as one more group, rows gathered through the permutation:
+    the arguments moe_layer_forward passes to its expert GEMMs), against the oracle's FFN.
+    Segments: the hottest expert (several 256-row tiles), the smallest expert above 256 rows
+    (two tiles), the smallest above 512 rows if any, and the shared expert's first and last
+    row tiles."""
+    T, K, E, F = spec.T, spec.K, spec.E, spec.F
+    P = T * K
+    idx, _ = moe.route(cfg, L["x"], W_dev["w_router"], L["bias"])
+    offs, st, _ = moe.permute(cfg, idx)
+    offs_ext = torch.cat([offs, torch.tensor([P + T], dtype=torch.int32, device=offs.device)])
+    h = moe.expert_gate_up(cfg, offs_ext, L["x"], W_dev["w_gate"], W_dev["w_up"], gather=st, n_rows=P + T,
+                           s_gate=W_dev["s_gate"], s_up=W_dev["s_up"])
+    y = moe.expert_down(cfg, offs_ext, h, W_dev["w_down"], s_down=W_dev["s_down"])
+    torch.cuda.synchronize()
+    del h
+    oh = to_host(offs_ext).astype(np.int64)
+    sth = to_host(st).astype(np.int64)
+    counts = np.diff(oh[:E + 1])
+    W = oracle_weights(L)
+    x_host = L["x"].cpu()
+    segs = [("hottest expert", int(np.argmax(counts)))]
+    for lim in (256, 512):
+        over = np.nonzero(counts > lim)[0]
+        if over.size:
+            segs.append((f"smallest expert above {lim} rows", int(over[np.argmin(counts[over])])))
+    done = []
+    for label, e in segs:
+        a, b = int(oh[e]), int(oh[e + 1])
+        ref = O.swiglu_ffn(x_host[torch.from_numpy(sth[a:b])], *W.expert(e))
+        c = compare_out(to_host(y[a:b]), ref, 2e-2, f"{label} {e} ({b - a} rows)")
+        done.append(f"{label} {e}: {b - a} rows, rel {c['rel']:.2e}")
+    sg = W.shared()
+    for label, t0 in (("shared expert, first tile", 0), ("shared expert, last tile", max(0, T - 256))):
+        t1 = min(T, t0 + 256)
+        ref = O.swiglu_ffn(x_host[t0:t1], *sg)
+        c = compare_out(to_host(y[P + t0:P + t1]), ref, 2e-2, label)
+        done.append(f"{label}: {t1 - t0} rows, rel {c['rel']:.2e}")
+    assert counts.max() > 256, "the hottest expert should span several row tiles"
+    return done
+
+
+@pytest.mark.parametrize("name", ["prefill", "skew", "full"])
+def test_whole_segments_full_size(name):
+    """Whole expert segments at the full workload sizes, every row compared (packed weights, the
+    layout the benchmark times)."""
+    spec = synth.spec(name)
+    L = device_layer(spec)
+    cfg = moe.config_for(spec, packed=True)
+    Wp = moe.pack_layer(L)
+    done = whole_segments(spec, L, Wp, cfg)
+    del Wp
+    torch.cuda.empty_cache()
+    print(f"{name}: " + "; ".join(done))
+
+
+@pytest.mark.parametrize("name", list(MANY_ITEMS))
+def test_whole_segments_many_items(name):
+    """Whole segments of the narrow many-items layers (several items per 256x256 block)."""
+    spec = MANY_ITEMS[name]
+    L = device_layer(spec)
+    cfg = moe.config_for(spec, packed=True)
+    done = whole_segments(spec, L, moe.pack_layer(L), cfg)
+    print(f"{name}: " + "; ".join(done))

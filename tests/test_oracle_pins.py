@@ -470,6 +470,32 @@ def pin_fp8_quantisation():
     assert np.all(np.abs(wd - w) <= step + 1e-30)
 
 
+def pin_rows_output():
+    """Output rows for a given routing (any expert ids, empty slots, repeats): pure-Python brute force."""
+    rng = np.random.default_rng(47)
+    T, D, E, K, F = 6, 5, 7, 3, 4
+    L = rand_layer(rng, T, D, E, K, F, 3)
+    W = O.LayerWeights.from_dict(L)
+    rows = [4, 1, 5]
+    idx = np.array([[2, 6, -1], [6, 6, 0], [-1, -1, -1]])   # not a top-k routing: the oracle takes it as given
+    prob = np.array([[0.5, 0.25, 0.9], [0.125, 0.375, 1.0], [0.3, 0.3, 0.3]])
+    got = O.rows_output(L["x"], W, rows, idx, prob)
+    for i, t in enumerate(rows):
+        xr = L["x"][t].tolist()
+        want = brute_ffn_row(xr, L["s_gate"].tolist(), L["s_up"].tolist(), L["s_down"].tolist())
+        for j in range(K):
+            e = int(idx[i, j])
+            if e >= 0:
+                y = brute_ffn_row(xr, L["w_gate"][e].tolist(), L["w_up"][e].tolist(), L["w_down"][e].tolist())
+                want = [a + prob[i, j] * b for a, b in zip(want, y)]
+        assert np.allclose(got[i], want, rtol=1e-12, atol=1e-13), (i, got[i], want)
+    # with the oracle's own top-k routing it is the full layer's rows
+    full = O.layer_forward(L["x"], W, K)
+    sel = [0, 3, 5]
+    assert np.allclose(O.rows_output(L["x"], W, sel, full["idx"][sel], full["prob"][sel]), full["out"][sel],
+                       rtol=1e-12, atol=1e-13)
+
+
 def pin_expert_load():
     """Expert Activation Skew = max count / mean count over all experts: hand-worked values,
     closed forms, invariances, and the counts of a routing whose choices are forced."""
@@ -550,7 +576,7 @@ PINS = [pin_route_bruteforce, pin_route_ties, pin_route_properties, pin_route_bi
         pin_ffn_closed_form, pin_ffn_bruteforce, pin_layer_worked_example,
         pin_layer_special_cases, pin_dynamic_topk_route, pin_dynamic_topk_permute, pin_dynamic_topk_layer,
         pin_ep_receive_plan, pin_group_stats, pin_ep_share_composition, pin_fp8_codec, pin_fp8_quantisation,
-        pin_expert_load, pin_group_counts, pin_page_constants]
+        pin_rows_output, pin_expert_load, pin_group_counts, pin_page_constants]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -710,12 +736,16 @@ def _skew_mean_over_touched(counts):
                 skew=float(c.max() / mean) if mean > 0 else 0.0, touched=int(t.size))
 
 
+def _rows_output_slots_reversed(x, W, rows, idx_rows, prob_rows):
+    return _orig["rows_output"](x, W, rows, idx_rows, np.asarray(prob_rows)[:, ::-1])
+
+
 def _strided_groups(counts, groups):
     c = np.asarray(counts)
     return np.array([int(c[g::groups].sum()) for g in range(groups)])
 
 
-_orig = {n: getattr(O, n) for n in ("quantize_rows_fp8", "ep_receive_plan", "group_stats", "select_topk", "swiglu_ffn", "permute", "combine",
+_orig = {n: getattr(O, n) for n in ("rows_output", "quantize_rows_fp8", "ep_receive_plan", "group_stats", "select_topk", "swiglu_ffn", "permute", "combine",
                                     "router_logits", "softmax", "silu", "route")}
 
 MUTANTS = {
@@ -740,6 +770,7 @@ MUTANTS = {
     "fp8_scale_without_448": ("quantize_rows_fp8", _scale_by_max),
     "skew_mean_over_touched_experts": ("expert_load", _skew_mean_over_touched),
     "expert_groups_strided": ("group_counts", _strided_groups),
+    "row_weights_in_reversed_slots": ("rows_output", _rows_output_slots_reversed),
 }
 
 
