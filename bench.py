@@ -9,14 +9,18 @@ K steps; each step is bracketed by HIP events on the stream the library
 launches on, with a 512 MiB write between steps (outside the events) so the
 256 MiB Infinity Cache does not keep the previous step's experts.
 
-One JSON line is printed. Besides the layer throughput it carries:
+One JSON line is printed. The headline (value, ms_per_step, config) is the
+--workload (default: decode, T=32). Besides it the line carries:
   roofline      the dominant kernel (expert gate/up projection with the
                 SwiGLU epilogue, timed alone through moe_expert_gate_up with
                 the layer's exact arguments): algorithmic bytes or flops per
                 launch / average launch time, against the MI355X peak;
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload;
-  secondary     the prefill workload (T=8192) measured the same way, for the
-                MFMA-side figure, unless --no-secondary.
+  cpu_baseline  the CPU oracle timed on bounded samples of the decode and
+                prefill batches (expert weights copied to host before timing);
+  workloads     the other four named workloads (tiny, prefill, skew, full
+                width) measured the same way, each with its own roofline; the
+                full-width entry carries the per-group activation counts of
+                the 8 x 36 expert groups and the Expert Activation Skew.
 """
 from __future__ import annotations
 
@@ -75,9 +79,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "skew", "full"])
-    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=32)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32, help="decode tokens in the CPU sample")
+    ap.add_argument("--cpu-prefill-tokens", type=int, default=256, help="prefill tokens in the CPU sample")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--fp8", action="store_true",
                     help="fp8 (E4M3) vs bf16 expert weights at decode and prefill, one JSON line each")
@@ -139,16 +144,39 @@ def layer_flops_bytes(spec, counts):
     return flops, wbytes + abytes, touched
 
 
-def gate_up_kernel(rows: int, groups: int) -> str:
+# tile-height thresholds of the expert GEMMs, in mean rows per group (as gemm_block_rows in
+# csrc/grouped_gemm.hip and the 256x256 launcher in csrc/grouped_gemm_big8.hip)
+ROWS_32, ROWS_256, ROWS_256_SKIP = 24, 48, 160
+
+
+def gate_up_kernel(rows: int, groups: int, packed: bool) -> str:
     """Name of the gate/up kernel the library picks for `rows` rows over `groups` groups (bf16)."""
-    if rows <= 24 * groups:  # thresholds as gemm_block_rows
+    if rows <= ROWS_32 * groups:
         return "gemm_bf16_mfma<EPI_SWIGLU>, 32-row tiles"
-    if rows >= 96 * groups:
-        return "gemm_bf16_big8<EPI_SWIGLU>, 256x256 tiles, 8 waves"
-    return "gemm_bf16_mfma<EPI_SWIGLU>, %d-row tiles" % (64 if rows <= 48 * groups else 128)
+    if rows >= ROWS_256 * groups:
+        skip = packed and rows < ROWS_256_SKIP * groups
+        return "gemm_bf16_big8<EPI_SWIGLU%s>, 256x256 tiles, 8 waves" % (", skipping empty half items" if skip else "")
+    return "gemm_bf16_mfma<EPI_SWIGLU>, 64-row tiles"
+
+
+def roofline(k_bytes: int, k_flops: int, k_ms: float, peak_tf: float, prefer: str | None = None) -> dict:
+    """Roofline entry of one kernel: bound = the larger roofline time (or `prefer`), both fractions reported."""
+    gbs = k_bytes / (k_ms * 1e-3) / 1e9
+    tfs = k_flops / (k_ms * 1e-3) / 1e12
+    bound = prefer or ("hbm" if k_bytes / (HBM_PEAK_GBS * 1e9) >= k_flops / (peak_tf * 1e12) else "mfma")
+    if bound == "hbm":
+        r = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        r = dict(bound="mfma", achieved=round(tfs, 1), peak=peak_tf, unit="TFLOP/s", frac=round(tfs / peak_tf, 4))
+    r.update(launch_ms=round(k_ms, 4), algorithmic_bytes=int(k_bytes), algorithmic_flops=int(k_flops),
+             intensity_flop_per_byte=round(k_flops / k_bytes, 1), mfma_frac=round(tfs / peak_tf, 4),
+             hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+    return r
 
 
 def measure(spec, steps, warmup, flush_on, packed=True):
+    """The layer and its dominant kernel on one workload: a dict with the layer's timing, the work
+    accounting of this batch's routing, and the gate/up kernel's roofline entry."""
     import numpy as np
     import torch
 
@@ -176,9 +204,12 @@ def measure(spec, steps, warmup, flush_on, packed=True):
     offs, st, dest = moe.permute(cfg, idx)
     counts = np.diff(offs.cpu().numpy())
     flops, nbytes, touched = layer_flops_bytes(spec, counts)
+    es = 2 if spec.dtype == "bf16" else 4
+    peak_tf = MFMA_BF16_PEAK_TFLOPS if spec.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     res = dict(ms=ms_step, ms_min=float(np.min(ms)), wall=wall, tokens_per_s=T / (ms_step * 1e-3),
                touched=touched, layer_tflops=flops / (ms_step * 1e-3) / 1e12,
-               layer_gbs=nbytes / (ms_step * 1e-3) / 1e9, skew=float(counts.max() / counts.mean()))
+               layer_gbs=nbytes / (ms_step * 1e-3) / 1e9, skew=float(counts.max() / counts.mean()),
+               layer_flops=flops, layer_bytes=nbytes, counts=counts, peak_tf=peak_tf)
     # --- dominant kernel: expert gate/up + SwiGLU, the layer's own arguments -
     P = T * K
     fused = spec.Fs == spec.F and spec.Fs > 0
@@ -192,28 +223,41 @@ def measure(spec, steps, warmup, flush_on, packed=True):
                                          h=h, ws=gws)
     kms, _ = timed(gate_up, steps, warmup, flush)
     k_ms = float(np.mean(kms))
-    es = 2 if spec.dtype == "bf16" else 4
     k_experts = touched + (1 if fused else 0)
     k_bytes = k_experts * 2 * F * D * es + T * D * es + n_rows * F * es
     k_flops = 2 * n_rows * 2 * F * D
-    t_hbm = k_bytes / (HBM_PEAK_GBS * 1e9)
-    peak_tf = MFMA_BF16_PEAK_TFLOPS if spec.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-    t_mfma = k_flops / (peak_tf * 1e12)
-    gbs = k_bytes / (k_ms * 1e-3) / 1e9
-    tfs = k_flops / (k_ms * 1e-3) / 1e12
-    if t_hbm >= t_mfma:
-        roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4))
-    else:
-        roof = dict(bound="mfma", achieved=round(tfs, 1), peak=peak_tf, unit="TFLOP/s", frac=round(tfs / peak_tf, 4))
-    kname = gate_up_kernel(n_rows, E + (1 if fused else 0)) if spec.dtype == "bf16" else "gemm_generic<EPI_SWIGLU>"
+    # the prefill-shaped workloads are judged by their matrix-core fraction (their gate/up intensity,
+    # 245-500 flop/B, sits near or above the 312 flop/B ridge); decode by its HBM fraction
+    prefer = "mfma" if spec.dtype == "bf16" and n_rows >= ROWS_256 * k_experts else None
+    roof = roofline(k_bytes, k_flops, k_ms, peak_tf, prefer)
+    kname = gate_up_kernel(n_rows, k_experts, packed) if spec.dtype == "bf16" else "gemm_generic<EPI_SWIGLU>"
     roof.update(traffic=measured_traffic(spec.name), kernel=kname + " (expert gate/up + SwiGLU)",
-                launch_ms=round(k_ms, 4), algorithmic_bytes=int(k_bytes), algorithmic_flops=int(k_flops),
-                experts_read=k_experts, mfma_frac=round(tfs / peak_tf, 4), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+                experts_read=k_experts)
     res["roofline"] = roof
     res["L"] = L
     res["layout"] = "packed" if packed else "rows"
     del W
     return res
+
+
+def workload_entry(spec, r: dict) -> dict:
+    """JSON entry of one workload's measurement (everything but the headline fields)."""
+    import numpy as np
+
+    e = {"workload": spec.name, "tokens": spec.T, "d_model": spec.D, "routed_experts": spec.E, "top_k": spec.K,
+         "d_expert": spec.F, "d_shared": spec.Fs, "dtype": "bf16" if spec.dtype == "bf16" else "f32",
+         "router_bias": "zipf" if spec.skew else "none", "weight_layout": r["layout"],
+         "value": round(r["tokens_per_s"], 1), "unit": "tokens/s", "ms_per_step": round(r["ms"], 5),
+         "ms_min": round(r["ms_min"], 5), "layer_tflops": round(r["layer_tflops"], 2),
+         "layer_mfma_frac": round(r["layer_tflops"] / r["peak_tf"], 4), "layer_gbs": round(r["layer_gbs"], 1),
+         "layer_hbm_frac": round(r["layer_gbs"] / HBM_PEAK_GBS, 4), "experts_touched": r["touched"],
+         "roofline": r["roofline"]}
+    # Expert Activation Skew: the largest expert's pair count over the mean count of all E experts
+    c = np.asarray(r["counts"], dtype=np.int64)
+    e["expert_activation_skew"] = round(float(c.max() / c.mean()), 3)
+    if spec.groups:  # pairs per group of E/G consecutive experts
+        e["group_counts"] = [int(v) for v in c.reshape(spec.groups, -1).sum(axis=1)]
+    return e
 
 
 SWEEP_T = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384]
@@ -222,9 +266,9 @@ SWEEP_T = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384]
 def tile_kernel(T, spec):
     """Row tiles the expert GEMMs use for T tokens (mean rows per group decides), as the library picks."""
     rows, groups = T * spec.K + (T if spec.Fs == spec.F else 0), spec.E + (1 if spec.Fs == spec.F else 0)
-    if rows <= 24 * groups:  # thresholds as gemm_block_rows
+    if rows <= ROWS_32 * groups:
         return 32
-    return 256 if rows >= 48 * groups else (64 if rows <= 48 * groups else 128)
+    return 256 if rows >= ROWS_256 * groups else 64
 
 
 def sweep(steps, warmup, flush_on):
@@ -412,24 +456,43 @@ def ep_share(steps, warmup, flush_on, n_src=8, n_groups=8, group=0):
                 group_pair_fraction=[round(float(v), 5) for v in f])
 
 
-CPU_BASELINE_MIN_S = 10.0  # repeat whole passes over the sample until at least this much CPU time
+CPU_BASELINE_MIN_S = 10.0  # repeat whole passes over a sample until at least this much CPU time
 
 
-def cpu_baseline(spec, L, n_tokens: int):
-    """The oracle, as it stands, on the first n_tokens tokens of the workload (single thread),
-    repeated pass by pass until CPU_BASELINE_MIN_S seconds have accumulated."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def oracle_rate(spec, L, x, label: str) -> dict:
+    """The oracle, as it stands, on the host tokens x (single thread), repeated pass by pass until
+    CPU_BASELINE_MIN_S seconds have accumulated. The expert weights the sample routes to are copied to
+    host memory before timing (the oracle's own float64 conversion of them is part of its time)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
 
+    import top_routed_expert_amd as moe
     from oracle import moe_oracle as O
 
-    n = min(n_tokens, spec.T)
-    x = L["x"][:n].cpu()
-    host = lambda t: None if t is None else t.cpu()
-    W = O.LayerWeights(host(L["w_router"]), lambda e: (host(L["w_gate"][e]), host(L["w_up"][e]), host(L["w_down"][e])),
-                       (lambda: (host(L["s_gate"]), host(L["s_up"]), host(L["s_down"]))) if spec.Fs else None,
-                       host(L.get("bias")))
+    n = x.shape[0]
+    # experts the sample uses (the library's routing of the same tokens decides what to copy; any
+    # other expert the oracle asks for is copied when asked, inside the timed region)
+    cfg = moe.config_for(spec)
+    idx, _ = moe.route(cfg, x.to(L["x"].device), L["w_router"], L.get("bias"))
+    used = sorted(set(int(e) for e in idx.cpu().numpy().reshape(-1).tolist() if e >= 0))
+    host = {e: (L["w_gate"][e].cpu(), L["w_up"][e].cpu(), L["w_down"][e].cpu()) for e in used}
+    expert = lambda e: host[e] if e in host else (L["w_gate"][e].cpu(), L["w_up"][e].cpu(), L["w_down"][e].cpu())
+    sh = (L["s_gate"].cpu(), L["s_up"].cpu(), L["s_down"].cpu()) if spec.Fs else None
+    bias = L.get("bias")
+    W = O.LayerWeights(L["w_router"].cpu(), expert, (lambda: sh) if sh else None,
+                       None if bias is None else bias.cpu())
     prev = torch.get_num_threads()
     torch.set_num_threads(1)
     try:
@@ -443,9 +506,24 @@ def cpu_baseline(spec, L, n_tokens: int):
                 assert np.all(np.isfinite(r["out"]))
     finally:
         torch.set_num_threads(prev)
-    return dict(value=round(passes * n / dt, 3), unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{passes} passes over the first {n} of the {spec.T} tokens of the {spec.name} batch, "
-                       f"whole layer (numpy fp64, expert weights copied to host as used), {dt:.1f} s")
+    return dict(value=round(passes * n / dt, 3), unit="tokens/s",
+                sample=f"{passes} pass(es) over the first {n} tokens of the {label} batch ({len(used)} experts), "
+                       f"whole layer, numpy float64, {dt:.1f} s")
+
+
+def cpu_baseline(L, decode_tokens: int, prefill_tokens: int) -> dict:
+    """The oracle on the decode batch's first tokens (the headline unit) and on a slice of the prefill
+    batch (more rows per expert, so its per-expert weight conversion is shared by more tokens).
+    Decode and prefill use the same weights (same shape and seed); L holds them."""
+    import synth
+
+    d, p = synth.spec("decode"), synth.spec("prefill")
+    r_d = oracle_rate(d, L, synth.make_x(d, "cpu", tokens=slice(0, min(decode_tokens, d.T))), "decode")
+    r_p = oracle_rate(p, L, synth.make_x(p, "cpu", tokens=slice(0, min(prefill_tokens, p.T))), "prefill")
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return dict(value=r_d["value"], unit="tokens/s", cores=1, kind="oracle", sample=r_d["sample"],
+                nproc=os.cpu_count(), cpus_available=aff, cpu_model=cpu_model(),
+                prefill=dict(value=r_p["value"], unit="tokens/s", sample=r_p["sample"]))
 
 
 def main():
@@ -503,23 +581,36 @@ def main():
         "layer": {"ms_min": round(res["ms_min"], 5), "experts_touched": res["touched"],
                   "expert_load_skew": round(res["skew"], 3), "tflops": round(res["layer_tflops"], 2),
                   "gbs": round(res["layer_gbs"], 1),
-                  "mfma_frac": round(res["layer_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                  "mfma_frac": round(res["layer_tflops"] / res["peak_tf"], 4),
                   "hbm_frac": round(res["layer_gbs"] / HBM_PEAK_GBS, 4), "timed_wall_s": round(res["wall"], 3),
                   "cache_flush_between_steps": not args.no_flush},
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(spec, res["L"], args.cpu_sample_tokens)
-    del res["L"]
-    if not args.no_secondary and spec.name != "prefill":
-        torch.cuda.empty_cache()
-        sec = synth.spec("prefill")
-        print(f"[bench] secondary workload={sec.name} T={sec.T}", file=sys.stderr, flush=True)
-        r2 = measure(sec, args.steps, args.warmup, not args.no_flush, args.layout == "packed")
-        line["secondary"] = {"workload": sec.name, "tokens": sec.T, "value": round(r2["tokens_per_s"], 1),
-                             "unit": "tokens/s", "ms_per_step": round(r2["ms"], 5),
-                             "layer_mfma_frac": round(r2["layer_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "layer_tflops": round(r2["layer_tflops"], 2), "roofline": r2["roofline"]}
+        same = lambda a, b: (a.D, a.E, a.F, a.Fs, a.dtype, a.seed) == (b.D, b.E, b.F, b.Fs, b.dtype, b.seed)
+        if same(spec, synth.spec("decode")):
+            line["cpu_baseline"] = cpu_baseline(res["L"], args.cpu_sample_tokens, args.cpu_prefill_tokens)
+        else:
+            del res["L"]
+            torch.cuda.empty_cache()
+            Ld = synth.make_layer(synth.spec("decode"), "cuda")
+            line["cpu_baseline"] = cpu_baseline(Ld, args.cpu_sample_tokens, args.cpu_prefill_tokens)
+            del Ld
+    res.pop("L", None)
+    if not args.no_secondary:
+        others = {}
+        for name in ("tiny", "decode", "prefill", "skew", "full"):
+            if name == spec.name:
+                continue
+            torch.cuda.empty_cache()
+            sp = synth.spec(name)
+            print(f"[bench] workload={sp.name} T={sp.T}", file=sys.stderr, flush=True)
+            r2 = measure(sp, args.steps, args.warmup, not args.no_flush, args.layout == "packed")
+            del r2["L"]
+            others[name] = workload_entry(sp, r2)
+            print(f"[bench] {name}: layer {r2['ms']:.4f} ms/step; gate/up kernel "
+                  f"{r2['roofline']['launch_ms']:.4f} ms", file=sys.stderr, flush=True)
+        line["workloads"] = others
     print(json.dumps(line), flush=True)
 
 
