@@ -44,6 +44,7 @@ static EmulBarrier g_block_barrier;
 static EmulBarrier g_wave_barrier[16];
 static long long g_wave_slots[1024];
 thread_local long long* emul_wave_slots = g_wave_slots;
+bool emul_lanes_synced() { return emul_sync_mode; }
 void emul_syncthreads() {
   if (emul_sync_mode) g_block_barrier.wait();
 }

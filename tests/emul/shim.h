@@ -83,8 +83,12 @@ inline int emul_dpp_source(int lane, int ctrl) {
   fprintf(stderr, "DPP control 0x%x is not emulated\n", ctrl);
   abort();
 }
+// Lane by lane (kernels whose lane moves feed values only, not addresses), a
+// move returns the lane's own value.
+bool emul_lanes_synced();
 inline int emul_update_dpp(int old, int src, int ctrl, int row_mask, int bank_mask, bool bound_ctrl) {
   (void)bank_mask, (void)bound_ctrl;  // all banks enabled in this library
+  if (!emul_lanes_synced()) return old;
   const int lane = threadIdx.x & 63;
   emul_wave_slots[threadIdx.x] = src;
   emul_wave_sync();

@@ -65,13 +65,20 @@ def check_outputs(spec, cfg, L, out, ref_out, rows=None, tie=None, tie_ref=None)
         assert torch.equal(out, out32.to(torch.bfloat16)), "bf16 output is not the rounding of the fp32 output"
         c16 = compare_bf16_out(to_host(sel(out)), ref_out)
         if tie is not None and len(tie):
-            compare_rows(to_host(at(out32, tie)), tie_ref, c32["rms"], 2e-2, False, "near-tie rows (fp32)")
-            compare_rows(to_host(at(out, tie)), tie_ref, c32["rms"], 2e-2, True, "near-tie rows (bf16)")
+            rms = rms_of(ref_out, tie_ref)
+            compare_rows(to_host(at(out32, tie)), tie_ref, rms, 2e-2, False, "near-tie rows (fp32)")
+            compare_rows(to_host(at(out, tie)), tie_ref, rms, 2e-2, True, "near-tie rows (bf16)")
         return c32, c16
     c = compare_out(to_host(sel(out)), ref_out, out_tol(spec))
     if tie is not None and len(tie):
-        compare_rows(to_host(at(out, tie)), tie_ref, c["rms"], out_tol(spec), False, "near-tie rows")
+        compare_rows(to_host(at(out, tie)), tie_ref, rms_of(ref_out, tie_ref), out_tol(spec), False, "near-tie rows")
     return c, c
+
+
+def rms_of(*parts) -> float:
+    """RMS over all compared rows (the near-tie rows included: a layer may have nothing else)."""
+    a = np.concatenate([np.asarray(p, dtype=np.float64).reshape(-1) for p in parts])
+    return math.sqrt(float(np.mean(a ** 2))) if a.size else 0.0
 
 
 def run_full_compare(spec, L=None):
@@ -141,6 +148,20 @@ def test_stages_small():
     cfg32 = moe.Config(cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_expert, cfg.d_shared, cfg.dtype, torch.float32)
     out32 = moe.combine(cfg32, y, dest, prob, ys)
     compare_out(to_host(out32), out_ref, 1e-6, "combine fp32")
+
+
+def test_expert_outputs_beyond_fp16_range():
+    """Down projections scaled by 2^17 (exact in bf16): expert outputs reach ~5e5, far beyond the
+    fp16 range (65504). On the 256-row-tile path the routed outputs are staged as fp16 with one
+    power-of-two scale per 64-column row chunk, so they must come through as at unit scale."""
+    spec = SMALL["bf16_tiles256"]
+    L = dict(device_layer(spec))
+    scale = 2.0 ** 17
+    L["w_down"] = (L["w_down"].float() * scale).to(torch.bfloat16)
+    L["s_down"] = (L["s_down"].float() * scale).to(torch.bfloat16)
+    r, c32, c16 = run_full_compare(spec, L=L)
+    print(f"scaled down projections: RMS {c32['rms']:.3e} out_rel(before cast)={c32['rel']:.3e}")
+    assert c32["rms"] > 65504.0  # the outputs really are beyond the fp16 range
 
 
 def test_routed_only():

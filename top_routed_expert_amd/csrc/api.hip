@@ -172,9 +172,15 @@ struct LayerWs {
   int32_t* dest;
   FfnWs ffn;             // routed (+ fused shared) expert rows
   FfnWs ffn_shared;      // shared expert on its own when its width differs
-  float* y;              // [T*K (+T), D] fp32
-  float* y_shared;
+  float* y;              // [T*K (+T), D] fp32 (NULL with y16)
+  float* y_shared;       // [T, D] fp32: the shared expert's rows
   bool fused_shared;
+  // routed expert outputs in the 16-bit format (moe_internal.h) when the down
+  // projection runs on 256-row tiles: half the bytes written by the down GEMM
+  // and read by the combine
+  bool y16;
+  uint16_t* y16v;        // [T*K, D]
+  uint8_t* y16e;         // [T*K, D/64]
 };
 LayerWs carve_layer(Arena& a, const moe_config* c, int64_t T) {
   LayerWs w{};
@@ -191,8 +197,15 @@ LayerWs carve_layer(Arena& a, const moe_config* c, int64_t T) {
   const int64_t rows = P + (w.fused_shared ? T : 0);
   w.ffn = carve_ffn(a, c, c->n_experts + (w.fused_shared ? 2 : 0), rows, c->d_expert);
   if (shared && !w.fused_shared) w.ffn_shared = carve_ffn(a, c, 1, T, c->d_shared);
-  w.y = a.take<float>((P + (shared ? T : 0)) * c->d_model);
-  w.y_shared = shared ? w.y + P * c->d_model : nullptr;
+  w.y16 = w.ffn.sched.block_rows == 256 && c->d_model % 64 == 0;
+  if (w.y16) {
+    w.y16v = a.take<uint16_t>(P * c->d_model);
+    w.y16e = a.take<uint8_t>(P * (c->d_model / 64));
+    w.y_shared = shared ? a.take<float>(T * c->d_model) : nullptr;
+  } else {
+    w.y = a.take<float>((P + (shared ? T : 0)) * c->d_model);
+    w.y_shared = shared ? w.y + P * c->d_model : nullptr;
+  }
   return w;
 }
 
@@ -278,10 +291,16 @@ moe_status run_gate_up(const moe_config* c, const SchedWs& ws, bool build, int n
   return MOE_OK;
 }
 
+// y16 (optional): rows below y16_rows in the 16-bit format (y16, y16_exp); the
+// rest go to y at row r - y16_rows.
 moe_status run_down(const moe_config* c, const SchedWs& ws, bool build, int n_groups, int n_main, int64_t n_rows,
                     const int32_t* offsets, const void* h, const void* w_down, const void* s_down, int d_ff, float* y,
-                    hipStream_t s, const float* const* scales = nullptr) {
+                    hipStream_t s, const float* const* scales = nullptr, uint16_t* y16 = nullptr,
+                    uint8_t* y16_exp = nullptr, int64_t y16_rows = 0) {
   GemmArgs g{};
+  g.out16 = y16;
+  g.out16_exp = y16_exp;
+  g.out16_rows = y16_rows;
   MOE_TRY(fill_tiles(g, ws, offsets, n_groups, n_rows, build, -1, s));
   if (fp8(c)) {  // scales: down, shared down
     g.b_fp8 = 1;
@@ -309,7 +328,8 @@ moe_status run_ffn(const moe_config* c, int n_groups, int n_main, int64_t n_rows
                    const void* x, int64_t n_x_rows, const int32_t* gather, int64_t n_gather, const void* w_gate,
                    const void* w_up, const void* w_down, const void* s_gate, const void* s_up, const void* s_down,
                    int d_ff, float* y, const FfnWs& ws, hipStream_t s, bool tiles_ready = false,
-                   int skip_group = -1, const float* const* scales = nullptr) {
+                   int skip_group = -1, const float* const* scales = nullptr, uint16_t* y16 = nullptr,
+                   uint8_t* y16_exp = nullptr, int64_t y16_rows = 0) {
   // scales (fp8 weights): gate, up, down of the main group, then of the extra group
   const float* gu[4] = {nullptr, nullptr, nullptr, nullptr};
   const float* dn[2] = {nullptr, nullptr};
@@ -319,7 +339,8 @@ moe_status run_ffn(const moe_config* c, int n_groups, int n_main, int64_t n_rows
   }
   MOE_TRY(run_gate_up(c, ws.sched, !tiles_ready, n_groups, n_main, n_rows, offsets, x, n_x_rows, gather, n_gather,
                       w_gate, w_up, s_gate, s_up, d_ff, ws.h, s, skip_group, gu));
-  MOE_TRY(run_down(c, ws.sched, false, n_groups, n_main, n_rows, offsets, ws.h, w_down, s_down, d_ff, y, s, dn));
+  MOE_TRY(run_down(c, ws.sched, false, n_groups, n_main, n_rows, offsets, ws.h, w_down, s_down, d_ff, y, s, dn, y16,
+                   y16_exp, y16_rows));
   return MOE_OK;
 }
 
@@ -619,16 +640,21 @@ moe_status moe_layer_forward_dynamic(const moe_config* cfg, int64_t T, const voi
   const int n_groups = E + (L.fused_shared ? 2 : 0);
   const float* sc[6] = {w->w_gate_scale, w->w_up_scale, w->w_down_scale, w->s_gate_scale, w->s_up_scale,
                         w->s_down_scale};
+  //    (with y16, routed rows below T*K in the 16-bit format, shared rows to y_shared)
   MOE_TRY(run_ffn(cfg, n_groups, E, P + extra, L.offsets_ext, x, T, L.sorted_token, P, w->w_gate, w->w_up,
-                  w->w_down, w->s_gate, w->s_up, w->s_down, cfg->d_expert, L.y, L.ffn, s, small,
-                  L.fused_shared ? E : -1, sc));
+                  w->w_down, w->s_gate, w->s_up, w->s_down, cfg->d_expert, L.y16 ? L.y_shared : L.y, L.ffn, s,
+                  small, L.fused_shared ? E : -1, sc, L.y16v, L.y16e, L.y16 ? P : 0));
   if (cfg->d_shared > 0 && !L.fused_shared) {
     const float* sc_shared[6] = {w->s_gate_scale, w->s_up_scale, w->s_down_scale, nullptr, nullptr, nullptr};
     MOE_TRY(run_ffn(cfg, 1, 1, T, nullptr, x, T, nullptr, 0, w->s_gate, w->s_up, w->s_down, nullptr, nullptr,
                     nullptr, cfg->d_shared, L.y_shared, L.ffn_shared, s, false, -1, sc_shared));
   }
   // 4. weighted combine: shared + sum_k prob * routed, one rounding to out_dtype
-  MOE_TRY_HIP(launch_combine(cfg->out_dtype, T, D, K, L.y, P, L.dest, prob, L.y_shared, out, s), "combine");
+  if (L.y16)
+    MOE_TRY_HIP(launch_combine16(cfg->out_dtype, T, D, K, L.y16v, L.y16e, P, L.dest, prob, L.y_shared, out, s),
+                "combine");
+  else
+    MOE_TRY_HIP(launch_combine(cfg->out_dtype, T, D, K, L.y, P, L.dest, prob, L.y_shared, out, s), "combine");
   return ok();
 }
 

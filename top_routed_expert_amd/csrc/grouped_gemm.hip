@@ -476,6 +476,7 @@ static hipError_t launch_fast(const GemmArgs& g, hipStream_t s) {
 hipError_t launch_grouped_gemm(int dtype, bool fast, int epi, int block_rows, const GemmArgs& g, hipStream_t s) {
   if (g.max_tiles <= 0 || g.N <= 0) return hipSuccess;
   if (g.b_fp8 && !fast) return hipErrorInvalidValue;  // fp8 weights: bf16 MFMA kernels only
+  if (g.out16 && !fast) return hipErrorInvalidValue;
   if (!fast) {
     if (g.b_packed) return hipErrorInvalidValue;  // packed weights exist only on the bf16 MFMA path
     const int n_nb = (g.N + 63) / 64;
@@ -490,6 +491,7 @@ hipError_t launch_grouped_gemm(int dtype, bool fast, int epi, int block_rows, co
     return hipGetLastError();
   }
   if (block_rows == 256) return launch_grouped_gemm_big8(epi, g, s);
+  if (g.out16) return hipErrorInvalidValue;  // the 16-bit expert-output format: 256x256 kernel only
   const bool narrow = g.N <= 512;  // router-sized outputs: 64 columns per block
   if (block_rows == 64) {
     if (epi == EPI_SWIGLU) return launch_fast<EPI_SWIGLU, 4, 2, MOE_NS_SMALL>(g, s);

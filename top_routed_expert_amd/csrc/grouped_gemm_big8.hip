@@ -366,6 +366,9 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
           fd[n] = sd[sc];
         }
       }
+      // routed rows in the 16-bit format (the item's rows are all on one side of out16_rows)
+      const bool half = p.out16 != nullptr && t.row0 < p.out16_rows;
+      const int64_t row_shift = p.out16 != nullptr ? p.out16_rows : 0;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
 #pragma unroll
@@ -382,7 +385,27 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
           float4 v = *(const float4*)&wbuf[rr16 * 64 + (c4 ^ (((rr16 >> 2) & 3) << 4))];
           const int64_t r = (int64_t)t.row0 + wm * 128 + m * 16 + rr16;
           const int col = col0 + c4;
-          if (r < t.row1 && col < p.N) {
+          if (half) {
+            // the row's 64-column maximum over its 16 lanes (one DPP row), then its exponent
+            float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+            a = fmaxf(a, __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)__float_as_uint(a), (int)__float_as_uint(a), 0xb1, 0xf, 0xf, false)));
+            a = fmaxf(a, __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)__float_as_uint(a), (int)__float_as_uint(a), 0x4e, 0xf, 0xf, false)));
+            a = fmaxf(a, __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)__float_as_uint(a), (int)__float_as_uint(a), 0x141, 0xf, 0xf, false)));
+            a = fmaxf(a, __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)__float_as_uint(a), (int)__float_as_uint(a), 0x140, 0xf, 0xf, false)));
+            int e = (int)((__float_as_uint(a) >> 23) & 255u);
+            e = e < EXP16_MIN ? EXP16_MIN : e;
+            const float sc = ldexpf(1.f, EXP16_BIAS - e);  // exact power of two
+            const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.x * sc)) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.y * sc)) << 16);
+            const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.z * sc)) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.w * sc)) << 16);
+            if (r < t.row1 && col < p.N) {
+              // read once, by the combine: non-temporal
+              typedef uint32_t u32x2_st __attribute__((ext_vector_type(2)));
+              __builtin_nontemporal_store(u32x2_st{lo, hi}, (u32x2_st*)&p.out16[r * p.ldo + col]);
+              if ((lane & 15) == 0) p.out16_exp[r * (p.ldo >> 6) + (col0 >> 6)] = (uint8_t)e;
+            }
+          } else if (r < t.row1 && col < p.N) {
             if (p.bias) {
               v.x += p.bias[col];
               v.y += p.bias[col + 1];
@@ -391,7 +414,8 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
             }
             // read once, by the combine: non-temporal, so it does not displace operands in L2
             typedef float f32x4_st __attribute__((ext_vector_type(4)));
-            __builtin_nontemporal_store(f32x4_st{v.x, v.y, v.z, v.w}, (f32x4_st*)&((float*)p.out)[r * p.ldo + col]);
+            __builtin_nontemporal_store(f32x4_st{v.x, v.y, v.z, v.w},
+                                        (f32x4_st*)&((float*)p.out)[(r - row_shift) * p.ldo + col]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -567,6 +591,7 @@ hipError_t launch_grouped_gemm_big8(int epi, const GemmArgs& g, hipStream_t s) {
   if (g.Kdim % B8_AKS || g.Kdim < 2 * B8_AKS) return hipErrorInvalidValue;
   if ((uint64_t)g.n_a_rows * (uint64_t)g.Kdim / 8u > 0xffffffffull) return hipErrorInvalidValue;
   if (g.N % 8 || g.ldo % 8) return hipErrorInvalidValue;
+  if (g.out16 && (epi != EPI_F32 || g.N % 64 || g.ldo != g.N || !g.out16_exp)) return hipErrorInvalidValue;
   int cus = 0;
   const hipError_t ce = stream_cus(s, &cus);
   if (ce != hipSuccess) return ce;

@@ -126,7 +126,22 @@ struct GemmArgs {
   const float* bias;      // EPI_F32: per-column bias or NULL
   int32_t ksplit;         // EPI_F32 only: the contraction is cut into ksplit slices;
   int64_t slice_stride;   //   slice s writes its partial sums to out + s*slice_stride
+  // EPI_F32, 256x256 kernel only (out16 != NULL): rows r < out16_rows are stored as fp16 in
+  // out16 [out16_rows, ldo] with one exponent byte per 64 columns in out16_exp
+  // [out16_rows, ldo/64] (the 16-bit expert-output format, below); rows r >= out16_rows go to
+  // `out` (fp32) at row r - out16_rows. Needs N % 64 == 0 and ldo == N.
+  uint16_t* out16;
+  uint8_t* out16_exp;
+  int64_t out16_rows;
 };
+
+// 16-bit expert-output format. A row's 64-column chunk c holds fp16 values
+// q = fp16_rne(y * 2^(141 - e)) and one byte e = max(14, biased fp32 exponent of
+// max |y| over the chunk), so the chunk's largest magnitude lands in [2^14, 2^15)
+// and no value overflows fp16; y = q * 2^(e - 141) up to fp16 rounding (2^-11
+// relative). EXP16_BIAS is that 141.
+constexpr int EXP16_BIAS = 141;
+constexpr int EXP16_MIN = 14;
 
 // Per-column scales of group g (fp8 weights).
 __device__ __forceinline__ const float* group_scale(const GemmArgs& p, const float* main, const float* extra, int g) {
@@ -198,5 +213,9 @@ hipError_t launch_quant_fp8(const bf16_t* src, int64_t n_mats, int64_t rows, int
 hipError_t launch_combine(int out_dtype, int64_t T, int D, int K, const float* y_perm, int64_t n_perm_rows,
                           const int32_t* dest, const float* prob, const float* y_shared, void* out,
                           hipStream_t s);
+// The same combine with the routed rows in the 16-bit expert-output format (D % 64 == 0).
+hipError_t launch_combine16(int out_dtype, int64_t T, int D, int K, const uint16_t* y16, const uint8_t* y16_exp,
+                            int64_t n_perm_rows, const int32_t* dest, const float* prob, const float* y_shared,
+                            void* out, hipStream_t s);
 
 }  // namespace moe
