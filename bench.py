@@ -96,6 +96,15 @@ def parse():
                     help="weight layout the timed steps read (bf16 layers; converted once before timing)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 1 GiB device-to-device copy: the known-size reference for HBM byte counters")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write the markdown summary of a rocprofv3 --kernel-trace --stats run (csv, -o run) in DIR "
+                         "to --out, with --title and --command; no GPU needed")
+    ap.add_argument("--summarize-pmc", metavar="DIR",
+                    help="write the gate/up HBM traffic summary from rocprofv3 --pmc runs in DIR/pmc_<workload>_"
+                         "<FETCH_SIZE|WRITE_SIZE> (csv, -o run) to --out; no GPU needed")
+    ap.add_argument("--out")
+    ap.add_argument("--title", default="")
+    ap.add_argument("--command", default="")
     return ap.parse_args()
 
 
@@ -526,8 +535,133 @@ def cpu_baseline(L, decode_tokens: int, prefill_tokens: int) -> dict:
                 prefill=dict(value=r_p["value"], unit="tokens/s", sample=r_p["sample"]))
 
 
+# ---------------------------------------------------------- profile summaries ---
+
+def _short_kernel(n: str) -> str:
+    import re
+    n = re.sub(r"\(anonymous namespace\)::", "", n).replace("void ", "")
+    return n.split("(")[0]
+
+
+def summarize_trace(d: str, title: str, command: str, out: str) -> None:
+    """Markdown summary of a kernel-trace run: per (kernel, grid) average and minimum duration."""
+    import collections
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(d, "run_kernel_trace.csv"))))
+    agg = collections.OrderedDict()
+    for r in rows:
+        if "moe::" not in r["Kernel_Name"]:
+            continue
+        gx = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
+        gy = int(r["Grid_Size_Y"]) // int(r["Workgroup_Size_Y"])
+        k = (_short_kernel(r["Kernel_Name"]), f"{gx} x {gy}")
+        agg.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000)
+    L = [f"# {title}\n", "Command (repo root, one MI355X, `TMPDIR=/tmp`):\n", "```", command, "```\n",
+         "Durations per dispatch from the kernel trace, grouped by kernel and grid (blocks x slices). "
+         "Written by `python bench.py --summarize-trace <dir>`.\n",
+         "| kernel | grid (blocks x y) | calls | avg us | min us |", "|---|---|---|---|---|"]
+    for (n, g), v in agg.items():
+        L.append(f"| `{n}` | {g} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} |")
+    st = list(csv.DictReader(open(os.path.join(d, "run_kernel_stats.csv"))))
+    L += ["", "rocprofv3 --stats totals of the library's kernels over the whole run:", "",
+          "| kernel | calls | total ms | avg us |", "|---|---|---|---|"]
+    for r in st:
+        if "moe::" in r["Name"]:
+            L.append(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {int(r['TotalDurationNs']) / 1e6:.3f} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} |")
+    open(out, "w").write("\n".join(L) + "\n")
+
+
+PMC_WORKLOADS = ("decode", "prefill", "skew", "full")
+
+
+def summarize_pmc(d: str, out: str) -> None:
+    """Gate/up HBM traffic per launch from FETCH_SIZE / WRITE_SIZE runs, each counter scaled by what it
+    reads for the run's 1 GiB device copy (bench.py --copy-calibration), against the algorithmic bytes."""
+    import collections
+    import csv
+
+    import synth
+
+    def load(w, c):
+        agg = collections.OrderedDict()
+        for r in csv.DictReader(open(os.path.join(d, f"pmc_{w}_{c}", "run_counter_collection.csv"))):
+            if r["Counter_Name"] == c:
+                agg.setdefault((r["Kernel_Name"], int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+        return agg
+
+    L = ["# HBM traffic of the expert gate/up kernel (PMC), MI355X, packed weights\n",
+         "Commands (repo root), one counter per run, each under `timeout -s KILL 240`; summary written by "
+         f"`python bench.py --summarize-pmc <dir> --out {out}`:\n", "```"]
+    for w in PMC_WORKLOADS:
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            L.append(f"rocprofv3 --pmc {c} --output-format csv -d <dir>/pmc_{w}_{c} -o run -- python bench.py "
+                     f"--workload {w} --steps 3 --warmup 1 --no-cpu-baseline --no-secondary --copy-calibration "
+                     f"> <dir>/pmc_{w}_{c}/bench.log")
+    L += ["```\n",
+          "`--copy-calibration` copies 1 GiB device to device first (`__amd_rocclr_copyBuffer`, grid 131072), a "
+          "kernel of known traffic: 1048576 KiB read and 1048576 KiB written. Each counter is scaled by "
+          "1048576 / (its value for that copy), then x 1024 to bytes. The gate/up kernel is the one with the "
+          "most FETCH_SIZE per dispatch among the expert gate/up launches (the layer's own and the standalone "
+          "one are the same kernel and grid). Per dispatch, in KiB:\n",
+          "| workload | gate/up kernel | FETCH (copy) | FETCH (kernel) | WRITE (copy) | WRITE (kernel) | dispatches |",
+          "|---|---|---|---|---|---|---|"]
+    lines, other = [], []
+    for w in PMC_WORKLOADS:
+        f, wr = load(w, "FETCH_SIZE"), load(w, "WRITE_SIZE")
+        ck = [k for k in f if k[0] == "__amd_rocclr_copyBuffer" and k[1] == 131072]
+        cf, cw = f[ck[0]][0], wr[ck[0]][0]
+        ff, fw = 1048576.0 / cf, 1048576.0 / cw
+        # the gate/up launch: EPI_SWIGLU (template argument 0) of the expert GEMMs
+        gu = [k for k in f if ("gemm_bf16_big8<0" in k[0] or "gemm_bf16_mfma<0" in k[0])]
+        key = max(gu, key=lambda k: sum(f[k]) / len(f[k]))
+        fv = sum(f[key]) / len(f[key])
+        wv = sum(wr.get(key, [0.0])) / max(1, len(wr.get(key, [0.0])))
+        L.append(f"| {w} | `{_short_kernel(key[0])}` | {cf:.1f} | {fv:.1f} | {cw:.1f} | {wv:.1f} | {len(f[key])} |")
+        spec = synth.spec(w)
+        traffic = fv * ff * 1024 + wv * fw * 1024
+        lines.append((w, traffic, key))
+        for k in f:
+            if "moe::" not in k[0] or "pack_kernel" in k[0] or k == key:
+                continue
+            fb = sum(f[k]) / len(f[k]) * ff * 1024
+            wb = sum(wr.get(k, [0.0])) / max(1, len(wr.get(k, [0.0]))) * fw * 1024
+            if fb + wb >= 1e6:
+                other.append(f"- {w}: `{_short_kernel(k[0])}` (grid {k[1]}): {fb / 1e9:.3f} GB fetched, "
+                             f"{wb / 1e9:.3f} GB written")
+    L.append("")
+    for w, t, _ in lines:
+        L.append(f"traffic_bytes[{w}]: {int(t)}")
+    L.append("")
+    L.append("Against the algorithmic bytes of the same launch (touched experts' gate and up weights, the token "
+             "rows once, the SwiGLU output: `roofline.algorithmic_bytes` of the bench line each run printed to "
+             "`<dir>/pmc_<workload>_FETCH_SIZE/bench.log`):\n")
+    for w, t, _ in lines:
+        log = os.path.join(d, f"pmc_{w}_FETCH_SIZE", "bench.log")
+        alg = None
+        if os.path.exists(log):
+            for ln in open(log).read().splitlines()[::-1]:
+                if ln.startswith("{"):
+                    alg = json.loads(ln)["roofline"]["algorithmic_bytes"]
+                    break
+        if alg:
+            L.append(f"- {w}: {t / 1e9:.3f} GB measured vs {alg / 1e9:.3f} GB algorithmic ({t / alg:.3f}x)")
+    L.append("")
+    L.append("Other kernels in the same runs (per launch, scaled):\n")
+    L += other
+    L += ["", "Kernel sources these counters belong to (bench.py reports the traffic only while they hash the same):",
+          "", f"source_sha256: {kernel_source_hash()}"]
+    open(out, "w").write("\n".join(L) + "\n")
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.title, args.command, args.out)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.out)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)

@@ -54,6 +54,7 @@ template <class K, class A> void emul_launch(K kernel, unsigned blocks, unsigned
 #include "emul_pack.cpp"
 #include "emul_permute.cpp"
 #include "emul_route.cpp"
+#include "emul_router.cpp"
 
 template <class T> T* buffer(size_t n) {  // exact size: ASan sees any access past its end
   T* p = (T*)malloc(n ? n * sizeof(T) : 1);

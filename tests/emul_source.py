@@ -21,7 +21,8 @@ EMUL = os.path.join(ROOT, "tests", "emul")
 # (the fp8 quantiser's row maximum goes through LDS too, but only into values, not addresses:
 # it runs lane by lane, as the GEMMs do)
 SYNC_KERNELS = {"build_tiles_kernel", "permute_rank_kernel", "permute_place_kernel", "permute_small_kernel",
-                "ep_plan_kernel", "topk_kernel", "group_stats_kernel", "combine_kernel", "gemm_generic"}
+                "ep_plan_kernel", "topk_kernel", "group_stats_kernel", "combine_kernel", "gemm_generic",
+                "router_topk_kernel"}
 
 
 def clang() -> str | None:
@@ -39,18 +40,29 @@ def internal_header() -> str:
     return read("moe_internal.h").replace("#include <hip/hip_runtime.h>", '#include "shim.h"')
 
 
-def big8_source(kernel_src: str) -> str:
-    """grouped_gemm_big8.hip for the host: asm LDS reads checked, asm waits dropped, launches emulated."""
-    s = kernel_src.replace('#include "moe_internal.h"', '#include "emul_internal.h"')
-    s, _ = re.subn(r"typedef __attribute__\(\(address_space\(3\)\)\) void (lds8?_void_t);", r"typedef void \1;", s)
-    s, k0 = re.subn(r"\(uint32_t\)\(uintptr_t\)\(lds8?_void_t\*\)&(\w+)\[0\]\[0\]",
-                    lambda m: f"emul_lds_base((void*)&{m.group(1)}, sizeof({m.group(1)}))", s)
-    s, k1 = re.subn(r'asm volatile\("ds_read_b128 %0, %1 offset:%2" : "=v"\(([^)]*)\) : "v"\((\w+)\), '
+def _asm_to_host(s: str) -> tuple:
+    """Inline asm of the LDS-staged kernels: LDS address spaces and bases, checked ds_read_b128 reads,
+    waits and barriers dropped. Returns the source and the number of reads rewritten."""
+    s, _ = re.subn(r"typedef __attribute__\(\(address_space\(3\)\)\) void (\w+);", r"typedef void \1;", s)
+    s, _ = re.subn(r"\(uint32_t\)\(uintptr_t\)\(\w+\*\)&(\w+)\[0\]\[0\]",
+                   lambda m: f"emul_lds_base((void*)&{m.group(1)}, sizeof({m.group(1)}))", s)
+    s, _ = re.subn(r"\(uint32_t\)\(uintptr_t\)\(\w+\*\)&(\w+)\[0\]",
+                   lambda m: f"emul_lds_base((void*)&{m.group(1)}, sizeof({m.group(1)}))", s)
+    s, k1 = re.subn(r'asm volatile\("ds_read_b128 %0, %1 offset:%2" : "=v"\(([^)]*\]?)\) : "v"\((\w+)\), '
                     r'"n"\(([^)]*)\)\);',
                     lambda m: (f"{m.group(1)} = emul_ds_read<std::remove_reference_t<decltype({m.group(1)})>>"
                                f"({m.group(2)} + ({m.group(3)}));"), s)
     s, _ = re.subn(r'asm volatile\("s_waitcnt lgkmcnt\(%1\)" : "\+v"\([^)]*\) : "n"\([^)]*\)\);', ";", s)
+    s, _ = re.subn(r'asm volatile\("s_waitcnt lgkmcnt\(\d+\)"(?: : "\+v"\([^;]*?\))+\);', ";", s, flags=re.S)
     s, _ = re.subn(r'asm volatile\("[^"]*" ::: "memory"\);', ";", s)
+    return s, k1
+
+
+def big8_source(kernel_src: str) -> str:
+    """grouped_gemm_big8.hip for the host: asm LDS reads checked, asm waits dropped, launches emulated."""
+    s = kernel_src.replace('#include "moe_internal.h"', '#include "emul_internal.h"')
+    k0 = s.count("(uint32_t)(uintptr_t)(lds8_void_t*)&")
+    s, k1 = _asm_to_host(s)
     s, k4 = re.subn(r"(gemm_bf16_big8?<[^>]*>)<<<\(unsigned\)blocks, (256|512), 0, s>>>\(g\);",
                     lambda m: f"emul_launch({m.group(1)}, (unsigned)blocks, {m.group(2)}, g);", s)
     left = re.findall(r"asm volatile.*|<<<.*>>>", s)
@@ -77,6 +89,7 @@ def _kernel_name_start(s: str, i: int) -> int:
 def launches_source(src: str) -> str:
     """A kernel source whose launches `k<<<grid, threads, shm, stream>>>(args)` all go through the runner."""
     s = src.replace('#include "moe_internal.h"', '#include "emul_internal.h"')
+    s, _ = _asm_to_host(s)
     n = 0
     while True:
         i = s.find("<<<")
@@ -99,7 +112,7 @@ def launches_source(src: str) -> str:
         sync = "true" if name.split("<")[0] in SYNC_KERNELS else "false"
         s = s[:start] + f"emul_run({sync}, {name}, emul_grid({cfg[0]}), {cfg[1]}, {s[k + 1:e]})" + s[e + 1:]
         n += 1
-    assert n >= 1 and "asm" not in s, n
+    assert n >= 1 and "asm volatile" not in s, n
     return s
 
 
@@ -117,6 +130,7 @@ def write_tree(d, big8_src: str | None = None) -> None:
     open(os.path.join(d, "emul_gemm.cpp"), "w").write(launches_source(read("grouped_gemm.hip")))
     open(os.path.join(d, "emul_permute.cpp"), "w").write(launches_source(read("permute.hip")))
     open(os.path.join(d, "emul_route.cpp"), "w").write(launches_source(read("route.hip")))
+    open(os.path.join(d, "emul_router.cpp"), "w").write(launches_source(read("router.hip")))
     open(os.path.join(d, "emul_combine.cpp"), "w").write(launches_source(read("combine.hip")))
     open(os.path.join(d, "emul_pack.cpp"), "w").write(launches_source(read("pack.hip")))
     open(os.path.join(d, "emul_api.cpp"), "w").write(api_source())

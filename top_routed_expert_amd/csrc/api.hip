@@ -215,6 +215,13 @@ moe_status run_route(const moe_config* c, int64_t T, const void* x, const void* 
                      const int32_t* k_tok, int32_t* idx, float* prob, float* gap, const RouteWs& ws, hipStream_t s,
                      float* gmass = nullptr, int G = 0) {
   const bool fast = fast_path(c->dtype, c->d_model, 64);
+  // many tokens: linear layer, softmax and top-K in one kernel
+  if (fast && gmass == nullptr && router_topk_fits(T, c->d_model, c->n_experts, c->top_k)) {
+    MOE_TRY_HIP(launch_router_topk((const bf16_t*)x, T, c->d_model, (const bf16_t*)w_router, packed(c), bias,
+                                   c->n_experts, c->top_k, k_tok, idx, prob, gap, s),
+                "router");
+    return MOE_OK;
+  }
   GemmArgs g{};
   g.a = x;
   g.n_a_rows = T;

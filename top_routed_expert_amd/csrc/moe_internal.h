@@ -165,6 +165,15 @@ hipError_t launch_grouped_gemm(int dtype, bool fast, int epi, int block_rows, co
 // waves, bf16 or fp8 weights).
 hipError_t launch_grouped_gemm_big8(int epi, const GemmArgs& g, hipStream_t s);
 
+// router.hip: linear layer, softmax and top-K in one kernel, 32 tokens per
+// block (bf16, router row-major or packed with the same results, T > 64,
+// E <= 320, d_model a multiple of 64 and at least 128); k_tok and gap as
+// launch_topk.
+bool router_topk_fits(int64_t T, int D, int E, int K);
+hipError_t launch_router_topk(const bf16_t* x, int64_t T, int D, const bf16_t* w_router, bool packed,
+                              const float* bias, int E, int K, const int32_t* k_tok, int32_t* idx, float* prob,
+                              float* gap, hipStream_t s);
+
 // route.hip
 // Logits are the sum of nsplit partial arrays [nsplit][T][E], added in slice order.
 // k_tok (optional): token t keeps its first k_tok[t] (clamped to [0, K])
