@@ -216,9 +216,9 @@ moe_status run_route(const moe_config* c, int64_t T, const void* x, const void* 
                      float* gmass = nullptr, int G = 0) {
   const bool fast = fast_path(c->dtype, c->d_model, 64);
   // many tokens: linear layer, softmax and top-K in one kernel
-  if (fast && gmass == nullptr && router_topk_fits(T, c->d_model, c->n_experts, c->top_k)) {
+  if (fast && router_topk_fits(T, c->d_model, c->n_experts, c->top_k)) {
     MOE_TRY_HIP(launch_router_topk((const bf16_t*)x, T, c->d_model, (const bf16_t*)w_router, packed(c), bias,
-                                   c->n_experts, c->top_k, k_tok, idx, prob, gap, s),
+                                   c->n_experts, c->top_k, k_tok, idx, prob, gap, gmass, G, s),
                 "router");
     return MOE_OK;
   }
@@ -501,7 +501,7 @@ moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx
   const PermuteWs w = carve_permute(a, cfg, T);
   hipStream_t s = (hipStream_t)stream;
   MOE_TRY_HIP(launch_permute(topk_idx, T, cfg->top_k, cfg->n_experts, w.rank, w.counts, offsets, sorted_token, dest,
-                             nullptr, 0, s),
+                             nullptr, 0, nullptr, nullptr, 0, 0, s),
               "permute");
   if (x_perm)
     MOE_TRY_HIP(launch_gather_rows(x, T, cfg->d_model, (int)elem_bytes(cfg->dtype), sorted_token, T * cfg->top_k,
@@ -636,9 +636,10 @@ moe_status moe_layer_forward_dynamic(const moe_config* cfg, int64_t T, const voi
                                      L.ffn.sched.tiles, L.ffn.sched.n_tiles, L.ffn.sched.max_tiles,
                                      L.ffn.sched.block_rows, s),
                 "permute");
-  } else {
+  } else {  // the place kernel writes the tile table too
     MOE_TRY_HIP(launch_permute(idx, T, K, E, L.perm.rank, L.perm.counts, offsets_out, L.sorted_token, L.dest,
-                               L.offsets_ext, extra, s),
+                               L.offsets_ext, extra, L.ffn.sched.tiles, L.ffn.sched.n_tiles, L.ffn.sched.max_tiles,
+                               L.ffn.sched.block_rows, s),
                 "permute");
   }
   // 3. expert FFNs: routed segments (rows gathered through sorted_token) and,
@@ -650,7 +651,7 @@ moe_status moe_layer_forward_dynamic(const moe_config* cfg, int64_t T, const voi
   //    (with y16, routed rows below T*K in the 16-bit format, shared rows to y_shared)
   MOE_TRY(run_ffn(cfg, n_groups, E, P + extra, L.offsets_ext, x, T, L.sorted_token, P, w->w_gate, w->w_up,
                   w->w_down, w->s_gate, w->s_up, w->s_down, cfg->d_expert, L.y16 ? L.y_shared : L.y, L.ffn, s,
-                  small, L.fused_shared ? E : -1, sc, L.y16v, L.y16e, L.y16 ? P : 0));
+                  true, L.fused_shared ? E : -1, sc, L.y16v, L.y16e, L.y16 ? P : 0));
   if (cfg->d_shared > 0 && !L.fused_shared) {
     const float* sc_shared[6] = {w->s_gate_scale, w->s_up_scale, w->s_down_scale, nullptr, nullptr, nullptr};
     MOE_TRY(run_ffn(cfg, 1, 1, T, nullptr, x, T, nullptr, 0, w->s_gate, w->s_up, w->s_down, nullptr, nullptr,

@@ -167,12 +167,12 @@ hipError_t launch_grouped_gemm_big8(int epi, const GemmArgs& g, hipStream_t s);
 
 // router.hip: linear layer, softmax and top-K in one kernel, 32 tokens per
 // block (bf16, router row-major or packed with the same results, T > 64,
-// E <= 320, d_model a multiple of 64 and at least 128); k_tok and gap as
-// launch_topk.
+// E <= 320, d_model a multiple of 64 and at least 128); k_tok, gap and gmass
+// as launch_topk.
 bool router_topk_fits(int64_t T, int D, int E, int K);
 hipError_t launch_router_topk(const bf16_t* x, int64_t T, int D, const bf16_t* w_router, bool packed,
                               const float* bias, int E, int K, const int32_t* k_tok, int32_t* idx, float* prob,
-                              float* gap, hipStream_t s);
+                              float* gap, float* gmass, int G, hipStream_t s);
 
 // route.hip
 // Logits are the sum of nsplit partial arrays [nsplit][T][E], added in slice order.
@@ -192,9 +192,12 @@ hipError_t launch_group_stats(const float* gmass, const int32_t* idx, int64_t T,
 // the E routed segments (ending at the valid pair count V), then [V, T*K)
 // (rows of pairs without an expert: no tiles), then the extra_rows rows
 // from T*K on (the shared expert).
+// tiles (optional): also the expert GEMMs' tile table over the groups of
+// offsets_ext, as launch_permute_small writes it (E <= 1023).
 hipError_t launch_permute(const int32_t* idx, int64_t T, int K, int E, int32_t* rank, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_token, int32_t* dest,
-                          int32_t* offsets_ext, int32_t extra_rows, hipStream_t s);
+                          int32_t* offsets_ext, int32_t extra_rows, Tile* tiles, int32_t* n_tiles,
+                          int32_t max_tiles, int block_rows, hipStream_t s);
 bool permute_small_fits(int64_t T, int K, int E);
 // Single-block permutation for small batches; also writes the tile table of
 // the expert GEMMs over the groups of offsets_ext (E, or E+2 with

@@ -6,11 +6,12 @@
 //   dest[j] = offsets[e] + #{ j' < j : idx[j'] == e },   e = idx[j]
 // which is stable and unique, so the result is independent of scheduling.
 //
-//  1. rank: one block per expert walks all pairs in order, a block-wide
-//     prefix sum of match flags per 4096-pair chunk giving each matching
-//     pair its rank; the total is the expert's count. No atomics.
+//  1. rank: one block of 1024 threads per expert walks all pairs in order, a
+//     block-wide prefix sum of match flags per 16384-pair chunk giving each
+//     matching pair its rank; the total is the expert's count. No atomics.
 //  2. place: every block rebuilds the exclusive scan of the E counts in LDS,
-//     then maps each pair to dest and writes sorted_token[dest] = t.
+//     then maps each pair to dest and writes sorted_token[dest] = t; block 0
+//     also writes the tile table of the expert GEMMs when asked.
 // Small batches take a single-block path that also builds the tile table of
 // the expert GEMMs (one launch instead of three).
 #include "moe_internal.h"
@@ -19,8 +20,9 @@ namespace moe {
 
 namespace {
 
-constexpr int PR_PER = 16;            // pairs per thread per chunk
-constexpr int PR_CHUNK = 256 * PR_PER;
+constexpr int PR_PER = 16;             // pairs per thread per chunk
+constexpr int PR_THREADS = 1024;       // threads of a rank block
+constexpr int PR_CHUNK = PR_THREADS * PR_PER;
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -31,9 +33,10 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-__global__ void __launch_bounds__(256) permute_rank_kernel(const int32_t* __restrict__ idx, int64_t P, int E,
-                                                           int32_t* __restrict__ rank, int32_t* __restrict__ counts) {
-  __shared__ int s_wave[4];
+__global__ void __launch_bounds__(PR_THREADS) permute_rank_kernel(const int32_t* __restrict__ idx, int64_t P, int E,
+                                                                  int32_t* __restrict__ rank,
+                                                                  int32_t* __restrict__ counts) {
+  __shared__ int s_wave[PR_THREADS / 64];
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int running = 0;
@@ -61,7 +64,7 @@ __global__ void __launch_bounds__(256) permute_rank_kernel(const int32_t* __rest
     __syncthreads();
     int before = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < PR_THREADS / 64; ++w) {
       before += w < wave ? s_wave[w] : 0;
       total += s_wave[w];
     }
@@ -81,7 +84,9 @@ __global__ void __launch_bounds__(256) permute_place_kernel(const int32_t* __res
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ sorted_token,
                                                             int32_t* __restrict__ dest,
-                                                            int32_t* __restrict__ offsets_ext, int32_t extra_rows) {
+                                                            int32_t* __restrict__ offsets_ext, int32_t extra_rows,
+                                                            Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+                                                            int32_t max_tiles, int BM) {
   __shared__ int s_off[1025];
   __shared__ int s_wave[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -114,6 +119,44 @@ __global__ void __launch_bounds__(256) permute_place_kernel(const int32_t* __res
     if (offsets_ext && tid == 0) {  // rows of pairs without an expert, then the extra rows
       offsets_ext[E + 1] = (int32_t)P;
       offsets_ext[E + 2] = (int32_t)P + extra_rows;
+    }
+    if (tiles) {
+      // the expert GEMMs' tile table over the E routed segments and, with
+      // extra_rows, group E (rows of pairs without an expert: no tiles) and
+      // group E+1 (the extra rows): thread tid owns groups 4*tid .. 4*tid+3,
+      // thread 255 also group E+1
+      int g0[5], g1[5], nt[5], mine = 0;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const int g = i < 4 ? 4 * tid + i : E + 1;
+        g0[i] = g1[i] = 0;
+        if (i < 4 && g < E) {
+          g0[i] = s_off[g];
+          g1[i] = s_off[g + 1];
+        } else if (i == 4 && tid == 255 && extra_rows > 0) {
+          g0[i] = (int)P;
+          g1[i] = (int)P + extra_rows;
+        }
+        nt[i] = (g1[i] - g0[i] + BM - 1) / BM;
+        mine += nt[i];
+      }
+      __syncthreads();  // s_wave is reused
+      const int incl2 = wave_incl_scan(mine, lane);
+      if (lane == 63) s_wave[wave] = incl2;
+      __syncthreads();
+      int slot = incl2 - mine, n_all = 0;
+      for (int w = 0; w < 4; ++w) {
+        slot += w < wave ? s_wave[w] : 0;
+        n_all += s_wave[w];
+      }
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const int g = i < 4 ? 4 * tid + i : E + 1;
+        const int first = slot;
+        for (int row = g0[i]; row < g1[i]; row += BM, ++slot)
+          if (slot < max_tiles) tiles[slot] = Tile{g, row, row + BM < g1[i] ? row + BM : g1[i], first, nt[i], 0, 0, 0};
+      }
+      if (tid == 0) *n_tiles = n_all < max_tiles ? n_all : max_tiles;
     }
   }
   for (int64_t j = (int64_t)blockIdx.x * 256 + tid; j < P; j += (int64_t)gridDim.x * 256) {
@@ -315,15 +358,17 @@ hipError_t launch_permute_small(const int32_t* idx, int64_t T, int K, int E, int
 
 hipError_t launch_permute(const int32_t* idx, int64_t T, int K, int E, int32_t* rank, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_token, int32_t* dest, int32_t* offsets_ext,
-                          int32_t extra_rows, hipStream_t s) {
+                          int32_t extra_rows, Tile* tiles, int32_t* n_tiles, int32_t max_tiles, int block_rows,
+                          hipStream_t s) {
   const int64_t P = T * K;
-  permute_rank_kernel<<<E, 256, 0, s>>>(idx, P, E, rank, counts);
+  permute_rank_kernel<<<E, PR_THREADS, 0, s>>>(idx, P, E, rank, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   int64_t blocks = (P + 255) / 256;
   blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
   permute_place_kernel<<<(unsigned)blocks, 256, 0, s>>>(idx, P, K, E, rank, counts, offsets, sorted_token, dest,
-                                                        offsets_ext, extra_rows);
+                                                        offsets_ext, extra_rows, tiles, n_tiles, max_tiles,
+                                                        block_rows);
   return hipGetLastError();
 }
 

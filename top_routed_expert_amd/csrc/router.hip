@@ -106,7 +106,8 @@ __global__ void __launch_bounds__(256) router_topk_kernel(const bf16_t* __restri
                                                           const float* __restrict__ bias, int E, int K,
                                                           const int32_t* __restrict__ k_tok,
                                                           int32_t* __restrict__ idx, float* __restrict__ prob,
-                                                          float* __restrict__ gap) {
+                                                          float* __restrict__ gap, float* __restrict__ gmass,
+                                                          int G) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[RT_NS * RT_STAGE];  // the epilogue's logits reuse it
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t row0 = (int64_t)blockIdx.x * RT_ROWS;
@@ -246,6 +247,22 @@ __global__ void __launch_bounds__(256) router_topk_kernel(const bf16_t* __restri
       sum += v[i];
     }
     sum = row_sum16(sum);
+    // optional: the token's routing probability mass per expert group (G equal
+    // contiguous groups), for the expert-parallel balance statistics
+    if (gmass) {
+      const int gs = E / G;
+#pragma unroll 1
+      for (int g = 0; g < G; ++g) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < RT_VPL; ++i) {
+          const int e = j16 + 16 * i;
+          if (e < E && e / gs == g) a += v[i] / sum;
+        }
+        a = row_sum16(a);
+        if (real && j16 == 0) gmass[t * G + g] = a;
+      }
+    }
     unsigned long long key[RT_VPL];
 #pragma unroll
     for (int i = 0; i < RT_VPL; ++i) {
@@ -300,14 +317,17 @@ bool router_topk_fits(int64_t T, int D, int E, int K) {
 
 hipError_t launch_router_topk(const bf16_t* x, int64_t T, int D, const bf16_t* w_router, bool packed,
                               const float* bias, int E, int K, const int32_t* k_tok, int32_t* idx, float* prob,
-                              float* gap, hipStream_t s) {
+                              float* gap, float* gmass, int G, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (E > RT_NCT * 16 || K > E || D % RT_KS || D < 2 * RT_KS) return hipErrorInvalidValue;
+  if (gmass && (G < 1 || E % G)) return hipErrorInvalidValue;
   const int64_t blocks = (T + RT_ROWS - 1) / RT_ROWS;
   if (packed)
-    router_topk_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(x, T, D, w_router, bias, E, K, k_tok, idx, prob, gap);
+    router_topk_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(x, T, D, w_router, bias, E, K, k_tok, idx, prob, gap,
+                                                              gmass, G);
   else
-    router_topk_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(x, T, D, w_router, bias, E, K, k_tok, idx, prob, gap);
+    router_topk_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(x, T, D, w_router, bias, E, K, k_tok, idx, prob, gap,
+                                                               gmass, G);
   return hipGetLastError();
 }
 
