@@ -117,8 +117,9 @@ def compare_routing(idx_gpu, prob_gpu, ref, x, w_router) -> dict:
                 bound_use=float(np.max(dp / np.where(bound > 0, bound, 1.0))) if dp.size else 0.0)
 
 
-def check_near_ties(idx_gpu, prob_gpu, ref, x, w_router, K: int) -> np.ndarray:
-    """Validity of the GPU's routing of the near-tie tokens (see the module notes); returns those tokens."""
+def check_near_ties(idx_gpu, prob_gpu, ref, x, w_router, K: int, k_per_token=None) -> np.ndarray:
+    """Validity of the GPU's routing of the near-tie tokens (see the module notes); returns those tokens.
+    With k_per_token, token t's set is its first k_t = clip(k_t, 0, K) slots, the rest holding -1."""
     tie = np.nonzero(ref["gap"] < NEAR_TIE)[0]
     if tie.size == 0:
         return tie
@@ -129,25 +130,29 @@ def check_near_ties(idx_gpu, prob_gpu, ref, x, w_router, K: int) -> np.ndarray:
     ig = np.asarray(idx_gpu)[tie].astype(np.int64)
     pg = np.asarray(prob_gpu, dtype=np.float64)[tie]
     E = p.shape[1]
+    kt = np.full(len(tie), K) if k_per_token is None else np.clip(np.asarray(k_per_token)[tie], 0, K)
     for i, t in enumerate(tie):
-        chosen = ig[i]
-        assert np.all((chosen >= 0) & (chosen < E)) and len(set(chosen.tolist())) == K, \
-            f"near-tie token {t}: ids {chosen} are not {K} distinct experts"
+        n = int(kt[i])
+        chosen = ig[i][:n]
+        assert np.all(ig[i][n:] == -1), f"near-tie token {t}: slots past its {n} experts hold ids"
+        assert np.all((chosen >= 0) & (chosen < E)) and len(set(chosen.tolist())) == n, \
+            f"near-tie token {t}: ids {chosen} are not {n} distinct experts"
         mask = np.zeros(E, dtype=bool)
         mask[chosen] = True
-        low = float(np.min((p[i] + b[i])[mask]))
+        low = float(np.min((p[i] + b[i])[mask])) if n else np.inf
         high = float(np.max((p[i] - b[i])[~mask])) if (~mask).any() else -np.inf
-        assert low >= high, f"near-tie token {t}: chosen {chosen} is not a top-{K} set within the bound " \
+        assert low >= high, f"near-tie token {t}: chosen {chosen} is not a top-{n} set within the bound " \
                             f"({low:.9g} < {high:.9g})"
-        assert np.all(np.abs(pg[i] - p[i][chosen]) <= b[i][chosen]), f"near-tie token {t}: probabilities off"
-        assert np.all(np.diff(pg[i]) <= 0), f"near-tie token {t}: probabilities not in descending order"
+        assert np.all(np.abs(pg[i][:n] - p[i][chosen]) <= b[i][chosen]), f"near-tie token {t}: probabilities off"
+        assert np.all(np.diff(pg[i][:n]) <= 0), f"near-tie token {t}: probabilities not in descending order"
     return tie
 
 
 def near_tie_reference(x, W, tie, idx_gpu, ref) -> np.ndarray:
     """The oracle's output rows of the near-tie tokens, recomputed with the GPU's ids and the oracle's p of them."""
     ig = np.asarray(idx_gpu)[tie].astype(np.int64)
-    return O.rows_output(x, W, tie, ig, np.take_along_axis(ref["p32"][tie].astype(np.float64), ig, axis=1))
+    pr = np.take_along_axis(ref["p32"][tie].astype(np.float64), np.maximum(ig, 0), axis=1)
+    return O.rows_output(x, W, tie, ig, np.where(ig >= 0, pr, 0.0))
 
 
 def compare_rows(out_gpu_rows, out_ref_rows, rms: float, tol_rel: float, bf16: bool, what: str) -> float:
