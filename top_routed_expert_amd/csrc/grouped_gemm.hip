@@ -311,10 +311,13 @@ __global__ void __launch_bounds__(256) gemm_bf16_mfma(GemmArgs p) {
 }
 
 // Generic grouped GEMM: 64x64 output tile, 16x16 threads with 4x4 outputs
-// each, contraction in chunks of 16 through LDS. TI is float or bf16_t.
+// each, contraction in chunks of 32 through LDS. The next chunk's operands
+// are loaded into registers before the current chunk is multiplied, so a
+// chunk's load latency overlaps the previous chunk's arithmetic (small
+// layers are latency-bound here). TI is float or bf16_t.
 template <typename TI, int EPI>
 __global__ void __launch_bounds__(256) gemm_generic(GemmArgs p) {
-  constexpr int BM = 64, BN = 64, BK = 16;
+  constexpr int BM = 64, BN = 64, BK = 32, PER = BM * BK / 256;
   constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
   __shared__ float sA[BK][BM + 1];
   __shared__ float sB[NB][BK][BN + 1];
@@ -330,34 +333,47 @@ __global__ void __launch_bounds__(256) gemm_generic(GemmArgs p) {
   B[0] = group_b<TI>(p, p.b0, p.b0_extra, t.group);
   if constexpr (NB == 2) B[1] = group_b<TI>(p, p.b1, p.b1_extra, t.group);
 
-  // Staging: element e = tid + 256*i is (row or column e / 16, contraction e % 16).
-  int64_t asrc[4];
+  // Staging: element e = tid + 256*i is (row or column e / 32, contraction e % 32).
+  const int kk = tid & (BK - 1);
+  int64_t asrc[PER];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t r = (int64_t)t.row0 + ((tid + 256 * i) >> 4);
+  for (int i = 0; i < PER; ++i) {
+    const int64_t r = (int64_t)t.row0 + ((tid + 256 * i) >> 5);
     asrc[i] = r < t.row1 ? source_row(p, r) : -1;
   }
+  float ra[PER], rb[NB][PER];
+  auto load = [&](int k0) {
+    const int k = k0 + kk;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int rc = (tid + 256 * i) >> 5, col = nb * BN + rc;
+      ra[i] = (asrc[i] >= 0 && k < p.Kdim) ? load_f32(A + asrc[i] * p.Kdim + k) : 0.f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        rb[b][i] = (col < p.N && k < p.Kdim) ? load_f32(B[b] + (int64_t)col * p.Kdim + k) : 0.f;
+    }
+  };
   float acc[NB][4][4] = {};
+  load(0);
   for (int k0 = 0; k0 < p.Kdim; k0 += BK) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + 256 * i, rc = e >> 4, kk = e & 15, k = k0 + kk;
-      sA[kk][rc] = (asrc[i] >= 0 && k < p.Kdim) ? load_f32(A + asrc[i] * p.Kdim + k) : 0.f;
-      const int col = nb * BN + rc;
+    for (int i = 0; i < PER; ++i) {
+      const int rc = (tid + 256 * i) >> 5;
+      sA[kk][rc] = ra[i];
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        sB[b][kk][rc] = (col < p.N && k < p.Kdim) ? load_f32(B[b] + (int64_t)col * p.Kdim + k) : 0.f;
+      for (int b = 0; b < NB; ++b) sB[b][kk][rc] = rb[b][i];
     }
     __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < BK; ++kk) {
+    if (k0 + BK < p.Kdim) load(k0 + BK);
+#pragma unroll 8
+    for (int c = 0; c < BK; ++c) {
       float a[4], bv[NB][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = sA[kk][ty * 4 + i];
+      for (int i = 0; i < 4; ++i) a[i] = sA[c][ty * 4 + i];
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bv[b][j] = sB[b][kk][tx * 4 + j];
+        for (int j = 0; j < 4; ++j) bv[b][j] = sB[b][c][tx * 4 + j];
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
