@@ -293,6 +293,16 @@ static int run_layer(int argc, char** argv) {
   if (wsb <= moe_noalloc_scratch_bytes())
     fails += check(moe_layer_forward_noalloc(&cfg, T, x, &w, out, idx, prob, offs, nullptr),
                    "moe_layer_forward_noalloc");
+  // balance statistics over G groups: the chosen pairs of all groups add up to T*K
+  const int G = E % 8 == 0 ? 8 : (E % 4 == 0 ? 4 : 1);
+  const size_t gsb = moe_route_group_stats_workspace_bytes(&cfg, T, G);
+  char* gws = buffer<char>(gsb);
+  double* stats = buffer<double>(2 * G);
+  fails += check(moe_route_group_stats(&cfg, T, x, w.w_router, bias, nullptr, G, idx, prob, stats, gws, gsb,
+                                       nullptr), "moe_route_group_stats");
+  double pairs = 0.0;
+  for (int g = 0; g < G; ++g) pairs += stats[G + g];
+  if (pairs != (double)T * K) { printf("  group pair counts add up to %.0f, expected %d\n", pairs, T * K); ++fails; }
   printf("  experts of token 0:");
   for (int k = 0; k < K; ++k) printf(" %d", idx[k]);
   printf("\n%s\n", fails ? "FAILED" : "all calls ok");

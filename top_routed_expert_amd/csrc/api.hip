@@ -673,6 +673,7 @@ size_t moe_route_group_stats_workspace_bytes(const moe_config* cfg, int64_t T, i
   Arena a(nullptr);
   carve_route(a, cfg, T);
   a.take<float>(T * n_groups);
+  a.take<double>(group_stats_partials(T, n_groups));
   return a.off;
 }
 
@@ -696,15 +697,16 @@ moe_status moe_route_group_stats(const moe_config* cfg, int64_t T, const void* x
     return fail(MOE_ERR_WORKSPACE, "moe_route_group_stats needs %zu workspace bytes, got %zu", need, ws_bytes);
   hipStream_t s = (hipStream_t)stream;
   if (T == 0) {  // no tokens: the statistics kernel writes zeros (it reads nothing)
-    MOE_TRY_HIP(launch_group_stats(nullptr, nullptr, 0, cfg->top_k, cfg->n_experts, n_groups, stats, s),
+    MOE_TRY_HIP(launch_group_stats(nullptr, nullptr, 0, cfg->top_k, cfg->n_experts, n_groups, nullptr, stats, s),
                 "group statistics");
     return ok();
   }
   Arena a(ws);
   const RouteWs w = carve_route(a, cfg, T);
   float* gmass = a.take<float>(T * n_groups);
+  double* part = a.take<double>(group_stats_partials(T, n_groups));
   MOE_TRY(run_route(cfg, T, x, w_router, bias, k_per_token, topk_idx, topk_prob, nullptr, w, s, gmass, n_groups));
-  MOE_TRY_HIP(launch_group_stats(gmass, topk_idx, T, cfg->top_k, cfg->n_experts, n_groups, stats, s),
+  MOE_TRY_HIP(launch_group_stats(gmass, topk_idx, T, cfg->top_k, cfg->n_experts, n_groups, part, stats, s),
               "group statistics");
   return ok();
 }

@@ -183,9 +183,11 @@ hipError_t launch_router_topk(const bf16_t* x, int64_t T, int D, const bf16_t* w
 hipError_t launch_topk(const float* logits, int nsplit, int64_t T, int E, int K, const int32_t* k_tok, int32_t* idx,
                        float* prob, float* gap, float* gmass, int G, hipStream_t s);
 // out [2G] fp64: per-group probability mass summed over tokens, then the
-// number of chosen pairs per group.
-hipError_t launch_group_stats(const float* gmass, const int32_t* idx, int64_t T, int K, int E, int G, double* out,
-                              hipStream_t s);
+// number of chosen pairs per group; part: group_stats_partials(T, G) fp64
+// values of scratch (per-chunk partial sums).
+int64_t group_stats_partials(int64_t T, int G);
+hipError_t launch_group_stats(const float* gmass, const int32_t* idx, int64_t T, int K, int E, int G, double* part,
+                              double* out, hipStream_t s);
 
 // permute.hip. Pairs with idx outside [0, E) get dest -1 and no row.
 // offsets_ext [E+3] (optional), the row groups of the fused expert launch:

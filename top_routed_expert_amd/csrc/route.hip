@@ -207,23 +207,17 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
 
 // Expert-parallel balance statistics (page "Step3.5 Flash 大模型技术深度解析",
 // section 3.2.3: 288 experts in G groups, one group per GPU; the balance
-// loss L_EP = G * sum_g f_g p_g). Block g sums, over all tokens in a fixed
-// order (thread i takes tokens i, i+256, ..., then a fixed-shape tree), the
-// group's probability mass gmass[t][g] and its number of chosen pairs, in
-// fp64: out[g] = sum_t p_g(t), out[G + g] = #{(t, k): idx[t,k] in group g}.
-__global__ void __launch_bounds__(256) group_stats_kernel(const float* __restrict__ gmass,
-                                                          const int32_t* __restrict__ idx, int64_t T, int K, int E,
-                                                          int G, double* __restrict__ out) {
-  __shared__ double s_m[256], s_c[256];
-  const int g = blockIdx.x, tid = threadIdx.x, gs = E / G;
-  double m = 0.0, c = 0.0;
-  for (int64_t t = tid; t < T; t += 256) {
-    m += (double)gmass[t * G + g];
-    for (int k = 0; k < K; ++k) {
-      const int e = idx[t * K + k];
-      c += (e >= 0 && e < E && e / gs == g) ? 1.0 : 0.0;
-    }
-  }
+// loss L_EP = G * sum_g f_g p_g): out[g] = sum_t p_g(t) (the group's
+// probability mass gmass[t][g]) and out[G + g] = #{(t, k): idx[t,k] in group
+// g}, in fp64. Two passes, each in a fixed order, so the sums do not depend
+// on scheduling: block (b, g) of the first sums tokens b*GS_CHUNK ..
+// (b+1)*GS_CHUNK - 1 (thread i takes tokens i, i+256, ..., then a
+// fixed-shape tree) into part[g][b]; block g of the second sums part[g][0 ..
+// nb-1] the same way (nb = 0: zeros).
+constexpr int GS_CHUNK = 1024;
+
+__device__ __forceinline__ void block_sum2(double& m, double& c, double* s_m, double* s_c) {
+  const int tid = threadIdx.x;
   s_m[tid] = m;
   s_c[tid] = c;
   __syncthreads();
@@ -234,17 +228,61 @@ __global__ void __launch_bounds__(256) group_stats_kernel(const float* __restric
     }
     __syncthreads();
   }
+  m = s_m[0];
+  c = s_c[0];
+}
+
+__global__ void __launch_bounds__(256) group_partials_kernel(const float* __restrict__ gmass,
+                                                             const int32_t* __restrict__ idx, int64_t T, int K,
+                                                             int E, int G, double* __restrict__ part, int nb) {
+  __shared__ double s_m[256], s_c[256];
+  const int b = blockIdx.x, g = blockIdx.y, tid = threadIdx.x, gs = E / G;
+  const int64_t t0 = (int64_t)b * GS_CHUNK, t1 = t0 + GS_CHUNK < T ? t0 + GS_CHUNK : T;
+  double m = 0.0, c = 0.0;
+  for (int64_t t = t0 + tid; t < t1; t += 256) {
+    m += (double)gmass[t * G + g];
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[t * K + k];
+      c += (e >= 0 && e < E && e / gs == g) ? 1.0 : 0.0;
+    }
+  }
+  block_sum2(m, c, s_m, s_c);
   if (tid == 0) {
-    out[g] = s_m[0];
-    out[G + g] = s_c[0];
+    part[(int64_t)g * nb + b] = m;
+    part[(int64_t)(G + g) * nb + b] = c;
+  }
+}
+
+__global__ void __launch_bounds__(256) group_stats_kernel(const double* __restrict__ part, int nb, int G,
+                                                          double* __restrict__ out) {
+  __shared__ double s_m[256], s_c[256];
+  const int g = blockIdx.x, tid = threadIdx.x;
+  double m = 0.0, c = 0.0;
+  for (int b = tid; b < nb; b += 256) {
+    m += part[(int64_t)g * nb + b];
+    c += part[(int64_t)(G + g) * nb + b];
+  }
+  block_sum2(m, c, s_m, s_c);
+  if (tid == 0) {
+    out[g] = m;
+    out[G + g] = c;
   }
 }
 
 }  // namespace
 
-hipError_t launch_group_stats(const float* gmass, const int32_t* idx, int64_t T, int K, int E, int G, double* out,
-                              hipStream_t s) {
-  group_stats_kernel<<<G, 256, 0, s>>>(gmass, idx, T, K, E, G, out);
+int64_t group_stats_partials(int64_t T, int G) { return (T + GS_CHUNK - 1) / GS_CHUNK * 2 * G; }
+
+hipError_t launch_group_stats(const float* gmass, const int32_t* idx, int64_t T, int K, int E, int G, double* part,
+                              double* out, hipStream_t s) {
+  const int64_t nb = (T + GS_CHUNK - 1) / GS_CHUNK;
+  if (nb > 0) {
+    const dim3 grid((unsigned)nb, (unsigned)G);
+    group_partials_kernel<<<grid, 256, 0, s>>>(gmass, idx, T, K, E, G, part, (int)nb);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  group_stats_kernel<<<G, 256, 0, s>>>(part, (int)nb, G, out);
   return hipGetLastError();
 }
 
