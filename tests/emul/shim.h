@@ -105,6 +105,15 @@ inline int emul_readlane(int v, int l) {
   emul_wave_sync();
   return r;
 }
+inline unsigned long long __ballot(int pred) {  // bit l: lane l of the wave holds pred != 0
+  emul_wave_slots[threadIdx.x] = pred != 0;
+  emul_wave_sync();
+  unsigned long long m = 0;
+  for (int l = 0; l < 64; ++l)
+    if (emul_wave_slots[(threadIdx.x & ~63) + l]) m |= 1ull << l;
+  emul_wave_sync();
+  return m;
+}
 #define __builtin_amdgcn_update_dpp(old, src, ctrl, rm, bm, bc) emul_update_dpp((old), (src), (ctrl), (rm), (bm), (bc))
 #define __builtin_amdgcn_readlane(v, l) emul_readlane((v), (l))
 

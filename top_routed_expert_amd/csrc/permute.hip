@@ -208,11 +208,15 @@ __device__ __forceinline__ int block1024_excl_scan(int v, int* s_tot, int* total
 }
 
 // Small batches (T*K <= 1024, E <= 1022): the whole permutation and the
-// expert-GEMM tile table in one block of 1024 threads. Counts come from LDS
-// atomics (order-independent); each pair's rank among the earlier pairs of
-// its expert is counted directly over the pairs before it (a wave-uniform
-// loop over 16-byte LDS reads), so the result is the same stable
-// permutation as the two-kernel path.
+// expert-GEMM tile table in one block of 1024 threads (pair p = thread p, so
+// wave w holds pairs 64w .. 64w+63). A pair's stable rank among the earlier
+// pairs of its expert is (pairs of that expert in earlier waves) + (lanes
+// below it in its own wave with the same expert). The second term comes from
+// a ballot per distinct expert of the wave; the wave's first lane of each
+// expert writes that expert's count of the wave to s_cnt[w][e] (no atomics),
+// and thread e turns column e of s_cnt into an exclusive scan over the waves
+// and the expert's total. So the result is the same stable permutation as
+// the two-kernel path.
 __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __restrict__ idx, int P, int K, int E,
                                                              int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ sorted_token,
@@ -220,19 +224,38 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
                                                              int32_t* __restrict__ offsets_ext, int32_t extra_rows,
                                                              Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles,
                                                              int32_t max_tiles, int BM) {
-  __shared__ __attribute__((aligned(16))) int s_idx[1024];
+  __shared__ int s_cnt[16 * 1024];  // [wave][expert]
   __shared__ int s_off[1025];
   __shared__ int s_tot[16];
-  const int tid = threadIdx.x, wave = tid >> 6;
-  const int e_mine = tid < P ? idx[tid] : -1;
-  s_idx[tid] = e_mine;
-  s_off[tid] = 0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e_raw = tid < P ? idx[tid] : -1;
+  const bool valid = e_raw >= 0 && e_raw < E;
+  const int e_mine = valid ? e_raw : -1;
+  for (int i = tid; i < 16 * E; i += 1024) s_cnt[i] = 0;
   __syncthreads();
-  const bool valid = e_mine >= 0 && e_mine < E;
-  if (valid) atomicAdd(&s_off[e_mine], 1);
+  // same-expert lanes of this wave: one ballot per distinct expert, in lane order
+  uint64_t same = 0;
+  {
+    uint64_t todo = __ballot(valid);
+    while (todo) {
+      const int lead = __builtin_ctzll(todo);
+      const int e_lead = __builtin_amdgcn_readlane(e_mine, lead);
+      const uint64_t m = __ballot(e_mine == e_lead);
+      if (e_mine == e_lead) same = m;
+      if (lane == lead) s_cnt[wave * E + e_lead] = __builtin_popcountll(m);
+      todo &= ~m;
+    }
+  }
+  const int r_wave = __builtin_popcountll(same & ((1ull << lane) - 1ull));
   __syncthreads();
-  // exclusive scan of the counts (expert tid)
-  const int c = tid < E ? s_off[tid] : 0;
+  // column e: exclusive scan over the waves, total = the expert's pair count
+  int c = 0;
+  if (tid < E)
+    for (int w = 0; w < 16; ++w) {
+      const int v = s_cnt[w * E + tid];
+      s_cnt[w * E + tid] = c;
+      c += v;
+    }
   int total;
   const int off_mine = block1024_excl_scan(c, s_tot, &total);
   if (tid < E) s_off[tid] = off_mine;  // s_off now holds offsets
@@ -246,20 +269,9 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
     offsets_ext[E + 1] = P;
     offsets_ext[E + 2] = P + extra_rows;
   }
-  // stable rank: earlier pairs routed to the same expert. The loop bound is
-  // uniform per wave (the wave's last pair; 0 for waves past the last
-  // pair); 4 pairs per LDS read.
-  const int wave_end = wave * 64 < P ? min(P, (wave + 1) * 64) : 0;
-  int r = 0;
-#pragma unroll 8
-  for (int j0 = 0; j0 < wave_end; j0 += 4) {
-    const int4 q = *(const int4*)&s_idx[j0];
-    r += (j0 < tid && q.x == e_mine) + (j0 + 1 < tid && q.y == e_mine) + (j0 + 2 < tid && q.z == e_mine) +
-         (j0 + 3 < tid && q.w == e_mine);
-  }
   if (tid < P) {
     if (valid) {
-      const int d = s_off[e_mine] + r;
+      const int d = s_off[e_mine] + s_cnt[wave * E + e_mine] + r_wave;
       dest[tid] = d;
       sorted_token[d] = tid / K;
     } else {
