@@ -102,6 +102,10 @@ def parse():
     ap.add_argument("--summarize-pmc", metavar="DIR",
                     help="write the gate/up HBM traffic summary from rocprofv3 --pmc runs in DIR/pmc_<workload>_"
                          "<FETCH_SIZE|WRITE_SIZE> (csv, -o run) to --out; no GPU needed")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="write the SQ / L2 counter summary of the 256x256 expert GEMMs from rocprofv3 --pmc runs "
+                         "in DIR/<pass> (csv, -o run; passes listed in COUNTER_PASSES) and the kernel trace in "
+                         "DIR/trace to --out; no GPU needed")
     ap.add_argument("--out")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", default="")
@@ -572,6 +576,82 @@ def summarize_trace(d: str, title: str, command: str, out: str) -> None:
     open(out, "w").write("\n".join(L) + "\n")
 
 
+# counter passes of the 256x256 expert GEMMs (each within one run's per-block limits)
+COUNTER_PASSES = {
+    "sq_a": "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT "
+            "SQ_ACTIVE_INST_LDS SQ_WAVE_CYCLES SQ_WAIT_ANY",
+    "sq_b": "SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL SQ_LDS_IDX_ACTIVE SQ_LDS_ADDR_CONFLICT SQ_LDS_UNALIGNED_STALL "
+            "SQ_INSTS_LDS SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VMEM",
+    "sq_c": "SQ_INSTS_MFMA SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU SQ_INSTS_VMEM_RD "
+            "SQ_WAVES SQ_CYCLES TA_BUSY_avr",
+    "tcc": "TCC_HIT_sum TCC_MISS_sum TCC_REQ_sum",
+}
+
+
+def summarize_counters(d: str, out: str) -> None:
+    """Per-dispatch averages of the counter passes for the 256x256 gate/up and down kernels of a prefill run,
+    with the derived clock, matrix-core utilisation, wait fractions and L2 hit rate."""
+    import collections
+    import csv
+    kinds = {"gate/up": "gemm_bf16_big8<0", "down": "gemm_bf16_big8<1"}
+    vals = {k: collections.OrderedDict() for k in kinds}
+    for name in COUNTER_PASSES:
+        per = collections.defaultdict(lambda: collections.defaultdict(list))
+        for r in csv.DictReader(open(os.path.join(d, name, "run_counter_collection.csv"))):
+            for k, pat in kinds.items():
+                if pat in r["Kernel_Name"]:
+                    per[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        for k in kinds:
+            for c, v in per[k].items():
+                vals[k][c] = sum(v) / len(v)
+    dur = {}
+    for r in csv.DictReader(open(os.path.join(d, "trace", "run_kernel_trace.csv"))):
+        for k, pat in kinds.items():
+            if pat in r["Kernel_Name"]:
+                dur.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9)
+    L = ["# SQ / LDS / matrix-core / L2 counters of the 256x256 expert GEMMs, prefill (T=8192), MI355X\n",
+         "Commands (repo root, one MI355X, `TMPDIR=/tmp`), one pass each under `timeout -s KILL 120`, then "
+         f"`python bench.py --summarize-counters <dir> --out {out}`:\n", "```"]
+    for name, cs in COUNTER_PASSES.items():
+        L.append(f"rocprofv3 --pmc {cs} --output-format csv -d <dir>/{name} -o run -- python bench.py --workload "
+                 "prefill --steps 2 --warmup 1 --no-cpu-baseline --no-secondary")
+    L += ["rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- python bench.py --workload "
+          "prefill --steps 2 --warmup 1 --no-cpu-baseline --no-secondary", "```\n",
+          "Per dispatch, averaged over the dispatches of each kernel in the run (the layer steps and the gate/up "
+          "kernel alone). rocprofv3 reports each counter summed over its hardware instances: GRBM_GUI_ACTIVE over "
+          "the 8 XCDs, SQ_CYCLES over the 32 shader engines.\n",
+          "| counter | gate/up `gemm_bf16_big8<0, …>` | down `gemm_bf16_big8<1, …>` |", "|---|---|---|"]
+    names = sorted(set(vals["gate/up"]) | set(vals["down"]))
+    for c in names:
+        L.append(f"| {c} | {vals['gate/up'].get(c, float('nan')):.0f} | {vals['down'].get(c, float('nan')):.0f} |")
+    L += ["", "Derived:", ""]
+    for k in kinds:
+        v = vals[k]
+        cyc = v.get("GRBM_GUI_ACTIVE", 0.0) / 8
+        t = sum(dur.get(k, [0.0])) / max(1, len(dur.get(k, [])))
+        line = f"- {k}: {cyc / 1e6:.2f}M cycles per XCD"
+        if t > 0:
+            line += f" in {t * 1e3:.3f} ms (trace average), so about {cyc / t / 1e9:.2f} GHz"
+        if cyc > 0:
+            line += (f"; matrix cores busy {100 * v.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / (cyc * 1024):.1f}% of "
+                     "cycles (SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs))")
+        wc = v.get("SQ_WAVE_CYCLES", 0.0)
+        if wc > 0:
+            line += (f"; waves waiting on a counter {100 * v.get('SQ_WAIT_ANY', 0) / wc:.0f}% and to issue "
+                     f"{100 * v.get('SQ_WAIT_INST_ANY', 0) / wc:.0f}% of wave cycles")
+        la = v.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        if la > 0:
+            line += f"; LDS bank conflicts {100 * v.get('SQ_LDS_BANK_CONFLICT', 0) / la:.2f}% of LDS-active cycles"
+        req = v.get("TCC_REQ_sum", 0.0)
+        if req > 0:
+            line += (f"; L2 {req / 1e6:.1f}M requests ({req * 128 / 1e9:.2f} GB in 128-byte lines), hit rate "
+                     f"{100 * v.get('TCC_HIT_sum', 0) / req:.1f}%")
+        if v.get("SQ_INSTS_MFMA"):
+            line += f"; {v['SQ_INSTS_MFMA'] / 1e6:.1f}M MFMA instructions"
+        L.append(line)
+    open(out, "w").write("\n".join(L) + "\n")
+
+
 PMC_WORKLOADS = ("decode", "prefill", "skew", "full")
 
 
@@ -661,6 +741,9 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.out)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.out)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",

@@ -115,6 +115,12 @@ inline unsigned long long __ballot(int pred) {  // bit l: lane l of the wave hol
   return m;
 }
 #define __builtin_amdgcn_update_dpp(old, src, ctrl, rm, bm, bc) emul_update_dpp((old), (src), (ctrl), (rm), (bm), (bc))
+// mov_dpp: lanes without a source (or in disabled rows) get 0 with bound_ctrl, else keep src
+inline int emul_mov_dpp(int src, int ctrl, int row_mask, int bank_mask, bool bound_ctrl) {
+  if (!emul_lanes_synced()) return src;
+  return emul_update_dpp(bound_ctrl ? 0 : src, src, ctrl, row_mask, bank_mask, bound_ctrl);
+}
+#define __builtin_amdgcn_mov_dpp(src, ctrl, rm, bm, bc) emul_mov_dpp((src), (ctrl), (rm), (bm), (bc))
 #define __builtin_amdgcn_readlane(v, l) emul_readlane((v), (l))
 
 // LDS addresses taken as 32-bit values become region * 2^20 + offset.

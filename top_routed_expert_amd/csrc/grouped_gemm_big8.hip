@@ -369,6 +369,14 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
       // routed rows in the 16-bit format (the item's rows are all on one side of out16_rows)
       const bool half = p.out16 != nullptr && t.row0 < p.out16_rows;
       const int64_t row_shift = p.out16 != nullptr ? p.out16_rows : 0;
+      // 16-bit form: this lane's row of pass 0 of row tile 0 (rows advance by 4 per pass), its
+      // 4 columns and its row chunk's exponent byte; rows left before the item's end
+      const int64_t rb = (int64_t)t.row0 + wm * 128 + (lane >> 4);
+      const int rows_left = (int)((int64_t)t.row1 - rb);
+      const bool col_ok = col0 + (lane & 15) * 4 < p.N;
+      uint16_t* q16 = half ? p.out16 + rb * p.ldo + col0 + (lane & 15) * 4 : nullptr;
+      uint8_t* qe = half ? p.out16_exp + rb * (p.ldo >> 6) + (col0 >> 6) : nullptr;
+      const int64_t step16 = 4 * p.ldo, stepe = 4 * (p.ldo >> 6);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
 #pragma unroll
@@ -386,24 +394,27 @@ __global__ void __launch_bounds__(512) gemm_bf16_big8(GemmArgs p) {
           const int64_t r = (int64_t)t.row0 + wm * 128 + m * 16 + rr16;
           const int col = col0 + c4;
           if (half) {
-            // the row's 64-column maximum over its 16 lanes (one DPP row), then its exponent
-            float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-            a = fmaxf(a, __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)__float_as_uint(a), (int)__float_as_uint(a), 0xb1, 0xf, 0xf, false)));
-            a = fmaxf(a, __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)__float_as_uint(a), (int)__float_as_uint(a), 0x4e, 0xf, 0xf, false)));
-            a = fmaxf(a, __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)__float_as_uint(a), (int)__float_as_uint(a), 0x141, 0xf, 0xf, false)));
-            a = fmaxf(a, __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)__float_as_uint(a), (int)__float_as_uint(a), 0x140, 0xf, 0xf, false)));
-            int e = (int)((__float_as_uint(a) >> 23) & 255u);
+            // the row's 64-column maximum of |y| over its 16 lanes (one DPP row), taken on the
+            // bit patterns (non-negative floats order like unsigned integers), then its exponent
+            const uint32_t ax = __float_as_uint(v.x) & 0x7fffffffu, ay = __float_as_uint(v.y) & 0x7fffffffu;
+            const uint32_t az = __float_as_uint(v.z) & 0x7fffffffu, aw = __float_as_uint(v.w) & 0x7fffffffu;
+            uint32_t a = max(max(ax, ay), max(az, aw));
+            a = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0xb1, 0xf, 0xf, true));
+            a = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0x4e, 0xf, 0xf, true));
+            a = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0x141, 0xf, 0xf, true));
+            a = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0x140, 0xf, 0xf, true));
+            int e = (int)(a >> 23);
             e = e < EXP16_MIN ? EXP16_MIN : e;
             const float sc = ldexpf(1.f, EXP16_BIAS - e);  // exact power of two
             const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.x * sc)) |
                                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.y * sc)) << 16);
             const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.z * sc)) |
                                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v.w * sc)) << 16);
-            if (r < t.row1 && col < p.N) {
+            if (m * 16 + pass * 4 < rows_left && col_ok) {
               // read once, by the combine: non-temporal
               typedef uint32_t u32x2_st __attribute__((ext_vector_type(2)));
-              __builtin_nontemporal_store(u32x2_st{lo, hi}, (u32x2_st*)&p.out16[r * p.ldo + col]);
-              if ((lane & 15) == 0) p.out16_exp[r * (p.ldo >> 6) + (col0 >> 6)] = (uint8_t)e;
+              __builtin_nontemporal_store(u32x2_st{lo, hi}, (u32x2_st*)(q16 + (m * 4 + pass) * step16));
+              if ((lane & 15) == 0) qe[(m * 4 + pass) * stepe] = (uint8_t)e;
             }
           } else if (r < t.row1 && col < p.N) {
             if (p.bias) {
