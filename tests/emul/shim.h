@@ -48,6 +48,7 @@ inline int hipGetSymbolAddress(void** p, const void* sym) { *p = (void*)sym; ret
 inline float __uint_as_float(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
 inline uint32_t __float_as_uint(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
 inline float __expf(float x) { return expf(x); }
+#define __builtin_amdgcn_rcpf(x) (1.0f / (x))
 template <class T> T min(T a, T b) { return a < b ? a : b; }
 template <class T> T max(T a, T b) { return a > b ? a : b; }
 // Block barrier: a real barrier when the block runs one OS thread per lane
