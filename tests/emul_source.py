@@ -22,6 +22,7 @@ EMUL = os.path.join(ROOT, "tests", "emul")
 # it runs lane by lane, as the GEMMs do)
 SYNC_KERNELS = {"build_tiles_kernel", "permute_rank_kernel", "permute_place_kernel", "permute_small_kernel",
                 "ep_plan_kernel", "topk_kernel", "group_partials_kernel", "group_stats_kernel", "combine_kernel",
+                "combine16_kernel",
                 "gemm_generic",
                 "router_topk_kernel"}
 
