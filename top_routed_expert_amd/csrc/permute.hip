@@ -211,12 +211,12 @@ __device__ __forceinline__ int block1024_excl_scan(int v, int* s_tot, int* total
 // expert-GEMM tile table in one block of 1024 threads (pair p = thread p, so
 // wave w holds pairs 64w .. 64w+63). A pair's stable rank among the earlier
 // pairs of its expert is (pairs of that expert in earlier waves) + (lanes
-// below it in its own wave with the same expert). The second term comes from
-// a ballot per distinct expert of the wave; the wave's first lane of each
-// expert writes that expert's count of the wave to s_cnt[w][e] (no atomics),
-// and thread e turns column e of s_cnt into an exclusive scan over the waves
-// and the expert's total. So the result is the same stable permutation as
-// the two-kernel path.
+// below it in its own wave with the same expert). Each lane counts the
+// second term, and the wave's total for its expert, over the wave's 64 ids
+// in LDS; the wave's first lane of each expert writes that total to
+// s_cnt[w][e] (no atomics), and thread e turns column e of s_cnt into an
+// exclusive scan over the waves and the expert's total. So the result is
+// the same stable permutation as the two-kernel path.
 __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __restrict__ idx, int P, int K, int E,
                                                              int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ sorted_token,
@@ -225,28 +225,29 @@ __global__ void __launch_bounds__(1024) permute_small_kernel(const int32_t* __re
                                                              Tile* __restrict__ tiles, int32_t* __restrict__ n_tiles,
                                                              int32_t max_tiles, int BM) {
   __shared__ int s_cnt[16 * 1024];  // [wave][expert]
+  __shared__ __attribute__((aligned(16))) int s_idx[1024];
   __shared__ int s_off[1025];
   __shared__ int s_tot[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int e_raw = tid < P ? idx[tid] : -1;
   const bool valid = e_raw >= 0 && e_raw < E;
   const int e_mine = valid ? e_raw : -1;
+  s_idx[tid] = e_mine;
   for (int i = tid; i < 16 * E; i += 1024) s_cnt[i] = 0;
   __syncthreads();
-  // same-expert lanes of this wave: one ballot per distinct expert, in lane order
-  uint64_t same = 0;
-  {
-    uint64_t todo = __ballot(valid);
-    while (todo) {
-      const int lead = __builtin_ctzll(todo);
-      const int e_lead = __builtin_amdgcn_readlane(e_mine, lead);
-      const uint64_t m = __ballot(e_mine == e_lead);
-      if (e_mine == e_lead) same = m;
-      if (lane == lead) s_cnt[wave * E + e_lead] = __builtin_popcountll(m);
-      todo &= ~m;
-    }
+  // this wave's lanes with the same expert: below this one (r_wave) and in all (n_wave), from
+  // the wave's 64 ids in LDS, four per read
+  int r_wave = 0, n_wave = 0;
+  const int4* w4 = (const int4*)&s_idx[wave * 64];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int4 q = w4[j];
+    const int b = 4 * j;
+    r_wave += (b < lane && q.x == e_mine) + (b + 1 < lane && q.y == e_mine) + (b + 2 < lane && q.z == e_mine) +
+              (b + 3 < lane && q.w == e_mine);
+    n_wave += (q.x == e_mine) + (q.y == e_mine) + (q.z == e_mine) + (q.w == e_mine);
   }
-  const int r_wave = __builtin_popcountll(same & ((1ull << lane) - 1ull));
+  if (valid && r_wave == 0) s_cnt[wave * E + e_mine] = n_wave;  // the wave's first lane of the expert
   __syncthreads();
   // column e: exclusive scan over the waves, total = the expert's pair count
   int c = 0;
