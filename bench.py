@@ -20,7 +20,11 @@ One JSON line is printed. The headline (value, ms_per_step, config) is the
   workloads     the other four named workloads (tiny, prefill, skew, full
                 width) measured the same way, each with its own roofline; the
                 full-width entry carries the per-group activation counts of
-                the 8 x 36 expert groups and the Expert Activation Skew.
+                the 8 x 36 expert groups and the Expert Activation Skew;
+  measured_peaks what plain library work reaches on this GPU (a 2 GiB
+                device copy, an 8192^3 bf16 torch.matmul); MFMA-bound
+                rooflines also give frac_of_vendor_gemm, their rate over
+                that matmul's.
 """
 from __future__ import annotations
 
@@ -576,6 +580,54 @@ def summarize_trace(d: str, title: str, command: str, out: str) -> None:
     open(out, "w").write("\n".join(L) + "\n")
 
 
+def measured_peaks(reps: int = 10) -> dict:
+    """Rates this GPU reaches with plain library work, beside the published peaks: a 2 GiB
+    device-to-device copy (HBM read and write, counted both ways) and one 8192^3 bf16 matrix
+    product (torch.matmul, the vendor GEMM library). Timed with HIP events on the current stream."""
+    import torch
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    n = 1 << 31
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    x = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    y = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    for _ in range(2):
+        torch.matmul(x, y)
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(reps):
+        torch.matmul(x, y)
+    b.record()
+    torch.cuda.synchronize()
+    tflops = 2 * m ** 3 * reps / (a.elapsed_time(b) * 1e-3) / 1e12
+    del x, y
+    torch.cuda.empty_cache()
+    return {"hbm_copy_gbs": round(copy_gbs, 1), "bf16_matmul_tflops": round(tflops, 1),
+            "how": "2 GiB device copy (read + write bytes); torch.matmul bf16 8192x8192x8192; 10 runs each"}
+
+
+def of_measured(roof: dict, peaks: dict):
+    """An MFMA-bound roofline's achieved rate as a fraction of the vendor GEMM's measured rate.
+    HBM-bound ones get none: no plain library kernel reads HBM as fast as the expert GEMMs do (a
+    device copy moves about 4.8 TB/s of reads and writes together, torch's reductions read at
+    about 4 TB/s), so such a fraction would say nothing about the kernel."""
+    if roof.get("bound") != "mfma" or not peaks["bf16_matmul_tflops"]:
+        return None
+    return round(roof["achieved"] / peaks["bf16_matmul_tflops"], 4)
+
+
 # counter passes of the 256x256 expert GEMMs (each within one run's per-block limits)
 COUNTER_PASSES = {
     "sq_a": "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT "
@@ -828,6 +880,15 @@ def main():
             print(f"[bench] {name}: layer {r2['ms']:.4f} ms/step; gate/up kernel "
                   f"{r2['roofline']['launch_ms']:.4f} ms", file=sys.stderr, flush=True)
         line["workloads"] = others
+        torch.cuda.empty_cache()
+        peaks = measured_peaks()
+        print(f"[bench] measured: copy {peaks['hbm_copy_gbs']:.0f} GB/s, bf16 matmul "
+              f"{peaks['bf16_matmul_tflops']:.0f} TFLOP/s", file=sys.stderr, flush=True)
+        line["measured_peaks"] = peaks
+        for r in [line["roofline"]] + [e["roofline"] for e in others.values()]:
+            f = of_measured(r, peaks)
+            if f is not None:
+                r["frac_of_vendor_gemm"] = f
     print(json.dumps(line), flush=True)
 
 
