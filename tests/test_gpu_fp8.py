@@ -5,8 +5,9 @@ codes in the packed fp8 layout, unpacked here by its documented formula). The
 layer with fp8 weights (moe_layer_forward, MOE_LAYOUT_FP8) is compared with
 the oracle's layer on the dequantised weights decode(q) * s, under the same
 tolerance rules as the bf16 layer: the fp32-output run within 2e-2 of RMS,
-the bf16 output the rounding of that run. Small layers in full over the 32-,
-64- and 128-row tiles, the decode and prefill workloads on sampled rows.
+the bf16 output the rounding of that run; near-tie tokens held to the
+validity rule of the bf16 tests. Small layers in full over the 32-, 64- and
+128-row tiles, the decode and prefill workloads on sampled rows.
 """
 from __future__ import annotations
 
@@ -18,9 +19,10 @@ import torch
 
 import synth
 import top_routed_expert_amd as moe
-from moe_testutil import compare_bf16_out, compare_out, compare_routing, device_layer, oracle_weights, to_host
+from moe_testutil import check_near_ties, compare_bf16_out, compare_out, compare_routing, compare_rows, device_layer, \
+    oracle_weights, to_host
 from oracle import moe_oracle as O
-from test_gpu_parity import SMALL, sample_rows
+from test_gpu_parity import SMALL, rms_of, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -78,13 +80,27 @@ def run_fp8(spec, L, rows=None, k=None):
     kh = None if k is None else to_host(k)
     ref = O.route(x_host, Wq.router, spec.K, Wq.bias) if kh is None else O.route(x_host, Wq.router, spec.K, Wq.bias, kh)
     r = compare_routing(to_host(idx), to_host(prob), ref, x_host, Wq.router)
+    # near ties: a valid top-k set, and the output of the experts the GPU chose
+    gi = to_host(idx)
+    tie = check_near_ties(gi, to_host(prob), ref, x_host, Wq.router, spec.K, kh)
     keep = np.nonzero(ref["gap"] >= 1e-6)[0]
     rows = keep if rows is None else np.intersect1d(rows, keep)
-    rr = O.layer_rows(x_host, Wq, spec.K, rows) if kh is None else O.layer_rows(x_host, Wq, spec.K, rows, kh)
-    sel = lambda a: to_host(a[torch.from_numpy(rows).to(a.device)])
+    # one oracle pass over the experts for the compared rows (the oracle's routing) and the
+    # near-tie rows (the GPU's ids, the oracle's p of them): each expert dequantised once
+    ig = gi[tie].astype(np.int64)
+    p_tie = np.where(ig >= 0, np.take_along_axis(ref["p32"][tie].astype(np.float64), np.maximum(ig, 0), axis=1), 0.0)
+    all_out = O.rows_output(x_host, Wq, np.concatenate([rows, tie]), np.concatenate([ref["idx"][rows], ig]),
+                            np.concatenate([ref["prob"][rows].astype(np.float64), p_tie]))
+    rr = {"out_rows": all_out[:len(rows)]}
+    tie_ref = all_out[len(rows):]
+    sel = lambda a, r=rows: to_host(a[torch.from_numpy(np.asarray(r)).to(a.device)])
     c32 = compare_out(sel(out32), rr["out_rows"], 2e-2, "fp8 layer, fp32 output")
     assert torch.equal(out, out32.to(torch.bfloat16)), "bf16 output is not the rounding of the fp32 output"
     c16 = compare_bf16_out(sel(out), rr["out_rows"])
+    if tie.size:
+        rms = rms_of(rr["out_rows"], tie_ref)
+        compare_rows(sel(out32, tie), tie_ref, rms, 2e-2, False, "near-tie rows (fp8, fp32 output)")
+        compare_rows(sel(out, tie), tie_ref, rms, 2e-2, True, "near-tie rows (fp8, bf16 output)")
     return r, c32, c16
 
 

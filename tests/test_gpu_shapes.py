@@ -10,7 +10,9 @@ no shared expert or one of another width, fp32 and bf16 layers, skewed
 routing. Each layer is compared in full with the comparison rules of the
 parity tests (near-tie tokens held to the validity rule), and bf16 layers
 whose widths allow the packed layout must give bit-identical results with
-packed weights.
+packed weights. The layers of up to 3000 tokens also run with per-token
+expert counts drawn from {0, K/2, K}, and those whose widths allow it with
+fp8 expert weights (against the oracle on the dequantised weights).
 """
 from __future__ import annotations
 
@@ -22,6 +24,8 @@ import torch
 import synth
 import top_routed_expert_amd as moe
 from moe_testutil import device_layer
+from test_gpu_dynamic_topk import k_draw, run_dynamic
+from test_gpu_fp8 import run_fp8
 from test_gpu_parity import run_full_compare
 
 pytestmark = pytest.mark.gpu
@@ -73,3 +77,24 @@ def test_shape(name):
         torch.cuda.synchronize()
         for what, a, b in zip(("out", "topk_idx", "topk_prob", "offsets"), rows, packed):
             assert torch.equal(a, b), f"{name}: {what} differs between packed and row-major weights"
+
+
+DYN = [n for n, s in SHAPES.items() if s.T <= 3000]
+FP8 = [n for n, s in SHAPES.items()
+       if s.T <= 3000 and s.dtype == "bf16" and s.D % 64 == 0 and s.F % 64 == 0 and s.Fs % 64 == 0]
+
+
+@pytest.mark.parametrize("name", DYN)
+def test_shape_dynamic_topk(name):
+    spec = SHAPES[name]
+    print(f"shape {name}, dynamic top-k", flush=True)
+    r, c32, c16 = run_dynamic(spec, device_layer(spec), k_draw(spec))
+    print(f"{name}: near_ties={r['near_ties']} out_rel(before cast)={c32['rel']:.3e} out_rel={c16['rel']:.3e}")
+
+
+@pytest.mark.parametrize("name", FP8)
+def test_shape_fp8(name):
+    spec = SHAPES[name]
+    print(f"shape {name}, fp8 expert weights", flush=True)
+    r, c32, c16 = run_fp8(spec, device_layer(spec))
+    print(f"{name}: near_ties={r['near_ties']} out_rel(before cast)={c32['rel']:.3e} out_rel={c16['rel']:.3e}")
