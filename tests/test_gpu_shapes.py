@@ -13,6 +13,12 @@ whose widths allow the packed layout must give bit-identical results with
 packed weights. The layers of up to 3000 tokens also run with per-token
 expert counts drawn from {0, K/2, K}, and those whose widths allow it with
 fp8 expert weights (against the oracle on the dequantised weights).
+
+LIMITS adds layers at the edges of the configuration the library accepts:
+1024 routed experts and K = 64 (the largest it takes) on the decode-size,
+32-row and 256-row tile paths; 1022 and 1023 experts at T*K = 1024 (the
+single-block permutation takes at most 1022); 320 and 321 experts at 200
+tokens (the fused router takes at most 320).
 """
 from __future__ import annotations
 
@@ -98,3 +104,47 @@ def test_shape_fp8(name):
     print(f"shape {name}, fp8 expert weights", flush=True)
     r, c32, c16 = run_fp8(spec, device_layer(spec))
     print(f"{name}: near_ties={r['near_ties']} out_rel(before cast)={c32['rel']:.3e} out_rel={c16['rel']:.3e}")
+
+
+LIMITS = {
+    # bf16 expert widths of at least 128: at width 64 the one bf16 rounding of h alone moves the
+    # largest output by about 2.2e-2 of the RMS (float64, 1023 experts, K = 64, 16 tokens), past
+    # the 2e-2 bound without any fault
+    # the largest expert count and K: 16 tokens (split router, T*K = 1024 with E > 1022: the
+    # general permutation), 40 tokens (32-row tiles), 1024 tokens (256-row tiles: 64 rows per expert)
+    "E1024_K64_T16": synth.spec("tiny", T=16, D=256, E=1024, K=64, F=128, Fs=128, dtype="bf16", seed=301),
+    "E1024_K64_T40": synth.spec("tiny", T=40, D=256, E=1024, K=64, F=128, Fs=256, dtype="bf16", seed=302),
+    "E1024_K64_T1024": synth.spec("tiny", T=1024, D=256, E=1024, K=64, F=128, Fs=128, dtype="bf16", seed=303),
+    "E1024_K64_T40_f32": synth.spec("tiny", T=40, D=128, E=1024, K=64, F=32, Fs=0, dtype="f32", seed=304),
+    # the single-block permutation at its expert limit and one past it (T*K = 1024)
+    "E1022_K64_T16": synth.spec("tiny", T=16, D=256, E=1022, K=64, F=128, Fs=128, dtype="bf16", seed=305),
+    "E1023_K64_T16": synth.spec("tiny", T=16, D=256, E=1023, K=64, F=128, Fs=128, dtype="bf16", seed=306),
+    # the fused router at its expert limit and one past it (more than 64 tokens)
+    "E320_K8_T200": synth.spec("tiny", T=200, D=256, E=320, K=8, F=128, Fs=128, dtype="bf16", seed=307),
+    "E321_K8_T200": synth.spec("tiny", T=200, D=256, E=321, K=8, F=128, Fs=128, dtype="bf16", seed=308),
+    # K = 1 over 1024 experts with many tokens (two-kernel router, one row per pair)
+    "E1024_K1_T3000": synth.spec("tiny", T=3000, D=256, E=1024, K=1, F=128, Fs=0, dtype="bf16", seed=309),
+}
+
+
+@pytest.mark.parametrize("name", list(LIMITS))
+def test_limits(name):
+    spec = LIMITS[name]
+    print(f"limit {name}", flush=True)
+    r, c32, c16 = run_full_compare(spec)
+    print(f"{name}: near_ties={r['near_ties']} out_rel(before cast)={c32['rel']:.3e} out_rel={c16['rel']:.3e}")
+
+
+@pytest.mark.parametrize("name", ["E1024_K64_T40", "E1024_K64_T1024"])
+def test_limits_dynamic_topk(name):
+    spec = LIMITS[name]
+    print(f"limit {name}, dynamic top-k", flush=True)
+    r, c32, c16 = run_dynamic(spec, device_layer(spec), k_draw(spec))
+    print(f"{name}: near_ties={r['near_ties']} out_rel(before cast)={c32['rel']:.3e} out_rel={c16['rel']:.3e}")
+
+
+def test_limits_fp8():
+    spec = LIMITS["E1024_K64_T1024"]
+    print("limit E1024_K64_T1024, fp8 expert weights", flush=True)
+    r, c32, c16 = run_fp8(spec, device_layer(spec))
+    print(f"fp8: near_ties={r['near_ties']} out_rel(before cast)={c32['rel']:.3e} out_rel={c16['rel']:.3e}")

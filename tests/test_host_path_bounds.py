@@ -112,6 +112,32 @@ def test_halves_at_the_prefill_shape(host_path):
     assert calls_ok(out) == 4, out
 
 
+LIMIT_LAYERS = {
+    # the largest expert count and K, split router, general permutation (T*K = 1024, E > 1022)
+    "E1024_K64_T16": (16, 1024, 64, 256, 64, 1, 0, 0),
+    # the same over more tokens (rank/place permutation), packed weights
+    "E1024_K64_T40_packed": (40, 1024, 64, 256, 64, 2, 1, 0),
+    # the single-block permutation at its expert limit and one past it
+    "E1022_K64_T16": (16, 1022, 64, 256, 64, 3, 0, 0),
+    "E1023_K64_T16": (16, 1023, 64, 256, 64, 4, 0, 0),
+    # the fused router at its expert limit and one past it
+    "E320_K8_T200": (200, 320, 8, 256, 64, 5, 0, 0),
+    "E321_K8_T200_packed": (200, 321, 8, 256, 64, 6, 1, 0),
+    # fp32 with the largest expert count and K (real routing through the generic GEMM)
+    "E1024_K64_T40_fp32": (40, 1024, 64, 128, 32, 7, 0, 1),
+}
+
+
+@pytest.mark.skipif(os.environ.get("MOE_EMUL_LIMITS") != "1",
+                    reason="1.5 to 7 minutes of host time each: set MOE_EMUL_LIMITS=1 to run them")
+@pytest.mark.parametrize("name", list(LIMIT_LAYERS))
+def test_layer_at_the_limits_in_bounds(host_path, name):
+    """The layer entry points at the edges of the accepted configuration (1024 experts, K = 64, the
+    expert limits of the single-block permutation and of the fused router)."""
+    out = run(host_path, "layer", *LIMIT_LAYERS[name], timeout=1800)
+    assert calls_ok(out) >= 3 and "moe_layer_forward_noalloc" in out, out
+
+
 def test_planted_workspace_mistake_is_caught(tmp_path):
     """The check itself: carving the SwiGLU activations one row short of the workspace must be reported."""
     cc = ES.clang()
