@@ -637,6 +637,8 @@ COUNTER_PASSES = {
     "sq_c": "SQ_INSTS_MFMA SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU SQ_INSTS_VMEM_RD "
             "SQ_WAVES SQ_CYCLES TA_BUSY_avr",
     "tcc": "TCC_HIT_sum TCC_MISS_sum TCC_REQ_sum",
+    "tcp": "TCP_TCC_READ_REQ_sum TCP_TCC_READ_REQ_LATENCY_sum TCP_PENDING_STALL_CYCLES_sum TCP_TCR_TCP_STALL_CYCLES_sum "
+           "TA_ADDR_STALLED_BY_TC_CYCLES_sum TA_DATA_STALLED_BY_TC_CYCLES_sum TD_TC_STALL_sum TD_TD_BUSY_sum",
 }
 
 
@@ -700,6 +702,15 @@ def summarize_counters(d: str, out: str) -> None:
                      f"{100 * v.get('TCC_HIT_sum', 0) / req:.1f}%")
         if v.get("SQ_INSTS_MFMA"):
             line += f"; {v['SQ_INSTS_MFMA'] / 1e6:.1f}M MFMA instructions"
+        rq = v.get("TCP_TCC_READ_REQ_sum", 0.0)
+        if rq > 0 and cyc > 0:
+            lat = v.get("TCP_TCC_READ_REQ_LATENCY_sum", 0.0) / rq  # cycles from a vector L1 miss to its L2 data
+            per_cu = rq / 256 / cyc  # requests per cycle per compute unit
+            line += (f"; vector L1 to L2 reads {rq / 1e6:.1f}M ({rq * 128 / 1e9:.2f} GB), average latency "
+                     f"{lat:.0f} cycles, so about {per_cu * lat:.0f} reads in flight per compute unit on average "
+                     f"({per_cu * 128:.1f} bytes per cycle per compute unit); the vector L1 waits on pending L2 "
+                     f"data {100 * v.get('TCP_PENDING_STALL_CYCLES_sum', 0) / (256 * cyc):.0f}% of cycles and the "
+                     f"texture data unit on the cache {100 * v.get('TD_TC_STALL_sum', 0) / (256 * cyc):.0f}%")
         L.append(line)
     open(out, "w").write("\n".join(L) + "\n")
 
