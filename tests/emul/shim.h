@@ -148,3 +148,8 @@ inline emul_f32x2 emul_cvt_pk_f32_fp8(int w, bool hi) {  // values are not neede
   return emul_f32x2{0.f, 0.f};
 }
 #define __builtin_amdgcn_cvt_pk_f32_fp8(w, hi) emul_cvt_pk_f32_fp8((w), (hi))
+inline uint32_t emul_cvt_scalef32_pk_bf16_fp8(uint32_t w, float scale, bool hi) {  // shape only, as above
+  (void)w, (void)scale, (void)hi;
+  return 0u;
+}
+#define __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, hi) emul_cvt_scalef32_pk_bf16_fp8((w), (scale), (hi))

@@ -71,14 +71,15 @@ __host__ __device__ __forceinline__ int64_t packed_offset(int64_t ct, int64_t kb
   return (ct * (K / 32) + kb) * PACKED_FRAG + lane * 8;
 }
 
-// FP8 E4M3 -> bf16, exactly (an E4M3 value has at most 4 significant bits):
-// the hardware conversion gives fp32 (OCP E4M3 on gfx950), whose upper 16
-// bits are the bf16 value. HI selects bytes 2-3 of w instead of 0-1.
+// FP8 E4M3 -> bf16, exactly (an E4M3 value has at most 4 significant bits
+// and its exponent range lies inside bf16's): one gfx950 scaled conversion of
+// two codes (OCP E4M3) with scale 1, giving the two bf16 values packed. HI
+// selects bytes 2-3 of w instead of 0-1. (Through fp32 with the unscaled
+// conversion and keeping the upper halves gives the same bits for all 65536
+// code pairs, at three instructions instead of one.)
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_bf16x2(uint32_t w) {
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  const f32x2_t f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-  return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xFFFF0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 // 8 codes (lo: the first 4, hi: the next 4) -> one bf16x8 MFMA operand
 __device__ __forceinline__ uint4 fp8x8_bf16x8(uint32_t lo, uint32_t hi) {
