@@ -10,8 +10,6 @@ import os
 import subprocess
 import sys
 
-import pytest
-
 import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
