@@ -106,6 +106,8 @@ def parse():
     ap.add_argument("--summarize-pmc", metavar="DIR",
                     help="write the gate/up HBM traffic summary from rocprofv3 --pmc runs in DIR/pmc_<workload>_"
                          "<FETCH_SIZE|WRITE_SIZE> (csv, -o run) to --out; no GPU needed")
+    ap.add_argument("--counters-workload", default="prefill", choices=["prefill", "decode"],
+                    help="which expert GEMM kernels --summarize-counters reports")
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="write the SQ / L2 counter summary of the 256x256 expert GEMMs from rocprofv3 --pmc runs "
                          "in DIR/<pass> (csv, -o run; passes listed in COUNTER_PASSES) and the kernel trace in "
@@ -642,12 +644,28 @@ COUNTER_PASSES = {
 }
 
 
-def summarize_counters(d: str, out: str) -> None:
-    """Per-dispatch averages of the counter passes for the 256x256 gate/up and down kernels of a prefill run,
-    with the derived clock, matrix-core utilisation, wait fractions and L2 hit rate."""
+def synth_tokens(workload: str) -> int:
+    import synth
+    return synth.spec(workload).T
+
+
+# expert GEMM kernels whose counters summarize_counters reports, by workload: the 256x256 kernel at
+# prefill, the 32-row-tile kernel (weights streamed non-temporally) at decode
+COUNTER_KERNELS = {
+    "prefill": {"gate/up": "gemm_bf16_big8<0", "down": "gemm_bf16_big8<1"},
+    "decode": {"gate/up": "gemm_bf16_mfma<0, 2, 1, 2, 4, true, true", "down": "gemm_bf16_mfma<1, 2, 1, 2, 4, true, true"},
+}
+
+
+def summarize_counters(d: str, out: str, workload: str = "prefill") -> None:
+    """Per-dispatch averages of the counter passes for the expert gate/up and down kernels of a run of
+    `workload`, with the derived clock, matrix-core utilisation, wait fractions, L2 hit rate and vector L1
+    read latency."""
     import collections
     import csv
-    kinds = {"gate/up": "gemm_bf16_big8<0", "down": "gemm_bf16_big8<1"}
+    kinds = COUNTER_KERNELS[workload]
+    tiles = "256x256 expert GEMMs" if workload == "prefill" else "32-row-tile expert GEMMs"
+    T = synth_tokens(workload)
     vals = {k: collections.OrderedDict() for k in kinds}
     for name in COUNTER_PASSES:
         per = collections.defaultdict(lambda: collections.defaultdict(list))
@@ -663,18 +681,19 @@ def summarize_counters(d: str, out: str) -> None:
         for k, pat in kinds.items():
             if pat in r["Kernel_Name"]:
                 dur.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9)
-    L = ["# SQ / LDS / matrix-core / L2 counters of the 256x256 expert GEMMs, prefill (T=8192), MI355X\n",
+    wl = "" if workload == "prefill" else f" --counters-workload {workload}"
+    L = [f"# SQ / LDS / matrix-core / L1 / L2 counters of the {tiles}, {workload} (T={T}), MI355X\n",
          "Commands (repo root, one MI355X, `TMPDIR=/tmp`), one pass each under `timeout -s KILL 120`, then "
-         f"`python bench.py --summarize-counters <dir> --out {out}`:\n", "```"]
+         f"`python bench.py --summarize-counters <dir>{wl} --out {out}`:\n", "```"]
     for name, cs in COUNTER_PASSES.items():
         L.append(f"rocprofv3 --pmc {cs} --output-format csv -d <dir>/{name} -o run -- python bench.py --workload "
-                 "prefill --steps 2 --warmup 1 --no-cpu-baseline --no-secondary")
+                 f"{workload} --steps 2 --warmup 1 --no-cpu-baseline --no-secondary")
     L += ["rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- python bench.py --workload "
-          "prefill --steps 2 --warmup 1 --no-cpu-baseline --no-secondary", "```\n",
+          f"{workload} --steps 2 --warmup 1 --no-cpu-baseline --no-secondary", "```\n",
           "Per dispatch, averaged over the dispatches of each kernel in the run (the layer steps and the gate/up "
           "kernel alone). rocprofv3 reports each counter summed over its hardware instances: GRBM_GUI_ACTIVE over "
           "the 8 XCDs, SQ_CYCLES over the 32 shader engines.\n",
-          "| counter | gate/up `gemm_bf16_big8<0, …>` | down `gemm_bf16_big8<1, …>` |", "|---|---|---|"]
+          f"| counter | gate/up `{kinds['gate/up']}…>` | down `{kinds['down']}…>` |", "|---|---|---|"]
     names = sorted(set(vals["gate/up"]) | set(vals["down"]))
     for c in names:
         L.append(f"| {c} | {vals['gate/up'].get(c, float('nan')):.0f} | {vals['down'].get(c, float('nan')):.0f} |")
@@ -806,7 +825,7 @@ def main():
         summarize_pmc(args.summarize_pmc, args.out)
         return
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters, args.out)
+        summarize_counters(args.summarize_counters, args.out, args.counters_workload)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
