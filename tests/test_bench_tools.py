@@ -10,6 +10,8 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -85,9 +87,19 @@ def test_summarize_trace(tmp_path):
     assert "| `moe::combine_kernel<float>` | 2 | 0.010 | 5.00 |" in text
 
 
-def test_summarize_counters(tmp_path):
+KERNEL_NAMES = {
+    "prefill": ("moe::gemm_bf16_big8<0, true, false, false>(GemmArgs)",
+                "moe::gemm_bf16_big8<1, true, false, false>(GemmArgs)"),
+    "decode": ("moe::gemm_bf16_mfma<0, 2, 1, 2, 4, true, true, false>(GemmArgs)",
+               "moe::gemm_bf16_mfma<1, 2, 1, 2, 4, true, true, false>(GemmArgs)"),
+}
+
+
+@pytest.mark.parametrize("workload", ["prefill", "decode"])
+def test_summarize_counters(tmp_path, workload):
     # one dispatch of each expert GEMM; 8 XCDs of 2.0M cycles each in 1 ms: 2 GHz
-    gu, dn = "moe::gemm_bf16_big8<0, true, false, false>(GemmArgs)", "moe::gemm_bf16_big8<1, true, false, false>(GemmArgs)"
+    gu, dn = KERNEL_NAMES[workload]
+    router = "moe::gemm_bf16_mfma<1, 2, 1, 2, 4, true, false, false>(GemmArgs)"   # not an expert GEMM
     cyc = 2.0e6
     vals = {
         "GRBM_GUI_ACTIVE": 8 * cyc, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * cyc * 1024, "SQ_WAVE_CYCLES": 1000.0,
@@ -103,12 +115,15 @@ def test_summarize_counters(tmp_path):
         for kern in (gu, dn):
             for c in counters.split():
                 rows.append(dict(Kernel_Name=kern, Counter_Name=c, Counter_Value=vals.get(c, 0.0)))
+        for c in counters.split():   # the router's dispatch must not enter the averages
+            rows.append(dict(Kernel_Name=router, Counter_Name=c, Counter_Value=7 * vals.get(c, 1.0)))
         write_csv(str(tmp_path / name / "run_counter_collection.csv"), rows)
     write_csv(str(tmp_path / "trace" / "run_kernel_trace.csv"),
               [dict(Kernel_Name=k, Start_Timestamp=0, End_Timestamp=1_000_000) for k in (gu, dn)])
     out = tmp_path / "c.md"
-    bench.summarize_counters(str(tmp_path), str(out))
+    bench.summarize_counters(str(tmp_path), str(out), workload)
     text = out.read_text()
+    assert f"{workload} (T={32 if workload == 'decode' else 8192})" in text
     line = [l for l in text.splitlines() if l.startswith("- gate/up:")][0]
     for want in ("2.00M cycles per XCD", "1.000 ms", "about 2.00 GHz", "matrix cores busy 50.0%",
                  "waiting on a counter 25%", "to issue 40%", "bank conflicts 0.50%", "hit rate 40.0%",
