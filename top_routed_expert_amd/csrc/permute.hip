@@ -33,13 +33,19 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
+// Block b ranks the pairs of experts 2b and 2b+1 (one block per two experts,
+// so 288 experts fit one round of the compute units): per chunk, each thread
+// counts its pairs of both experts in one int (expert 2b in the low 16 bits,
+// 2b+1 in the high 16; a chunk holds at most 16384 pairs, so the low half
+// never carries into the high one), one block scan serves both, and each
+// expert's running total across chunks is kept apart.
 __global__ void __launch_bounds__(PR_THREADS) permute_rank_kernel(const int32_t* __restrict__ idx, int64_t P, int E,
                                                                   int32_t* __restrict__ rank,
                                                                   int32_t* __restrict__ counts) {
   __shared__ int s_wave[PR_THREADS / 64];
-  const int e = blockIdx.x;
+  const int e0 = 2 * (int)blockIdx.x, e1 = e0 + 1 < E ? e0 + 1 : -2;  // -2: no second expert
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int running = 0;
+  int running0 = 0, running1 = 0;
   for (int64_t base = 0; base < P; base += PR_CHUNK) {
     const int64_t j0 = base + (int64_t)tid * PR_PER;
     int v[PR_PER];
@@ -58,7 +64,7 @@ __global__ void __launch_bounds__(PR_THREADS) permute_rank_kernel(const int32_t*
     }
     int c = 0;
 #pragma unroll
-    for (int i = 0; i < PR_PER; ++i) c += v[i] == e;
+    for (int i = 0; i < PR_PER; ++i) c += (v[i] == e0) + ((v[i] == e1) << 16);
     const int incl = wave_incl_scan(c, lane);
     if (lane == 63) s_wave[wave] = incl;
     __syncthreads();
@@ -68,14 +74,21 @@ __global__ void __launch_bounds__(PR_THREADS) permute_rank_kernel(const int32_t*
       before += w < wave ? s_wave[w] : 0;
       total += s_wave[w];
     }
-    int r = running + before + incl - c;
+    const int excl = before + incl - c;
+    int r0 = running0 + (excl & 0xffff), r1 = running1 + (excl >> 16);
 #pragma unroll
-    for (int i = 0; i < PR_PER; ++i)
-      if (v[i] == e) rank[j0 + i] = r++;
-    running += total;
+    for (int i = 0; i < PR_PER; ++i) {
+      if (v[i] == e0) rank[j0 + i] = r0++;
+      else if (v[i] == e1) rank[j0 + i] = r1++;
+    }
+    running0 += total & 0xffff;
+    running1 += total >> 16;
     __syncthreads();
   }
-  if (tid == 0) counts[e] = running;
+  if (tid == 0) {
+    counts[e0] = running0;
+    if (e1 >= 0) counts[e1] = running1;
+  }
 }
 
 __global__ void __launch_bounds__(256) permute_place_kernel(const int32_t* __restrict__ idx, int64_t P, int K, int E,
@@ -374,7 +387,7 @@ hipError_t launch_permute(const int32_t* idx, int64_t T, int K, int E, int32_t* 
                           int32_t extra_rows, Tile* tiles, int32_t* n_tiles, int32_t max_tiles, int block_rows,
                           hipStream_t s) {
   const int64_t P = T * K;
-  permute_rank_kernel<<<E, PR_THREADS, 0, s>>>(idx, P, E, rank, counts);
+  permute_rank_kernel<<<(E + 1) / 2, PR_THREADS, 0, s>>>(idx, P, E, rank, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   int64_t blocks = (P + 255) / 256;
