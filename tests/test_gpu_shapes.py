@@ -3,7 +3,8 @@
 The parity cases elsewhere pick one shape per kernel path. This sweep draws
 24 more from a fixed generator: token counts on both sides of every switch the
 library makes (1 token; 32/33 and 64/65 around the router's split form and the
-single-block permutation at T*K = 1024; 12288/12289 around the fused router),
+single-block permutation at T*K = 1024; 6144/6145 and 12288/12289 around
+the fused router),
 widths that do and do not fit the MFMA tiles (expert widths of at least 96
 with more than 3000 tokens, see _shapes), 1 to 48 experts, K from 1 to 8,
 no shared expert or one of another width, fp32 and bf16 layers, skewed
@@ -45,14 +46,14 @@ pytestmark = pytest.mark.gpu
 
 def _shapes(n: int = 24, seed: int = 2026) -> dict:
     rng = random.Random(seed)
-    tokens = [1, 2, 5, 31, 32, 33, 63, 64, 65, 97, 128, 129, 257, 511, 1025, 2049, 3000, 12288, 12289]
+    tokens = [1, 2, 5, 31, 32, 33, 63, 64, 65, 97, 128, 129, 257, 511, 1025, 2049, 3000, 12288, 12289, 6144, 6145]
     widths = [64, 128, 192, 256, 320, 384, 512, 72, 200]
     ffn = [32, 64, 96, 128, 160, 192, 256, 320]
     out = {}
     for i in range(n):
         T = tokens[i % len(tokens)] if i < len(tokens) else rng.choice(tokens)
         big = T > 3000
-        D = rng.choice(widths[:4] if big else widths)
+        D = rng.choice(widths[1:4] if big else widths)   # the fused router takes d_model >= 128
         E = rng.randint(1, 48)
         K = rng.randint(1, min(E, 8))
         # with many tokens, widths of at least 96: at width 64 and below the one bf16 rounding of
@@ -72,7 +73,7 @@ SHAPES = _shapes()
 
 def test_sweep_spans_the_switches():
     ts = {s.T for s in SHAPES.values()}
-    assert {1, 32, 33, 64, 65, 12288, 12289} <= ts
+    assert {1, 32, 33, 64, 65, 6144, 6145, 12288, 12289} <= ts
     assert any(s.dtype == "f32" for s in SHAPES.values()) and any(s.Fs == 0 for s in SHAPES.values())
 
 

@@ -111,7 +111,9 @@ struct RouteWs {
   float* logits;
 };
 int route_ksplit(const moe_config* c, int64_t T) {
-  return router_ksplit(fast_path(c->dtype, c->d_model, 64), T, c->d_model);
+  const bool fast = fast_path(c->dtype, c->d_model, 64);
+  if (fast && router_topk_fits(T, c->d_model, c->n_experts, c->top_k)) return 1;  // no partial sums
+  return router_ksplit(fast, T, c->d_model, c->n_experts);
 }
 RouteWs carve_route(Arena& a, const moe_config* c, int64_t T) {
   return {a.take<float>(route_ksplit(c, T) * T * c->n_experts)};

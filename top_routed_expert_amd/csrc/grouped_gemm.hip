@@ -452,11 +452,24 @@ int gemm_block_rows(bool fast, int64_t rows, int n_groups, bool allow_big) {
   return rows <= MOE_ROWS_64 * (int64_t)n_groups ? 64 : 128;
 }
 
-int router_ksplit(bool fast, int64_t T, int Kdim) {
-  if (!fast || T > 64) return 1;
+// Up to 64 tokens: 16 slices (fewer when the stage count is not a multiple).
+// More tokens: a few row tiles leave most compute units idle while each block
+// walks the whole contraction, so the slices double (up to 16, dividing the
+// stage count) while the grid stays within 384 blocks, about one and a half
+// blocks per compute unit.
+int router_ksplit(bool fast, int64_t T, int Kdim, int E) {
+  if (!fast) return 1;
   const int nk = Kdim / 64;
   int ks = 16;
-  while (ks > 1 && nk % ks) ks >>= 1;
+  if (T <= 64) {
+    while (ks > 1 && nk % ks) ks >>= 1;
+    return ks;
+  }
+  const int64_t BM = gemm_block_rows(fast, T, 1, false);
+  const int64_t BN = E <= 512 ? 64 : 256;  // column width of the launch that takes BM-row tiles
+  const int64_t blocks = (T + BM - 1) / BM * ((E + BN - 1) / BN);
+  ks = 1;
+  while (ks < 16 && nk % (2 * ks) == 0 && blocks * 2 * ks <= 384) ks *= 2;
   return ks;
 }
 

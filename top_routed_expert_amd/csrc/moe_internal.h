@@ -152,8 +152,9 @@ __device__ __forceinline__ const float* group_scale(const GemmArgs& p, const flo
 // Row-tile height on the bf16 MFMA path (`fast`): 32, 64, 128 or (expert
 // GEMMs with many rows per group, `allow_big`) 256; 64 on the generic path.
 int gemm_block_rows(bool fast, int64_t rows, int n_groups, bool allow_big);
-// Contraction slices of the router GEMM for T tokens (1 unless T is small).
-int router_ksplit(bool fast, int64_t T, int Kdim);
+// Contraction slices of the router GEMM for T tokens and E experts (1 on the
+// generic path and when the row tiles alone fill the chip).
+int router_ksplit(bool fast, int64_t T, int Kdim, int E);
 int64_t gemm_max_tiles(int64_t n_rows, int n_groups, int block_rows);
 // Tiles of groups g = 0 .. n_groups-1 over rows [offsets[g], offsets[g+1]);
 // group skip_group (if >= 0) gets none.
@@ -165,8 +166,8 @@ hipError_t launch_grouped_gemm(int dtype, bool fast, int epi, int block_rows, co
 hipError_t launch_grouped_gemm_big8(int epi, const GemmArgs& g, hipStream_t s);
 
 // router.hip: linear layer, softmax and top-K in one kernel, 32 tokens per
-// block (bf16, router row-major or packed with the same results, T > 64,
-// E <= 320, d_model a multiple of 64 and at least 128); k_tok, gap and gmass
+// block (bf16, router row-major or packed with the same results,
+// 6144 < T <= 12288, E <= 320, d_model a multiple of 64 and at least 128); k_tok, gap and gmass
 // as launch_topk.
 bool router_topk_fits(int64_t T, int D, int E, int K);
 hipError_t launch_router_topk(const bf16_t* x, int64_t T, int D, const bf16_t* w_router, bool packed,

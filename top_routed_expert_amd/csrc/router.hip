@@ -314,9 +314,12 @@ __global__ void __launch_bounds__(256) router_topk_kernel(const bf16_t* __restri
 // Above 12288 tokens the two-kernel route is faster: every 32 tokens here read
 // the whole router matrix again (d_model 4096, 288 experts: 119.5 against
 // 107 us at 16384 tokens, 494 against 431 us at 65536; 59.7 against 75.9 us
-// at 8192).
+// at 8192). Up to 6144 tokens the router GEMM with its contraction split over
+// the idle compute units, then top-k over the partial sums, is faster too: a
+// block here walks the whole contraction for its 32 tokens, about 62 us
+// however few blocks there are.
 bool router_topk_fits(int64_t T, int D, int E, int K) {
-  return T > 64 && T <= 12288 && E <= 20 * 16 && K <= E && D % RT_KS == 0 && D >= 2 * RT_KS;
+  return T > 6144 && T <= 12288 && E <= 20 * 16 && K <= E && D % RT_KS == 0 && D >= 2 * RT_KS;
 }
 
 hipError_t launch_router_topk(const bf16_t* x, int64_t T, int D, const bf16_t* w_router, bool packed,
