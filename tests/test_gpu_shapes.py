@@ -22,7 +22,7 @@ full and the output on sampled rows.
 LIMITS adds layers at the edges of the configuration the library accepts:
 1024 routed experts and K = 64 (the largest it takes) on the decode-size,
 32-row and 256-row tile paths; 1022 and 1023 experts at T*K = 1024 (the
-single-block permutation takes at most 1022); 320 and 321 experts at 200
+single-block permutation takes at most 1022); 320 and 321 experts at 6200
 tokens (the fused router takes at most 320).
 """
 from __future__ import annotations
@@ -126,9 +126,9 @@ LIMITS = {
     # the single-block permutation at its expert limit and one past it (T*K = 1024)
     "E1022_K64_T16": synth.spec("tiny", T=16, D=256, E=1022, K=64, F=128, Fs=128, dtype="bf16", seed=305),
     "E1023_K64_T16": synth.spec("tiny", T=16, D=256, E=1023, K=64, F=128, Fs=128, dtype="bf16", seed=306),
-    # the fused router at its expert limit and one past it (more than 64 tokens)
-    "E320_K8_T200": synth.spec("tiny", T=200, D=256, E=320, K=8, F=128, Fs=128, dtype="bf16", seed=307),
-    "E321_K8_T200": synth.spec("tiny", T=200, D=256, E=321, K=8, F=128, Fs=128, dtype="bf16", seed=308),
+    # the fused router at its expert limit and one past it (6145 to 12288 tokens)
+    "E320_K8_T6200": synth.spec("tiny", T=6200, D=256, E=320, K=8, F=128, Fs=128, dtype="bf16", seed=307),
+    "E321_K8_T6200": synth.spec("tiny", T=6200, D=256, E=321, K=8, F=128, Fs=128, dtype="bf16", seed=308),
     # K = 1 over 1024 experts with many tokens (two-kernel router, one row per pair)
     "E1024_K1_T3000": synth.spec("tiny", T=3000, D=256, E=1024, K=1, F=128, Fs=0, dtype="bf16", seed=309),
 }

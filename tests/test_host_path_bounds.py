@@ -88,8 +88,10 @@ LAYERS = {
     # fp8 expert weights (quantised by the library), decode-like
     "decode_like_fp8": (8, 32, 8, 512, 128, 2, 2, 0),
     # rank/place permutation (T*K above 1024) and the 256x256 expert GEMM (its form that skips
-    # empty half items: 147 mean rows per group), packed
+    # empty half items: 147 mean rows per group), packed; router over 8 contraction slices
     "mid_packed_256_row_tiles": (264, 8, 4, 512, 256, 3, 1, 0),
+    # router over 4 slices added by the one-wave-per-token top-k, packed
+    "split_router_wave_topk": (100, 8, 2, 256, 64, 8, 1, 0),
     # row-major weights, ragged widths of the bf16 MFMA path
     "small_rows": (20, 16, 6, 256, 192, 4, 0, 0),
 }
@@ -120,9 +122,9 @@ LIMIT_LAYERS = {
     # the single-block permutation at its expert limit and one past it
     "E1022_K64_T16": (16, 1022, 64, 256, 64, 3, 0, 0),
     "E1023_K64_T16": (16, 1023, 64, 256, 64, 4, 0, 0),
-    # the fused router at its expert limit and one past it
-    "E320_K8_T200": (200, 320, 8, 256, 64, 5, 0, 0),
-    "E321_K8_T200_packed": (200, 321, 8, 256, 64, 6, 1, 0),
+    # the fused router (6145 to 12288 tokens) at its expert limit and one past it
+    "E320_K1_T6145": (6145, 320, 1, 128, 64, 5, 0, 0),
+    "E321_K1_T6145_packed": (6145, 321, 1, 128, 64, 6, 1, 0),
     # fp32 with the largest expert count and K (real routing through the generic GEMM)
     "E1024_K64_T40_fp32": (40, 1024, 64, 128, 32, 7, 0, 1),
 }

@@ -114,23 +114,35 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   const int lane = threadIdx.x & 63;
   int64_t t;
   const float* l;
-  if (nsplit > 1) {  // one token per block: the four waves add the partial sums
+  if (nsplit > 4) {  // one token per block: the four waves add the partial sums
     t = blockIdx.x;
     sum_partials<VPL>(logits, nsplit, T, E, t, s_logit, s_part);
     if (threadIdx.x >= 64) return;
     l = s_logit;
-  } else {           // one token per wave
+  } else {           // one token per wave, adding up to four partial sums itself
     t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;  // whole wave
     l = logits + t * E;
   }
+  // partial sums this wave adds, in slice order: ((p0 + p1) + p2) + p3
+  const int nadd = nsplit > 4 ? 1 : nsplit;
+  const int64_t slice = T * (int64_t)E;
 
   float v[VPL];
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int e = lane + 64 * j;
-    const float x = e < E ? l[e] : -INFINITY;
+    float x = -INFINITY;
+    if (e < E) {
+      x = l[e];
+      if (nadd > 1) {
+        const float x1 = l[slice + e];
+        const float x2 = nadd > 2 ? l[2 * slice + e] : 0.f;
+        const float x3 = nadd > 3 ? l[3 * slice + e] : 0.f;
+        x = ((x + x1) + x2) + x3;
+      }
+    }
     v[j] = x;
     m = fmaxf(m, x);
   }
@@ -289,7 +301,7 @@ hipError_t launch_group_stats(const float* gmass, const int32_t* idx, int64_t T,
 hipError_t launch_topk(const float* logits, int nsplit, int64_t T, int E, int K, const int32_t* k_tok, int32_t* idx,
                        float* prob, float* gap, float* gmass, int G, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const unsigned blocks = (unsigned)(nsplit > 1 ? T : (T + 3) / 4);
+  const unsigned blocks = (unsigned)(nsplit > 4 ? T : (T + 3) / 4);
   const int vpl = (E + 63) / 64;
 #define MOE_TOPK(V) \
   topk_kernel<V><<<blocks, 256, 0, s>>>(logits, nsplit, T, E, K, k_tok, idx, prob, gap, gmass, G)
