@@ -188,7 +188,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   }
   float p_last = 0.f;
   for (int r = 0; r <= kt; ++r) {
-    if (r == kt && kt == E) break;
+    if (r == kt && (kt == E || !gap)) break;  // round kt only finds the gap
     unsigned long long best = key[0];
 #pragma unroll
     for (int j = 1; j < VPL; ++j) best = key[j] > best ? key[j] : best;

@@ -279,8 +279,9 @@ __global__ void __launch_bounds__(256) router_topk_kernel(const bf16_t* __restri
     // count is reached only reduces (its lanes agree, so its moves stay inside the row)
     float p_last = 0.f;
     const bool store = real && j16 == 0;
+    const int rounds = gap ? K + 1 : K;  // the last round only finds the gap
 #pragma unroll 1
-    for (int r = 0; r <= K; ++r) {
+    for (int r = 0; r < rounds; ++r) {
       unsigned long long best = key[0];
 #pragma unroll
       for (int i = 1; i < RT_VPL; ++i) best = key[i] > best ? key[i] : best;
