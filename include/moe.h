@@ -304,7 +304,7 @@ moe_status moe_layer_forward_dynamic(const moe_config* cfg, int64_t T, const voi
  * ends. Nothing is allocated or freed by the call.
  *   - Layers whose moe_layer_workspace_bytes(cfg, T) exceeds that size are
  *     rejected with MOE_ERR_WORKSPACE before anything is enqueued (at
- *     d_model 4096 and expert width 1280: up to about 370 tokens).
+ *     d_model 4096 and expert width 1280: up to 354 tokens).
  *   - The scratch of the current device is used (hipGetDevice); `stream`
  *     must belong to that device.
  *   - Every call on a GPU shares that GPU's scratch and leaves its contents
