@@ -24,8 +24,11 @@ pytestmark = pytest.mark.gpu
 GRAPH_LAYERS = {
     # 32-row tiles, split router, single-block permutation (decode-like)
     "small_batch": synth.spec("tiny", T=32, D=512, E=32, K=8, F=256, Fs=256, dtype="bf16", seed=41),
-    # fused router, rank/place permutation, 256x256 expert GEMMs, 16-bit expert outputs
+    # router over four contraction slices with the wave top-k, rank/place permutation, 256x256
+    # expert GEMMs, 16-bit expert outputs
     "large_batch": synth.spec("tiny", T=2048, D=256, E=8, K=2, F=256, Fs=256, dtype="bf16", seed=42),
+    # the fused router kernel (6145 to 12288 tokens)
+    "fused_router": synth.spec("tiny", T=6200, D=256, E=8, K=2, F=256, Fs=256, dtype="bf16", seed=43),
 }
 
 
