@@ -225,9 +225,12 @@ def sample_rows(T: int, n: int, seed: int, must=()) -> np.ndarray:
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name,n_rows", [("decode", 32), ("prefill", 12), ("skew", 12), ("full", 6)])
-def test_layer_full_size(name, n_rows):
-    spec = synth.spec(name)
+# the four workloads, and the prefill shape at 512 tokens (32-row tiles with about 14 rows per
+# expert, router over 16 contraction slices) and 1024 tokens (64-row tiles, 8 slices)
+@pytest.mark.parametrize("name,n_rows,T", [("decode", 32, None), ("prefill", 12, None), ("skew", 12, None),
+                                           ("full", 6, None), ("prefill", 12, 512), ("prefill", 12, 1024)])
+def test_layer_full_size(name, n_rows, T):
+    spec = synth.spec(name) if T is None else synth.spec(name, T=T)
     L = device_layer(spec)
     cfg = moe.config_for(spec)
     out, idx, prob, offs = moe.layer_forward(cfg, L["x"], L, routing=True)
@@ -254,7 +257,7 @@ def test_layer_full_size(name, n_rows):
     tie = check_near_ties(gidx, to_host(prob), ref, x_host, W.router, spec.K)
     tie_ref = near_tie_reference(x_host, W, tie, gidx, ref) if tie.size else None
     c32, c16 = check_outputs(spec, cfg, L, out, rr["out_rows"], rows, tie, tie_ref)
-    msg = (f"{name}: near_ties={r['near_ties']} prob_err={r['prob_err']:.2e} prob_rel={r['prob_rel']:.2e} "
+    msg = (f"{name} T={spec.T}: near_ties={r['near_ties']} prob_err={r['prob_err']:.2e} prob_rel={r['prob_rel']:.2e} "
            f"bound_use={r['bound_use']:.3f} touched={load['touched']} "
            f"skew={load['skew']:.2f} out_rel(before cast)={c32['rel']:.3e} out_rel(output)={c16['rel']:.3e} "
            f"rows={len(rows)} near_tie_rows_checked={len(tie)}")
